@@ -1,0 +1,51 @@
+// cbd_device.h -- small gfx950 device helpers shared by the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cbd_kernarg.h"
+
+namespace cbd {
+namespace dev {
+
+// Buffer resource over one tensor.  Record count = tensor bytes, so a load
+// at an offset past the end returns zeros and a store there is dropped:
+// predication costs one out-of-range offset instead of a branch.
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  // dword3 0x00020000: raw (untyped) 32-bit data format for the gfx9 family.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // > every record count (tensors < 2 GiB)
+
+// f32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ inline uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Logical tile of hardware workgroup b.  Workgroups are dealt round-robin to
+// the 8 XCDs (each with its own L2); with remap on, XCD x receives the
+// contiguous logical range [x*q + min(x, r), ...), so neighbouring tiles --
+// which share operand panels -- meet in one L2.
+__device__ inline int logical_tile(int b, int total, int remap) {
+  if (!remap) return b;
+  int q = total >> 3, r = total & 7, x = b & 7, idx = b >> 3;
+  return x * q + (x < r ? x : r) + idx;
+}
+
+// Class owning logical tile t (tile_begin ascends with the class index).
+__device__ inline int find_class(const GemmArgs& a, int t) {
+  int r = 0;
+  for (int i = 1; i < a.num_sub; i++)
+    if (a.sub[i].tile_begin <= t) r = i;
+  return r;
+}
+
+}  // namespace dev
+}  // namespace cbd

@@ -1,0 +1,36 @@
+// cbd_internal.h -- the plan object and the launchers behind the C ABI.
+#pragma once
+#include <string>
+#include <vector>
+
+#include "../../include/cbd.h"
+#include "cbd_kernarg.h"
+
+struct cbd_plan_s {
+  cbd_problem prob;
+  cbd_plan_info_t info;
+  std::vector<cbd_subgemm_t> subs;       // in launch (LPT) order, ids 0..R-1
+  std::vector<cbd_zero_region_t> zeros;
+  cbd::GemmArgs gemm;                    // pointers filled per run
+  cbd::ZeroArgs zero;
+};
+
+namespace cbd {
+
+// Thread-local error detail for CBD_ERR_HIP and planner rejections.
+void set_error(const std::string& msg);
+
+// Launchers (defined next to their kernels).  Each returns 0 or a hipError_t.
+int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream);
+int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream);
+int launch_grouped(const GemmArgs& a, int dtype, int64_t grid, void* stream);
+int launch_zero_fill(const ZeroArgs& z, int64_t grid, void* stream);
+const char* hip_error_name(int err);
+
+// Tile shapes of each kernel family (the planner sizes grids with them).
+constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;
+constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 64, kFastThreads = 256;
+constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
+constexpr int kZeroThreads = 256, kZeroItemsPerThread = 4;
+
+}  // namespace cbd

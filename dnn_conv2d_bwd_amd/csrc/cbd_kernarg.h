@@ -1,0 +1,69 @@
+// cbd_kernarg.h -- plain-old-data launch arguments shared by the host planner
+// and the gfx950 kernels.  Everything a kernel needs arrives by value in the
+// kernel-argument segment; no device-side tables are allocated.
+#pragma once
+#include <stdint.h>
+
+namespace cbd {
+
+// Sub-GEMM (one stride-residue class) descriptors per launch.  The class
+// count is at most stride_h * stride_w, which the planner caps at 64.
+constexpr int kMaxSub = 64;
+constexpr int kMaxZero = 64;
+
+// One stride-residue class (i_h, i_w).  Along each axis the class owns the
+// taps cls + tstep*j, j < taps; it covers the dX positions phase + S*t,
+// t < pos; tap j of position t reads dY row t + beta - delta*j.
+struct SubDesc {
+  int32_t phase_h, phase_w;
+  int32_t beta_h, beta_w;
+  int32_t taps_h, taps_w;
+  int32_t cls_h, cls_w;
+  int32_t pos_h, pos_w;
+  int32_t tile_begin;  // first logical workgroup of this class
+};
+
+struct GemmArgs {
+  // problem (element counts; every tensor is < 2^31 bytes)
+  int32_t N, G, C, K, Cg, Kg;
+  int32_t Hi, Wi, Ho, Wo, Y, X;
+  int32_t Sh, Sw;
+  int32_t tstep_h, tstep_w;  // T = S / gcd(S, D)
+  int32_t delta_h, delta_w;  // delta = D / gcd(S, D)
+  // tensor sizes in bytes: buffer-resource record counts, so every access
+  // outside a tensor reads 0 / is dropped by the hardware
+  uint32_t dy_bytes, w_bytes, dx_bytes;
+  int32_t num_sub;
+  int32_t total_tiles;
+  int32_t tiles_m;     // GEMM-M tiles per group
+  int32_t tile_n;      // GEMM-N extent of one tile (positions)
+  int32_t xcd_remap;   // 1: give each XCD a contiguous range of logical tiles
+  int32_t iters;       // grouped kernel: positions per thread
+  int32_t pad_;
+  const void* dy;
+  const void* w;
+  void* dx;
+  SubDesc sub[kMaxSub];
+};
+
+// One dX phase lattice (phase_h + Sh*a, phase_w + Sw*b) that no tap reaches.
+struct ZeroDesc {
+  int32_t phase_h, phase_w;
+  int32_t pos_h, pos_w;
+  int64_t item_begin;  // first work item of this region
+};
+
+struct ZeroArgs {
+  int32_t N, C, Hi, Wi, Sh, Sw;
+  int32_t layout;      // 0 NCHW, 1 NHWC
+  int32_t esize;       // bytes per element (4 or 2)
+  int32_t chunk;       // bytes written per work item
+  int32_t num_regions;
+  int64_t total_items;
+  uint32_t dx_bytes;
+  int32_t pad_;
+  void* dx;
+  ZeroDesc reg[kMaxZero];
+};
+
+}  // namespace cbd

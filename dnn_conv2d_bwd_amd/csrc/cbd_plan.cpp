@@ -1,0 +1,366 @@
+// cbd_plan.cpp -- host planner: validates a problem, splits it into
+// stride-residue sub-GEMMs and zero regions, picks a kernel family and packs
+// the launch arguments.  Pure host code; needs no GPU.
+//
+// Per axis (stride S, dilation D, pad P, taps F, input extent L), a tap f
+// feeds dX position h iff h + P - f*D is a non-negative multiple of S whose
+// quotient is a valid output index (the adjoint of the forward window
+// h = o*S + f*D - P).  With g = gcd(S, D), T = S/g, delta = D/g:
+//   * the taps reaching one position form one residue class f = i (mod T),
+//     i in [0, T); class i holds ceil((F - i)/T) taps (none if i >= F);
+//   * class i serves the dX phase phi_i = (D*i - P) mod S, positions
+//     h = phi_i + S*t, t < ceil((L - phi_i)/S);
+//   * tap i + T*j of that class reads output row t + beta_i - delta*j with
+//     beta_i = (phi_i + P - D*i)/S (an exact integer);
+//   * phases hit by no class with taps are never reached: written as zero.
+// Every (class_h, class_w) pair with taps and positions is one GEMM (per
+// group): M = C/G, N = N*pos_h*pos_w, K = (K/G)*taps_h*taps_w.  This is the
+// stride-residue decomposition behind the multi-kernel backward data of
+// rocMLIR PR #246 "Backward data" and the v4r1 backward-data strategy named
+// in MIOpen PR #272; neither page derives it, the derivation above follows
+// from the forward window alone.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "cbd_internal.h"
+
+namespace {
+
+int64_t gcd64(int64_t a, int64_t b) {
+  while (b) {
+    int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t pos_mod(int64_t a, int64_t m) {
+  int64_t r = a % m;
+  return r < 0 ? r + m : r;
+}
+
+struct AxisClass {
+  int64_t cls, taps, phase, beta, pos;
+};
+
+struct Axis {
+  int64_t T, delta;
+  std::vector<AxisClass> classes;
+};
+
+Axis split_axis(int64_t L, int64_t F, int64_t S, int64_t D, int64_t P) {
+  Axis ax;
+  const int64_t g = gcd64(S, D);
+  ax.T = S / g;
+  ax.delta = D / g;
+  for (int64_t i = 0; i < ax.T; i++) {
+    AxisClass c;
+    c.cls = i;
+    c.taps = i < F ? ceil_div(F - i, ax.T) : 0;
+    c.phase = pos_mod(D * i - P, S);
+    c.beta = (c.phase + P - D * i) / S;
+    c.pos = c.phase < L ? ceil_div(L - c.phase, S) : 0;
+    ax.classes.push_back(c);
+  }
+  return ax;
+}
+
+int64_t out_extent(int64_t L, int64_t P, int64_t D, int64_t F, int64_t S) {
+  const int64_t room = L + 2 * P - D * (F - 1) - 1;
+  return room < 0 ? 0 : room / S + 1;
+}
+
+cbd_status fail(cbd_status st, const std::string& msg) {
+  cbd::set_error(msg);
+  return st;
+}
+
+bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg) {
+  return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Kg % cbd::kFastBK == 0 &&
+         Cg % 8 == 0;
+}
+
+bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
+  return p.layout == CBD_LAYOUT_NHWC && Cg == Kg && (Cg == 1 || Cg == 2 || Cg == 4 || Cg == 8) &&
+         p.g <= cbd::kGroupedThreads && cbd::kGroupedThreads % p.g == 0 &&
+         max_taps <= cbd::kGroupedMaxTaps;
+}
+
+}  // namespace
+
+extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* options,
+                                  cbd_plan_t** out_plan) {
+  if (!problem || !out_plan) return fail(CBD_ERR_INVALID_ARG, "NULL problem or out_plan");
+  *out_plan = nullptr;
+  const cbd_problem p = *problem;
+  int32_t force = CBD_KERNEL_AUTO;
+  if (options) {
+    for (int i = 0; i < 7; i++)
+      if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    force = options->force_kernel;
+    if (force < CBD_KERNEL_AUTO || force > CBD_KERNEL_GROUPED)
+      return fail(CBD_ERR_INVALID_ARG, "unknown force_kernel");
+  }
+  if (p.n < 1 || p.g < 1 || p.c < 1 || p.k < 1 || p.hi < 1 || p.wi < 1 || p.y < 1 || p.x < 1)
+    return fail(CBD_ERR_INVALID_ARG, "sizes must be >= 1");
+  if (p.stride_h < 1 || p.stride_w < 1 || p.dil_h < 1 || p.dil_w < 1)
+    return fail(CBD_ERR_INVALID_ARG, "stride and dilation must be >= 1");
+  if (p.pad_h < 0 || p.pad_w < 0) return fail(CBD_ERR_INVALID_ARG, "padding must be >= 0");
+  if (p.c % p.g || p.k % p.g) return fail(CBD_ERR_INVALID_ARG, "groups must divide C and K");
+  if (p.layout != CBD_LAYOUT_NCHW && p.layout != CBD_LAYOUT_NHWC)
+    return fail(CBD_ERR_INVALID_ARG, "unknown layout");
+  if (p.dtype != CBD_F32 && p.dtype != CBD_BF16) return fail(CBD_ERR_INVALID_ARG, "unknown dtype");
+  // Keep every intermediate comfortably inside 64-bit arithmetic before the
+  // size checks below.
+  const int64_t kDimMax = int64_t(1) << 31;
+  if (p.n >= kDimMax || p.c >= kDimMax || p.k >= kDimMax || p.hi >= kDimMax ||
+      p.wi >= kDimMax || p.y >= kDimMax || p.x >= kDimMax)
+    return fail(CBD_ERR_UNSUPPORTED, "dimension beyond 2^31");
+  if (p.pad_h > (1 << 20) || p.pad_w > (1 << 20) || p.dil_h > 64 || p.dil_w > 64 ||
+      p.stride_h > 64 || p.stride_w > 64)
+    return fail(CBD_ERR_UNSUPPORTED, "pad > 2^20, dilation > 64 or stride > 64");
+  if ((int64_t)p.stride_h * p.stride_w > cbd::kMaxSub)
+    return fail(CBD_ERR_UNSUPPORTED, "stride_h * stride_w > 64");
+
+  const int64_t Ho = out_extent(p.hi, p.pad_h, p.dil_h, p.y, p.stride_h);
+  const int64_t Wo = out_extent(p.wi, p.pad_w, p.dil_w, p.x, p.stride_w);
+  if (Ho < 1 || Wo < 1) return fail(CBD_ERR_INVALID_ARG, "filter larger than padded input");
+  const int64_t Cg = p.c / p.g, Kg = p.k / p.g;
+  const int64_t es = p.dtype == CBD_F32 ? 4 : 2;
+  const double lim = 2147483647.0;  // tensors must stay below 2^31 bytes
+  if ((double)p.n * p.c * p.hi * p.wi * es > lim || (double)p.n * p.k * Ho * Wo * es > lim ||
+      (double)p.k * Cg * p.y * p.x * es > lim)
+    return fail(CBD_ERR_UNSUPPORTED, "a tensor reaches 2^31 bytes (32-bit buffer addressing)");
+
+  const Axis ah = split_axis(p.hi, p.y, p.stride_h, p.dil_h, p.pad_h);
+  const Axis aw = split_axis(p.wi, p.x, p.stride_w, p.dil_w, p.pad_w);
+
+  cbd_plan_s* pl = new (std::nothrow) cbd_plan_s();
+  if (!pl) return fail(CBD_ERR_NO_MEMORY, "plan allocation failed");
+  pl->prob = p;
+  std::memset(&pl->info, 0, sizeof(pl->info));
+  std::memset(&pl->gemm, 0, sizeof(pl->gemm));
+  std::memset(&pl->zero, 0, sizeof(pl->zero));
+
+  // Sub-GEMMs and reached phases.
+  std::vector<cbd_subgemm_t> subs;
+  int64_t max_taps = 0;
+  std::vector<char> reached((size_t)(p.stride_h * p.stride_w), 0);
+  for (const AxisClass& ch : ah.classes) {
+    for (const AxisClass& cw : aw.classes) {
+      if (ch.taps * cw.taps == 0 || ch.pos * cw.pos == 0) continue;
+      cbd_subgemm_t s;
+      std::memset(&s, 0, sizeof(s));
+      s.class_h = (int32_t)ch.cls;
+      s.class_w = (int32_t)cw.cls;
+      s.phase_h = (int32_t)ch.phase;
+      s.phase_w = (int32_t)cw.phase;
+      s.beta_h = (int32_t)ch.beta;
+      s.beta_w = (int32_t)cw.beta;
+      s.taps_h = (int32_t)ch.taps;
+      s.taps_w = (int32_t)cw.taps;
+      s.tstep_h = (int32_t)ah.T;
+      s.tstep_w = (int32_t)aw.T;
+      s.delta_h = (int32_t)ah.delta;
+      s.delta_w = (int32_t)aw.delta;
+      s.pos_h = ch.pos;
+      s.pos_w = cw.pos;
+      s.m = Cg;
+      s.n = p.n * ch.pos * cw.pos;
+      s.k = Kg * ch.taps * cw.taps;
+      subs.push_back(s);
+      reached[(size_t)(ch.phase * p.stride_w + cw.phase)] = 1;
+      max_taps = std::max(max_taps, ch.taps * cw.taps);
+    }
+  }
+  // Longest-processing-time order: classes with the largest K launch first.
+  std::stable_sort(subs.begin(), subs.end(),
+                   [](const cbd_subgemm_t& x, const cbd_subgemm_t& y) { return x.k > y.k; });
+
+  // Kernel family.
+  int kernel;
+  if (force == CBD_KERNEL_AUTO) {
+    if (fast_ok(p, Cg, Kg) && Cg >= 128)
+      kernel = CBD_KERNEL_NHWC_BF16;
+    else if (grouped_ok(p, Cg, Kg, max_taps))
+      kernel = CBD_KERNEL_GROUPED;
+    else
+      kernel = CBD_KERNEL_GENERIC;
+  } else {
+    kernel = force;
+    if (kernel == CBD_KERNEL_NHWC_BF16 && !fast_ok(p, Cg, Kg)) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "NHWC bf16 kernel needs NHWC, bf16, K/G % 64 == 0, C/G % 8 == 0");
+    }
+    if (kernel == CBD_KERNEL_GROUPED && !grouped_ok(p, Cg, Kg, max_taps)) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "grouped kernel needs NHWC, C/G == K/G in {1,2,4,8}, G | 256, <= 9 taps per class");
+    }
+  }
+
+  int64_t bm = 0, bn = 0, bk = 0, threads = 0;
+  if (kernel == CBD_KERNEL_GENERIC) {
+    bm = cbd::kGenericBM; bn = cbd::kGenericBN; bk = cbd::kGenericBK; threads = cbd::kGenericThreads;
+  } else if (kernel == CBD_KERNEL_NHWC_BF16) {
+    bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;
+  } else {
+    threads = cbd::kGroupedThreads;
+  }
+
+  // Grouped kernel: positions per thread so that the grid is ~2048 workgroups.
+  int64_t iters = 1;
+  int64_t slots = 0;
+  if (kernel == CBD_KERNEL_GROUPED) {
+    slots = cbd::kGroupedThreads / p.g;
+    int64_t total_pos = 0;
+    for (const auto& s : subs) total_pos += s.n;
+    iters = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(total_pos, slots * 2048)));
+  }
+
+  // Tiles per class (contiguous ranges of the logical grid, in LPT order).
+  int64_t tile = 0;
+  int64_t tiles_m = kernel == CBD_KERNEL_GROUPED ? 1 : ceil_div(Cg, bm);
+  bool equal_k = true;
+  int64_t exec = 0;
+  for (size_t i = 0; i < subs.size(); i++) {
+    cbd_subgemm_t& s = subs[i];
+    s.id = (int32_t)i;
+    s.tile_begin = tile;
+    if (kernel == CBD_KERNEL_GROUPED)
+      s.tiles = ceil_div(s.n, slots * iters);
+    else
+      s.tiles = p.g * tiles_m * ceil_div(s.n, bn);
+    tile += s.tiles;
+    if (s.k != subs[0].k) equal_k = false;
+    exec += p.g * s.m * s.n * s.k;
+  }
+  // A launch must stay below 2^32 work-items.
+  if (tile * threads >= (int64_t(1) << 32)) {
+    delete pl;
+    return fail(CBD_ERR_UNSUPPORTED, "grid too large");
+  }
+
+  // Zero regions: every phase pair with positions that no class reaches.
+  std::vector<cbd_zero_region_t> zeros;
+  for (int64_t ph = 0; ph < p.stride_h; ph++) {
+    for (int64_t pw = 0; pw < p.stride_w; pw++) {
+      if (reached[(size_t)(ph * p.stride_w + pw)]) continue;
+      const int64_t nh = ph < p.hi ? ceil_div(p.hi - ph, p.stride_h) : 0;
+      const int64_t nw = pw < p.wi ? ceil_div(p.wi - pw, p.stride_w) : 0;
+      if (nh * nw == 0) continue;
+      cbd_zero_region_t z;
+      z.phase_h = (int32_t)ph;
+      z.phase_w = (int32_t)pw;
+      z.pos_h = nh;
+      z.pos_w = nw;
+      zeros.push_back(z);
+    }
+  }
+
+  // Kernel arguments.
+  cbd::GemmArgs& a = pl->gemm;
+  a.N = (int32_t)p.n; a.G = (int32_t)p.g; a.C = (int32_t)p.c; a.K = (int32_t)p.k;
+  a.Cg = (int32_t)Cg; a.Kg = (int32_t)Kg;
+  a.Hi = (int32_t)p.hi; a.Wi = (int32_t)p.wi; a.Ho = (int32_t)Ho; a.Wo = (int32_t)Wo;
+  a.Y = (int32_t)p.y; a.X = (int32_t)p.x;
+  a.Sh = p.stride_h; a.Sw = p.stride_w;
+  a.tstep_h = (int32_t)ah.T; a.tstep_w = (int32_t)aw.T;
+  a.delta_h = (int32_t)ah.delta; a.delta_w = (int32_t)aw.delta;
+  a.dy_bytes = (uint32_t)(p.n * p.k * Ho * Wo * es);
+  a.w_bytes = (uint32_t)(p.k * Cg * p.y * p.x * es);
+  a.dx_bytes = (uint32_t)(p.n * p.c * p.hi * p.wi * es);
+  a.num_sub = (int32_t)subs.size();
+  a.total_tiles = (int32_t)tile;
+  a.tiles_m = (int32_t)tiles_m;
+  a.tile_n = (int32_t)(kernel == CBD_KERNEL_GROUPED ? slots * iters : bn);
+  // XCD-contiguous tile ranges pay when one panel is shared by many tiles;
+  // with unequal K they would also hand the long tiles to a few XCDs.
+  a.xcd_remap = (kernel != CBD_KERNEL_GROUPED && equal_k && tile >= 64) ? 1 : 0;
+  a.iters = (int32_t)iters;
+  for (size_t i = 0; i < subs.size(); i++) {
+    cbd::SubDesc& d = a.sub[i];
+    const cbd_subgemm_t& s = subs[i];
+    d.phase_h = s.phase_h; d.phase_w = s.phase_w;
+    d.beta_h = s.beta_h; d.beta_w = s.beta_w;
+    d.taps_h = s.taps_h; d.taps_w = s.taps_w;
+    d.cls_h = s.class_h; d.cls_w = s.class_w;
+    d.pos_h = (int32_t)s.pos_h; d.pos_w = (int32_t)s.pos_w;
+    d.tile_begin = (int32_t)s.tile_begin;
+  }
+
+  cbd::ZeroArgs& z = pl->zero;
+  z.N = (int32_t)p.n; z.C = (int32_t)p.c; z.Hi = (int32_t)p.hi; z.Wi = (int32_t)p.wi;
+  z.Sh = p.stride_h; z.Sw = p.stride_w;
+  z.layout = p.layout;
+  z.esize = (int32_t)es;
+  z.chunk = (p.layout == CBD_LAYOUT_NHWC && (p.c * es) % 16 == 0) ? 16 : (int32_t)es;
+  z.num_regions = (int32_t)zeros.size();
+  z.dx_bytes = a.dx_bytes;
+  int64_t items = 0, zero_elems = 0;
+  for (size_t i = 0; i < zeros.size(); i++) {
+    cbd::ZeroDesc& d = z.reg[i];
+    d.phase_h = zeros[i].phase_h; d.phase_w = zeros[i].phase_w;
+    d.pos_h = (int32_t)zeros[i].pos_h; d.pos_w = (int32_t)zeros[i].pos_w;
+    d.item_begin = items;
+    const int64_t npos = p.n * zeros[i].pos_h * zeros[i].pos_w;
+    items += p.layout == CBD_LAYOUT_NHWC ? npos * (p.c * es / z.chunk) : npos * p.c;
+    zero_elems += npos * p.c;
+  }
+  z.total_items = items;
+  if (items >= (int64_t(1) << 32)) {
+    delete pl;
+    return fail(CBD_ERR_UNSUPPORTED, "zero-fill grid too large");
+  }
+
+  cbd_plan_info_t& info = pl->info;
+  info.ho = Ho;
+  info.wo = Wo;
+  info.num_subgemms = (int32_t)subs.size();
+  info.num_zero_regions = (int32_t)zeros.size();
+  info.kernel = kernel;
+  info.tile_m = (int32_t)bm;
+  info.tile_n = (int32_t)a.tile_n;
+  info.tile_k = (int32_t)bk;
+  info.threads_main = (int32_t)threads;
+  info.grid_main = tile;
+  info.grid_zero = ceil_div(items, cbd::kZeroThreads);
+  info.launches = (tile > 0 ? 1 : 0) + (items > 0 ? 1 : 0);
+  info.useful_flops = 2 * p.n * p.c * Kg * Ho * Wo * p.y * p.x;
+  info.executed_macs = exec;
+  info.zero_elems = zero_elems;
+
+  pl->subs = std::move(subs);
+  pl->zeros = std::move(zeros);
+  *out_plan = pl;
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_plan(const cbd_problem* problem, cbd_plan_t** out_plan) {
+  return cbd_plan_ex(problem, nullptr, out_plan);
+}
+
+extern "C" void cbd_plan_destroy(cbd_plan_t* plan) { delete plan; }
+
+extern "C" cbd_status cbd_plan_info(const cbd_plan_t* plan, cbd_plan_info_t* out) {
+  if (!plan || !out) return fail(CBD_ERR_INVALID_ARG, "NULL plan or out");
+  *out = plan->info;
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_plan_subgemm(const cbd_plan_t* plan, int32_t i, cbd_subgemm_t* out) {
+  if (!plan || !out) return fail(CBD_ERR_INVALID_ARG, "NULL plan or out");
+  if (i < 0 || (size_t)i >= plan->subs.size()) return fail(CBD_ERR_INVALID_ARG, "sub-GEMM index out of range");
+  *out = plan->subs[(size_t)i];
+  return CBD_OK;
+}
+
+extern "C" cbd_status cbd_plan_zero_region(const cbd_plan_t* plan, int32_t i, cbd_zero_region_t* out) {
+  if (!plan || !out) return fail(CBD_ERR_INVALID_ARG, "NULL plan or out");
+  if (i < 0 || (size_t)i >= plan->zeros.size()) return fail(CBD_ERR_INVALID_ARG, "zero-region index out of range");
+  *out = plan->zeros[(size_t)i];
+  return CBD_OK;
+}

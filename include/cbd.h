@@ -1,0 +1,171 @@
+/*
+ * cbd.h -- 2-D convolution backward-data (dX = conv_bwd_data(dY, W)) on
+ * AMD Instinct MI355X (gfx950), computed as an implicit GEMM with one
+ * sub-GEMM per stride-residue class, all classes in a single launch.
+ *
+ * Plain C ABI: no C++ types, no exceptions, no torch types.  Every call
+ * returns a status code; nothing aborts.
+ *
+ * The operation.  For the forward convolution
+ *   y[n, g*K/G+k, ho, wo] = sum_{c, r, s} x[n, g*C/G+c, ho*Sh + r*Dh - Ph,
+ *                                            wo*Sw + s*Dw - Pw] * W[g*K/G+k, c, r, s]
+ * (zero padding), backward-data is its adjoint in x:
+ *   dX[n, g*C/G+c, hi, wi] = sum over k and over the taps (r, s) with
+ *   hi + Ph - r*Dh = ho*Sh, wi + Pw - s*Dw = wo*Sw, 0 <= ho < Ho, 0 <= wo < Wo
+ *   of dY[n, g*K/G+k, ho, wo] * W[g*K/G+k, c, r, s].
+ * dX positions that no tap reaches are written as +0.
+ *   - Problem fields and the gkcyx / ngchw / ngkhw layouts: rocMLIR PR #246
+ *     "Backward data", the driver command lines at the end of the thread
+ *     (batchsize, in/out channels, in_h/in_w, fil_h/fil_w, padding, stride,
+ *     dilation, groupsize).
+ *   - NHWC / KYXC layouts, bf16 operands with f32 accumulation and a bf16
+ *     result, the caller-provided output that is overwritten: fusilli issue
+ *     #101 "Non-unit stride input backward different input and dispatches
+ *     between BOO and Fusilli" (BOO listing; torch-IR listing's
+ *     convolution_backward call with output_mask [true, false, false]).
+ *   - One sub-GEMM per stride residue ("multi-kernels", consecutive gemm
+ *     ids, arguments reconstructed by the library rather than passed a
+ *     kernel id by the client): rocMLIR PR #246; the v4r1 backward-data
+ *     strategy named in MIOpen PR #272 "[igemm_dynamic] v4r1 bwd dynamic
+ *     kernel".  Here the classes share one launch.
+ *   - Plan first, then run (problem -> find solution -> load -> run): the
+ *     MIOpen workflow described in the debian-ai thread "MIOpen package LFS
+ *     files".
+ */
+#ifndef CBD_H
+#define CBD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CBD_OK = 0,
+  CBD_ERR_INVALID_ARG = 1, /* inconsistent problem, NULL pointer, bad index */
+  CBD_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels accept
+                              (sizes beyond 32-bit buffer addressing, stride
+                              product > 64, misaligned pointers)           */
+  CBD_ERR_HIP = 3,         /* HIP runtime / launch error; see cbd_last_error */
+  CBD_ERR_NO_MEMORY = 4    /* host allocation failed                        */
+} cbd_status;
+
+typedef enum { CBD_F32 = 0, CBD_BF16 = 1 } cbd_dtype; /* dY, W and dX share it;
+                                                          accumulation is f32 */
+
+typedef enum {
+  /* dX [N][G*C/G][Hi][Wi], dY [N][G*K/G][Ho][Wo], W [G*K/G][C/G][Y][X]
+     (ngchw / ngkhw / gkcyx; identical to NCHW / KCYX) */
+  CBD_LAYOUT_NCHW = 0,
+  /* dX [N][Hi][Wi][G*C/G], dY [N][Ho][Wo][G*K/G], W [G*K/G][Y][X][C/G]
+     (NHWC / KYXC) */
+  CBD_LAYOUT_NHWC = 1
+} cbd_layout;
+
+/* The problem.  c and k are TOTAL channel counts; g divides both.  Channel
+ * numbering is group-major (channel = g*(C/G) + c, filter row = g*(K/G) + k).
+ * Hi and Wi are given (never inferred from Ho/Wo); Ho and Wo follow as
+ * floor((Hi + 2*Ph - Dh*(Y-1) - 1) / Sh) + 1 and likewise for W. */
+typedef struct {
+  int64_t n, g, c, k, hi, wi, y, x;
+  int32_t stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+  int32_t layout; /* cbd_layout */
+  int32_t dtype;  /* cbd_dtype  */
+} cbd_problem;
+
+typedef struct cbd_plan_s cbd_plan_t; /* opaque; immutable once created */
+
+/* Kernel families a plan may use for its main (GEMM) launch. */
+typedef enum {
+  CBD_KERNEL_AUTO = -1,
+  CBD_KERNEL_GENERIC = 0,   /* any layout / dtype: gathered 64x64 tiles, f32 MFMA */
+  CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 64 == 0, C/G % 8 == 0:
+                               256x256x64 tiles, bf16 MFMA, double-buffered LDS */
+  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G in {1,2,4,8}, G | 256:
+                               direct per-group accumulation, filter in registers */
+} cbd_kernel;
+
+typedef struct {
+  int32_t force_kernel; /* cbd_kernel; CBD_KERNEL_AUTO lets the planner choose */
+  int32_t reserved[7];  /* must be zero */
+} cbd_plan_options;
+
+/* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
+ * heap object that the caller frees with cbd_plan_destroy.  Errors:
+ * INVALID_ARG for NULL arguments, non-positive sizes, G not dividing C or K,
+ * negative padding, Ho or Wo < 1, unknown layout or dtype; UNSUPPORTED for
+ * tensors of 2^31 bytes or more, stride_h*stride_w > 64, dilation > 64. */
+cbd_status cbd_plan(const cbd_problem* problem, cbd_plan_t** out_plan);
+
+/* As cbd_plan, with options (options may be NULL).  A forced kernel that
+ * cannot run the problem gives UNSUPPORTED. */
+cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* options,
+                       cbd_plan_t** out_plan);
+
+/* Run a plan.  dy, w and dx are DEVICE pointers to dense tensors in the
+ * plan's layout and dtype, owned by the caller; dy and w are read only, dx
+ * is fully overwritten and must not overlap dy or w.  stream is a
+ * hipStream_t (NULL = the default stream).  Asynchronous and stream-ordered:
+ * no host synchronisation, no allocation, no copies; safe to call from
+ * several threads on distinct streams.  Errors: INVALID_ARG for NULL plan or
+ * pointers; UNSUPPORTED for pointers not aligned to 16 bytes; HIP when a
+ * launch fails (detail in cbd_last_error()). */
+cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                   void* stream);
+
+/* Free a plan.  NULL is allowed. */
+void cbd_plan_destroy(cbd_plan_t* plan);
+
+/* Static description of a status code. */
+const char* cbd_status_string(cbd_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* cbd_last_error(void);
+
+/* ---- read-only introspection (tests, bench) ---- */
+
+typedef struct {
+  int64_t ho, wo;
+  int32_t num_subgemms;     /* stride-residue classes with taps and positions */
+  int32_t num_zero_regions; /* dX phase lattices that no tap reaches */
+  int32_t kernel;           /* cbd_kernel of the main launch */
+  int32_t tile_m, tile_n, tile_k;
+  int32_t threads_main;     /* workgroup size of the main launch */
+  int32_t launches;         /* kernels per cbd_run (1 or 2) */
+  int64_t grid_main;        /* workgroups of the main launch */
+  int64_t grid_zero;        /* workgroups of the zero-fill launch (0 if none) */
+  int64_t useful_flops;     /* 2*N*C*(K/G)*Ho*Wo*Y*X */
+  int64_t executed_macs;    /* sum over sub-GEMMs of G*M*N*K (valid-tap MACs
+                               plus those of taps falling off dY's edge) */
+  int64_t zero_elems;       /* dX elements written by the zero-fill launch */
+} cbd_plan_info_t;
+
+typedef struct {
+  int32_t id;               /* 0 .. num_subgemms-1, consecutive */
+  int32_t class_h, class_w; /* tap class i: taps i, i+T, i+2T, ... */
+  int32_t phase_h, phase_w; /* dX positions phase + S*t */
+  int32_t beta_h, beta_w;   /* dY row of tap j at position t: t + beta - delta*j */
+  int32_t taps_h, taps_w;   /* taps in the class */
+  int32_t tstep_h, tstep_w; /* T = S / gcd(S, D) */
+  int32_t delta_h, delta_w; /* delta = D / gcd(S, D) */
+  int64_t pos_h, pos_w;     /* positions per axis: ceil((Hi - phase) / S) */
+  int64_t m, n, k;          /* per-group GEMM: M = C/G, N = N*pos_h*pos_w,
+                               K = (K/G)*taps_h*taps_w */
+  int64_t tile_begin, tiles;/* this class's workgroups in the main launch */
+} cbd_subgemm_t;
+
+typedef struct {
+  int32_t phase_h, phase_w; /* lattice phase + S*t that no tap reaches */
+  int64_t pos_h, pos_w;
+} cbd_zero_region_t;
+
+cbd_status cbd_plan_info(const cbd_plan_t* plan, cbd_plan_info_t* out);
+cbd_status cbd_plan_subgemm(const cbd_plan_t* plan, int32_t i, cbd_subgemm_t* out);
+cbd_status cbd_plan_zero_region(const cbd_plan_t* plan, int32_t i, cbd_zero_region_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBD_H */

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+All twelve workload problems at full size, in the launch configuration the
+benchmark times (automatic kernel choice), plus every problem on the
+generic kernel family, integer-exact (bit-for-bit) runs, sentinel / guard /
+determinism checks, a non-default stream, and seeded fuzz over layouts,
+dtypes, groups, strides, dilations and padding for each kernel family.
+
+The large bf16 case (dY 16x1x256x2048, W 2048x1x2x2048) is checked element
+by element on sampled outputs the oracle computes one at a time, and on
+every output against its two-GEMM form (fp64 numpy matmul; that reduction
+is pinned against the oracle in test_oracle_pins.py).
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import dnn_conv2d_bwd_amd as cbd
+import oracle
+from cbd_inputs import PROBLEMS, small_ints, uniform
+from cbd_inputs.problems import NCHW, NHWC, Problem
+
+from parity import GpuRun, check, check_bf16, check_f32, exact_expected_bits, operands, \
+    plan_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [p.name for p in PROBLEMS if p.name != "c4"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def by_name(name):
+    return [p for p in PROBLEMS if p.name == name][0]
+
+
+def unreached_mask(p):
+    """Positions (h, w) of dX that no tap reaches (brute force)."""
+    ho_n, wo_n = oracle.out_hw(p)
+
+    def reach(i, pad, dil, taps, s, on):
+        return any((i + pad - t * dil) >= 0 and (i + pad - t * dil) % s == 0
+                   and (i + pad - t * dil) // s < on for t in range(taps))
+    rh = np.array([reach(h, p.ph, p.dh, p.y, p.sh, ho_n) for h in range(p.hi)])
+    rw = np.array([reach(w, p.pw, p.dw, p.x, p.sw, wo_n) for w in range(p.wi)])
+    return ~(rh[:, None] & rw[None, :])
+
+
+def spatial(p, a):
+    """(N, C, H, W) view of a layout-ordered dX array."""
+    return a if p.layout == NCHW else np.transpose(a, (0, 3, 1, 2))
+
+
+# --------------------------------------------------------------- workload ---
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("force", [cbd.KERNEL_AUTO, cbd.KERNEL_GENERIC])
+def test_workload_vs_oracle(name, force):
+    p = by_name(name)
+    print(f"[parity] {name} force={force}", flush=True)
+    dy, w = operands(p)
+    ref = oracle.bwd_data(p, dy, w)
+    pl = plan_for(p, force)
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    ok, info = check(p, run, ref)
+    assert ok, info
+    assert run.guards_intact()
+    got = run.result_f32()
+    assert not np.isnan(got).any()
+    z = unreached_mask(p)
+    if z.any():
+        assert np.all(spatial(p, got)[:, :, z] == 0.0)
+    if name == "c3b":
+        assert np.count_nonzero(got == 0.0) >= got.size * 3 // 4
+    bits1 = run.result_bits().copy()
+    run()
+    assert np.array_equal(bits1, run.result_bits()), "not deterministic"
+
+
+@pytest.mark.parametrize("name", [p.name for p in PROBLEMS])
+def test_workload_integer_exact(name):
+    p = by_name(name)
+    print(f"[exact] {name}", flush=True)
+    dy, w = operands(p, "int")
+    pl = plan_for(p)
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    got = run.result_f32()
+    if name == "c4":
+        # two plain GEMMs (pinned reduction): dX[:,0,r::2,:] = dY[:,0] @ W[:,0,r,:]
+        ref = np.empty(got.shape, dtype=np.float64)
+        for r in range(2):
+            ref[:, 0, r::2, :] = (dy[:, 0].reshape(-1, p.k).astype(np.float64)
+                                  @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
+    else:
+        ref = oracle.bwd_data(p, dy, w)
+    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, ref)) if p.dtype == "bf16" \
+        else exact_expected_bits(p, ref).view(np.float32)
+    assert np.array_equal(got, want.reshape(got.shape))
+    assert run.guards_intact()
+
+
+def test_c4_full_size():
+    """The headline bf16 problem: sampled oracle outputs plus the full tensor
+    against the two-GEMM form."""
+    p = by_name("c4")
+    print("[parity] c4 full size", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p)
+    assert pl.info().kernel == cbd.KERNEL_NHWC_BF16
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    bits = run.result_bits().reshape(p.n, p.hi, p.wi, p.c)
+    assert run.guards_intact()
+    # sampled outputs, one by one, from the oracle: every tile corner plus random points
+    rng = np.random.default_rng(44)
+    pts = [(n, c, 0, wi) for n in (0, p.n - 1) for c in (0, 255, 256, p.c - 1)
+           for wi in (0, 1, 510, 511)]
+    pts += list(zip(rng.integers(0, p.n, 4000), rng.integers(0, p.c, 4000),
+                    np.zeros(4000, dtype=np.int64), rng.integers(0, p.wi, 4000)))
+    pts = np.array(pts, dtype=np.int64)
+    ref_pts = oracle.bwd_data_at(p, dy, w, pts)
+    got_pts = bits[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ok, info = check_bf16(got_pts, ref_pts)
+    assert ok, info
+    # every output against the fp64 two-GEMM form
+    ref = np.empty((p.n, 1, p.wi, p.c), dtype=np.float64)
+    dy2 = dy[:, 0].reshape(-1, p.k).astype(np.float64)
+    for r in range(2):
+        ref[:, 0, r::2, :] = (dy2 @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
+    ok, info = check_bf16(bits, ref)
+    print("[parity] c4", info, flush=True)
+    assert ok, info
+    bits1 = bits.copy()
+    run()
+    assert np.array_equal(bits1, run.result_bits().reshape(bits1.shape))
+
+
+def test_non_default_stream():
+    p = by_name("c3a")
+    dy, w = operands(p)
+    ref = oracle.bwd_data(p, dy, w)
+    pl = plan_for(p)
+    s = torch.cuda.Stream()
+    dy_d, w_d = to_device(dy, p), to_device(w, p)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        run = GpuRun(p, pl, dy_d, w_d)
+        run(stream=s)
+    s.synchronize()
+    ok, info = check(p, run, ref)
+    assert ok, info
+
+
+def test_convenience_entry_matches_torch_layouts():
+    """conv2d_bwd_data with torch-style arguments (NCHW and NHWC)."""
+    p = by_name("c3a")
+    dy, w = operands(p)
+    ref = oracle.bwd_data(p, dy, w)
+    dx = cbd.conv2d_bwd_data(to_device(dy, p), to_device(w, p), (p.n, p.c, p.hi, p.wi),
+                             stride=2, padding=1, dilation=1, groups=1, layout="nchw")
+    ok, info = check_f32(dx.cpu().numpy(), ref)
+    assert ok, info
+
+
+# ------------------------------------------------------------------- fuzz ---
+
+def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), family=None):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        layout = rng.choice(layouts)
+        dtype = rng.choice(dtypes)
+        if family == cbd.KERNEL_NHWC_BF16:
+            g = rng.choice([1, 1, 2])
+            cg = 8 * rng.randint(1, 40)
+            kg = 64 * rng.randint(1, 3)
+            layout, dtype = NHWC, "bf16"
+        elif family == cbd.KERNEL_GROUPED:
+            cg = rng.choice([1, 2, 4, 8])
+            kg = cg
+            g = rng.choice([1, 2, 4, 8, 16, 32, 64])
+            layout = NHWC
+        else:
+            g = rng.randint(1, 4)
+            cg, kg = rng.randint(1, 40), rng.randint(1, 40)
+        p = Problem("fuzz", rng.randint(1, 3), g, g * cg, g * kg, rng.randint(1, 23),
+                    rng.randint(1, 23), rng.randint(1, 5), rng.randint(1, 5), rng.randint(1, 4),
+                    rng.randint(1, 4), rng.randint(0, 3), rng.randint(0, 3), rng.randint(1, 3),
+                    rng.randint(1, 3), layout, dtype, "u", "u", 0, 0)
+        if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
+                or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0):
+            continue
+        if family == cbd.KERNEL_GROUPED:
+            try:
+                if plan_for(p, family).info().kernel != family:
+                    continue
+            except cbd.CbdError:
+                continue
+        out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("family,seed,count", [
+    (cbd.KERNEL_GENERIC, 11, 150),
+    (cbd.KERNEL_NHWC_BF16, 12, 60),
+    (cbd.KERNEL_GROUPED, 13, 80),
+])
+def test_fuzz_integer_exact(family, seed, count):
+    for i, p in enumerate(fuzz_problems(seed, count, family=family)):
+        print(f"[fuzz] family={family} i={i} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(1000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(1000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
+        pl = plan_for(p, family)
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        ref = oracle.bwd_data(p, dy, w)
+        want = exact_expected_bits(p, ref)
+        want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), p
+        assert run.guards_intact(), p
+
+
+@pytest.mark.parametrize("family,seed,count", [
+    (cbd.KERNEL_GENERIC, 21, 60),
+    (cbd.KERNEL_NHWC_BF16, 22, 30),
+    (cbd.KERNEL_GROUPED, 23, 40),
+])
+def test_fuzz_random_values(family, seed, count):
+    for i, p in enumerate(fuzz_problems(seed, count, family=family)):
+        print(f"[fuzz-val] family={family} i={i} {p}", flush=True)
+        sh = oracle.shapes(p)
+        from cbd_inputs import to_dtype
+        dy = to_dtype(uniform(2000 * seed + 3 * i + 1, sh["dy"]), p.dtype)
+        w = to_dtype(uniform(2000 * seed + 3 * i + 2, sh["w"]), p.dtype)
+        pl = plan_for(p, family)
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        ok, info = check(p, run, oracle.bwd_data(p, dy, w))
+        assert ok, (p, info)

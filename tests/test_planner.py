@@ -1,0 +1,229 @@
+"""Host planner and C ABI tests (CPU only: cbd_plan needs no GPU).
+
+* Residue classes: tap sets, phases, dY offsets and position counts checked
+  against brute-force enumeration of the forward window.
+* Coverage: every dX position is written by exactly one sub-GEMM or one
+  zero region (the single-writer property the kernels rely on).
+* CPU plan executor: a literal evaluation of the plan's descriptors must
+  equal the oracle bit for bit on integer data, over random tiny problems
+  (groups, strides, dilations with gcd(S, D) > 1, padding, both layouts).
+* Boundary: invalid and unsupported problems, NULL / misaligned /
+  overlapping pointers, exported symbols, plan accounting.
+"""
+import ctypes
+import math
+import os
+import random
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import dnn_conv2d_bwd_amd as cbd
+import oracle
+from cbd_inputs import PROBLEMS, small_ints
+from cbd_inputs.problems import NCHW, NHWC, Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def tiny(rng, layouts=(NCHW, NHWC)):
+    while True:
+        g = rng.randint(1, 4)
+        p = Problem("t", rng.randint(1, 2), g, g * rng.randint(1, 3), g * rng.randint(1, 3),
+                    rng.randint(1, 11), rng.randint(1, 11), rng.randint(1, 5), rng.randint(1, 5),
+                    rng.randint(1, 4), rng.randint(1, 4), rng.randint(0, 3), rng.randint(0, 3),
+                    rng.randint(1, 4), rng.randint(1, 4), rng.choice(layouts), "f32", "int", "int",
+                    0, 0)
+        if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 >= 0
+                and p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 >= 0):
+            return p
+
+
+def plan_of(p, force=cbd.KERNEL_AUTO):
+    dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+    return cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                    (p.dh, p.dw), p.layout, dt, force_kernel=force)
+
+
+def execute_plan(pl, p, dy, w):
+    """Evaluate the plan's sub-GEMM descriptors and zero regions literally."""
+    info = pl.info()
+    ho_n, wo_n = info.ho, info.wo
+    cg, kg = p.c // p.g, p.k // p.g
+    if p.layout == NCHW:
+        dy4, w4 = dy, w
+    else:
+        dy4, w4 = np.transpose(dy, (0, 3, 1, 2)), np.transpose(w, (0, 3, 1, 2))
+    dx = np.full((p.n, p.c, p.hi, p.wi), np.nan)
+    writes = np.zeros((p.hi, p.wi), dtype=np.int64)
+    for s in pl.subgemms():
+        for th in range(s.pos_h):
+            for tw in range(s.pos_w):
+                hi, wi = s.phase_h + p.sh * th, s.phase_w + p.sw * tw
+                writes[hi, wi] += 1
+                acc = np.zeros((p.n, p.c))
+                for jh in range(s.taps_h):
+                    for jw in range(s.taps_w):
+                        ty, tx = s.class_h + s.tstep_h * jh, s.class_w + s.tstep_w * jw
+                        ho = th + s.beta_h - s.delta_h * jh
+                        wo = tw + s.beta_w - s.delta_w * jw
+                        if not (0 <= ho < ho_n and 0 <= wo < wo_n):
+                            continue
+                        for g in range(p.g):
+                            d = dy4[:, g * kg:(g + 1) * kg, ho, wo]          # (n, kg)
+                            wt = w4[g * kg:(g + 1) * kg, :, ty, tx]          # (kg, cg)
+                            acc[:, g * cg:(g + 1) * cg] += d @ wt
+                dx[:, :, hi, wi] = acc
+    for z in pl.zero_regions():
+        for a in range(z.pos_h):
+            for b in range(z.pos_w):
+                hi, wi = z.phase_h + p.sh * a, z.phase_w + p.sw * b
+                writes[hi, wi] += 1
+                dx[:, :, hi, wi] = 0.0
+    return (dx if p.layout == NCHW else np.transpose(dx, (0, 2, 3, 1))), writes
+
+
+def test_axis_classes_match_enumeration():
+    """For every class: its taps are exactly those reaching its phase, and
+    tap j at position t reads dY row t + beta - delta*j."""
+    rng = random.Random(1)
+    for _ in range(400):
+        p = tiny(rng)
+        pl = plan_of(p)
+        ho_n, wo_n = pl.info().ho, pl.info().wo
+        for s in pl.subgemms():
+            for axis in ("h", "w"):
+                S, D, P, F, L, O = ((p.sh, p.dh, p.ph, p.y, p.hi, ho_n) if axis == "h"
+                                    else (p.sw, p.dw, p.pw, p.x, p.wi, wo_n))
+                phase, cls = getattr(s, "phase_" + axis), getattr(s, "class_" + axis)
+                taps, T = getattr(s, "taps_" + axis), getattr(s, "tstep_" + axis)
+                beta, delta = getattr(s, "beta_" + axis), getattr(s, "delta_" + axis)
+                pos = getattr(s, "pos_" + axis)
+                assert T == S // math.gcd(S, D) and delta == D // math.gcd(S, D)
+                assert pos == len(range(phase, L, S))
+                want = {f for f in range(F) if (phase + P - f * D) % S == 0}
+                assert want == {cls + T * j for j in range(taps)}
+                for t in range(pos):
+                    h = phase + S * t
+                    for j in range(taps):
+                        f = cls + T * j
+                        assert (h + P - f * D) == S * (t + beta - delta * j)
+
+
+def test_plan_executor_matches_oracle_bitwise():
+    rng = random.Random(2)
+    for i in range(600):
+        p = tiny(rng)
+        sh = oracle.shapes(p)
+        dy, w = small_ints(10 * i + 1, sh["dy"]), small_ints(10 * i + 2, sh["w"])
+        pl = plan_of(p)
+        got, writes = execute_plan(pl, p, dy, w)
+        assert np.all(writes == 1), (p, writes)
+        assert np.array_equal(got, oracle.bwd_data(p, dy, w)), p
+
+
+def test_workload_plans():
+    expect = {  # (sub-GEMMs, zero regions, kernel)
+        "c1": (1, 0, cbd.KERNEL_GENERIC), "c3a": (4, 0, cbd.KERNEL_GENERIC),
+        "c3b": (1, 3, cbd.KERNEL_GENERIC), "c4": (2, 0, cbd.KERNEL_NHWC_BF16),
+        "c5-s2": (4, 0, cbd.KERNEL_GROUPED), "c5-s1": (1, 0, cbd.KERNEL_GROUPED),
+    }
+    for p in PROBLEMS:
+        pl = plan_of(p)
+        info = pl.info()
+        ho, wo = oracle.out_hw(p)
+        assert (info.ho, info.wo) == (ho, wo)
+        assert info.useful_flops == 2 * p.n * p.c * (p.k // p.g) * ho * wo * p.y * p.x
+        subs = pl.subgemms()
+        assert [s.id for s in subs] == list(range(len(subs)))
+        assert all(subs[i].k >= subs[i + 1].k for i in range(len(subs) - 1))  # LPT
+        tiles = 0
+        for s in subs:
+            assert s.tile_begin == tiles
+            tiles += s.tiles
+        assert tiles == info.grid_main
+        if p.name in expect:
+            assert (info.num_subgemms, info.num_zero_regions, info.kernel) == expect[p.name]
+    c4 = plan_of([q for q in PROBLEMS if q.name == "c4"][0])
+    assert [(s.m, s.n, s.k) for s in c4.subgemms()] == [(2048, 4096, 2048)] * 2
+    assert c4.info().grid_main == 256 and c4.info().executed_macs * 2 == c4.info().useful_flops
+    c3b = plan_of([q for q in PROBLEMS if q.name == "c3b"][0])
+    assert c3b.info().zero_elems == 32 * 64 * 28 * 28 * 3 // 4
+
+
+def test_forced_kernels():
+    c4 = [q for q in PROBLEMS if q.name == "c4"][0]
+    assert plan_of(c4, cbd.KERNEL_GENERIC).info().kernel == cbd.KERNEL_GENERIC
+    c1 = [q for q in PROBLEMS if q.name == "c1"][0]
+    with pytest.raises(cbd.CbdError) as e:
+        plan_of(c1, cbd.KERNEL_NHWC_BF16)
+    assert e.value.status == 2
+    with pytest.raises(cbd.CbdError) as e:
+        plan_of(c1, cbd.KERNEL_GROUPED)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n", 0, 1), ("g", 3, 1), ("c", -1, 1), ("stride_h", 0, 1), ("pad_w", -1, 1),
+    ("dil_w", 0, 1), ("layout", 7, 1), ("dtype", 9, 1), ("y", 40, 1),
+    ("stride_h", 9, 2), ("dil_h", 65, 2), ("n", 1 << 40, 2),
+])
+def test_invalid_and_unsupported(field, value, status):
+    prob = cbd.make_problem(2, 2, 8, 8, 16, 16, 3, 3, 2, 1, 1, "nchw", "f32")
+    setattr(prob, field, value)
+    if field == "stride_h" and value == 9:
+        prob.stride_w = 8  # 72 > 64 classes
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Plan(prob)
+    assert e.value.status == status
+    assert cbd._lib.cbd_last_error().decode() != ""
+
+
+def test_tensor_size_limit():
+    prob = cbd.make_problem(1024, 1, 1024, 8, 64, 64, 1, 1, 1, 0, 1, "nhwc", "f32")  # dX 16 GiB
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.Plan(prob)
+    assert e.value.status == 2
+
+
+def test_exports_and_null_handling():
+    L = ctypes.CDLL(cbd.LIB_PATH)
+    header = open(os.path.join(ROOT, "include", "cbd.h")).read()
+    for name in cbd.EXPORTS:
+        assert hasattr(L, name), name
+        assert name + "(" in header, name
+    # every function declared in the header is exported
+    import re
+    declared = set(re.findall(r"\b(cbd_[a-z_]+)\s*\(", header))
+    assert declared == set(cbd.EXPORTS)
+    assert cbd._lib.cbd_status_string(0) == b"CBD_OK"
+    assert cbd._lib.cbd_status_string(3) == b"CBD_ERR_HIP"
+    cbd._lib.cbd_plan_destroy(None)
+    assert cbd._lib.cbd_plan(None, None) == 1
+    pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32")
+    assert cbd._lib.cbd_plan_info(pl.handle, None) == 1
+    assert cbd._lib.cbd_plan_subgemm(pl.handle, 5, ctypes.byref(cbd.SubGemm())) == 1
+    assert cbd._lib.cbd_plan_zero_region(pl.handle, 0, ctypes.byref(cbd.ZeroRegion())) == 1
+    # run-time argument checks happen before any HIP call
+    base = 1 << 40
+    assert cbd.run_raw(pl, 0, base, base + (1 << 30)) == 1                   # NULL dy
+    assert cbd.run_raw(pl, base + 8, base + (1 << 28), base + (1 << 30)) == 2  # misaligned
+    assert cbd.run_raw(pl, base, base + (1 << 28), base + 64) == 1           # dx overlaps dy
+
+
+def test_run_without_device_returns_hip_error():
+    """On a machine with no GPU, cbd_run reports CBD_ERR_HIP instead of
+    aborting (run in a child process to keep this one clean)."""
+    code = (
+        "import dnn_conv2d_bwd_amd as cbd\n"
+        "pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, 'nchw', 'f32')\n"
+        "b = 1 << 40\n"
+        "st = cbd.run_raw(pl, b, b + (1 << 28), b + (1 << 30))\n"
+        "print('STATUS', st)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120, env={**os.environ, "HIP_VISIBLE_DEVICES": "-1"})
+    assert r.returncode == 0, r.stderr
+    assert "STATUS 3" in r.stdout, r.stdout + r.stderr
