@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark: 2-D convolution backward-data on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--problem NAME]
+
+Workload (default): the bf16 NHWC stride-(1,2) problem of fusilli issue #101
+-- dY 16x1x256x2048, W 2048x1x2x2048 (KYXC), dX 16x1x512x2048, fp32
+accumulation, bf16 result -- seeded synthetic N(0,1) / N(0,0.02) operands
+already resident in HBM.  One step = one cbd_run (every launch of the hot
+path: the residue-class GEMM kernel, plus the zero-fill kernel when the
+problem has unreached phases).
+
+Prints ONE JSON line:
+  value        useful TFLOP/s (2*N*C*(K/G)*Ho*Wo*Y*X per step, zero-insertion
+               work excluded) over the K timed steps, wall clock between two
+               device synchronisations;
+  roofline     dominant kernel: algorithmic flops (or bytes) per launch divided
+               by its mean launch duration from HIP events recorded on the
+               launch stream, against the bf16 dense MFMA peak (or HBM);
+               `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE +
+               WRITE_SIZE (profiles/, scaled by a plain copy of known size),
+               null when the kernel source changed after the counters were taken;
+  cpu_baseline the CPU oracle on the host cores over a bounded random sample of
+               the same problem's outputs, scaled to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv bwd-data useful TFLOP/s + µs/call on 1 MI355X, % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 2.4 GHz * 4096 dense bf16 flop/clk/CU
+PEAK_F32_TFLOPS = 157.3     # 256 CU * 2.4 GHz * 256 f32 MFMA flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = {0: "kern_igemm_generic.hip", 1: "kern_igemm_nhwc_bf16.hip",
+              2: "kern_grouped_direct.hip"}
+KERNEL_SYMBOL = {0: "igemm_generic_kernel", 1: "igemm_nhwc_bf16_kernel",
+                 2: "grouped_direct_kernel"}
+
+
+def describe(p):
+    lay = "NCHW/KCYX" if p.layout == 0 else "NHWC/KYXC"
+    return (f"conv2d_bwd_data {p.dtype} {lay} N={p.n} G={p.g} C={p.c} K={p.k} "
+            f"Hi={p.hi} Wi={p.wi} {p.y}x{p.x} stride=({p.sh},{p.sw}) pad=({p.ph},{p.pw}) "
+            f"dil=({p.dh},{p.dw})")
+
+
+def algorithmic_bytes(p, info):
+    """dY elements some valid tap reads + all of W + all of dX (zeros included)."""
+    es = 4 if p.dtype == "f32" else 2
+    ho, wo = info.ho, info.wo
+
+    def used(extent_out, extent_in, pad, dil, taps, stride):
+        return sum(1 for o in range(extent_out)
+                   if any(0 <= o * stride + t * dil - pad < extent_in for t in range(taps)))
+    dy_used = p.n * p.k * used(ho, p.hi, p.ph, p.dh, p.y, p.sh) * used(wo, p.wi, p.pw, p.dw, p.x, p.sw)
+    return es * (dy_used + p.k * (p.c // p.g) * p.y * p.x + p.n * p.c * p.hi * p.wi)
+
+
+def read_traffic(kernel_id):
+    """HBM bytes per launch recorded under profiles/ for this kernel, if the
+    kernel source still matches the one the counters were taken on."""
+    src = os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", KERNEL_SRC[kernel_id])
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SRC[kernel_id].split('.')[0]}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p, dy, w, info, target_s):
+    """Oracle over a bounded random sample of output elements, scaled."""
+    import numpy as np
+
+    import oracle
+
+    dy64 = np.ascontiguousarray(dy, dtype=np.float64)
+    w64 = np.ascontiguousarray(w, dtype=np.float64)
+    rng = np.random.default_rng(7)
+    total = p.n * p.c * p.hi * p.wi
+
+    def points(count):
+        return np.stack([rng.integers(0, p.n, count), rng.integers(0, p.c, count),
+                         rng.integers(0, p.hi, count), rng.integers(0, p.wi, count)], axis=1)
+    probe = min(total, 20000)
+    pts = points(probe)
+    t0 = time.perf_counter()
+    oracle.bwd_data_at(p, dy64, w64, pts)
+    dt = time.perf_counter() - t0
+    count = int(min(total, max(probe, probe * target_s / max(dt, 1e-6))))
+    pts = points(count)
+    t0 = time.perf_counter()
+    oracle.bwd_data_at(p, dy64, w64, pts)
+    dt = time.perf_counter() - t0
+    flops = info.useful_flops * count / total
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{count} random dX elements of {total} ({count / total:.2%}), "
+                      f"fp64 gather per element, {dt:.2f} s; useful flops scaled by the "
+                      f"sampled fraction"}
+
+
+def copy_calibration(nbytes, reps):
+    """A plain device copy of known size (for scaling rocprofv3 byte counters)."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--problem", default="c4")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain copy of this size (rocprofv3 counter scaling)")
+    ap.add_argument("--force-kernel", type=int, default=-1)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(backward-data shards by batch with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dnn_conv2d_bwd_amd as cbd
+    from cbd_inputs import draw, problem_by_name, seed_for
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    p = problem_by_name(args.problem)
+    dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+    pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                  (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel)
+    info = pl.info()
+    sh = pl.shapes()
+    dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
+    w = draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)
+    tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    dy_d = torch.from_numpy(dy).to(tdt).cuda()
+    w_d = torch.from_numpy(w).to(tdt).cuda()
+    dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib << 20, 5)
+
+    for _ in range(args.warmup):
+        cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    step_s = wall / args.steps
+    launch_s = float(np.mean(launch_ms)) / 1e3
+
+    flops = info.useful_flops
+    alg_bytes = algorithmic_bytes(p, info)
+    if info.kernel == cbd.KERNEL_GROUPED or p.name in ("c3b",):
+        roof = {"bound": "hbm", "achieved": round(alg_bytes / launch_s / 1e9, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(flops / launch_s / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = read_traffic(info.kernel)
+    roof["kernel"] = KERNEL_SYMBOL[info.kernel]
+    roof["launch_us_mean"] = round(launch_s * 1e6, 3)
+    roof["launches_per_step"] = info.launches
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / step_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 6),
+        "us_per_call": round(step_s * 1e6, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded SplitMix64 / Box-Muller operands, no dataset)",
+        "config": {"workload": describe(p), "problem": p.name,
+                   "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
+                   "zero_regions": info.num_zero_regions, "grid": info.grid_main,
+                   "useful_gflop": round(flops / 1e9, 4),
+                   "executed_gmac": round(info.executed_macs / 1e9, 4),
+                   "alg_mbytes": round(alg_bytes / 1e6, 3)},
+        "roofline": roof,
+        "gpu": torch.cuda.get_device_name(0) or "gfx950",
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,8 +15,8 @@
 //   * LDS rows of 8 16-byte chunks are XOR-swizzled (chunk ^ ((row ^
 //     row>>3) & 7)) so both the transposed writes and the MFMA fragment
 //     reads spread over all banks;
-//   * two LDS stages (2 x 64 KiB): the next tile's global loads are in
-//     flight while the current one feeds the MFMAs;
+//   * two LDS stages (2 x 64 KiB) and register fragments one k step ahead:
+//     global loads run two k tiles ahead of the MFMAs, LDS writes one;
 //   * taps off dY's edge and ragged M/N tiles read zeros through buffer
 //     record bounds; stores outside dX's class lattice are dropped the same
 //     way; the f32 -> bf16 rounding (nearest-even) is fused in the epilogue.
@@ -150,41 +150,57 @@ __global__ __launch_bounds__(kFastThreads, 1) void igemm_nhwc_bf16_kernel(const 
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  // Fragment read offsets (bytes within a stage) for k step 0; the chunk
-  // index for k step ks is 2*ks + (lane >> 5), XOR-ed with the row swizzle.
+  // Fragment rows (A: channel, B: position) of this lane; the 16-byte chunk
+  // for k step ks is 2*ks + (lane >> 5), XOR-ed with the row swizzle.
   int a_row_of[4], b_row_of[4];
 #pragma unroll
   for (int b = 0; b < 4; b++) {
     a_row_of[b] = wm * 128 + b * 32 + (lane & 31);
     b_row_of[b] = wn * 128 + b * 32 + (lane & 31);
   }
+  bf16x8 fa[2][4], fb[2][4];
+  auto load_frags = [&](int buf, const char* base, int ks) {
+    const int chunk = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ra_ = a_row_of[b], rb_ = b_row_of[b];
+      fa[buf][b] = *(const bf16x8*)(base + ra_ * ROWB + ((chunk ^ swz(ra_)) << 4));
+      fb[buf][b] = *(const bf16x8*)(base + ABYTES + rb_ * ROWB + ((chunk ^ swz(rb_)) << 4));
+    }
+  };
+  auto mfma_step = [&](int buf) {
+#pragma unroll
+    for (int bm = 0; bm < 4; bm++)
+#pragma unroll
+      for (int bn = 0; bn < 4; bn++)
+        acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][bm], fb[buf][bn],
+                                                              acc[bm][bn], 0, 0, 0);
+  };
 
+  // Software pipeline.  During k tile kt: LDS stage kt&1 feeds the MFMAs
+  // (fragments double-buffered in registers, one k step ahead); tile kt+1,
+  // loaded into registers during tile kt-1, is written to the other stage
+  // halfway through; then the global loads of tile kt+2 are issued.
   issue_loads(0);
   store_stage(0);
+  if (KT > 1) issue_loads(1);
   __syncthreads();
+  load_frags(0, smem, 0);
 
   for (int kt = 0; kt < KT; kt++) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) issue_loads(kt + 1);
     const char* base = smem + cur * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ks++) {
-      const int chunk = 2 * ks + (lane >> 5);
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int b = 0; b < 4; b++) {
-        const int ra_ = a_row_of[b], rb_ = b_row_of[b];
-        af[b] = *(const bf16x8*)(base + ra_ * ROWB + ((chunk ^ swz(ra_)) << 4));
-        bfr[b] = *(const bf16x8*)(base + ABYTES + rb_ * ROWB + ((chunk ^ swz(rb_)) << 4));
-      }
-#pragma unroll
-      for (int bm = 0; bm < 4; bm++)
-#pragma unroll
-        for (int bn = 0; bn < 4; bn++)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], bfr[bn], acc[bm][bn], 0, 0, 0);
-    }
+    load_frags(1, base, 1);
+    mfma_step(0);
+    load_frags(0, base, 2);
+    mfma_step(1);
     if (kt + 1 < KT) store_stage(cur ^ 1);
+    if (kt + 2 < KT) issue_loads(kt + 2);
+    load_frags(1, base, 3);
+    mfma_step(0);
+    mfma_step(1);
     __syncthreads();
+    if (kt + 1 < KT) load_frags(0, smem + (cur ^ 1) * STAGE, 0);
   }
 
   // Epilogue.  Lane holds, per 32x32 block, rows 8*(v>>2) + 4*(lane>>5) + (v&3)
