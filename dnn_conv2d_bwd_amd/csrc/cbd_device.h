@@ -29,6 +29,14 @@ __device__ inline uint32_t bf16_rne(float f) {
 
 __device__ inline float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
+// Two f32 -> packed bf16 (lo in bits 0-15), round to nearest even; gfx950
+// does this in one instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16_pack2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Logical tile of hardware workgroup b.  Workgroups are dealt round-robin to
 // the 8 XCDs (each with its own L2); with remap on, XCD x receives the
 // contiguous logical range [x*q + min(x, r), ...), so neighbouring tiles --

@@ -79,9 +79,9 @@ cbd_status fail(cbd_status st, const std::string& msg) {
   return st;
 }
 
-bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg) {
+bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
   return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Kg % cbd::kFastBK == 0 &&
-         Cg % 8 == 0;
+         Cg % 8 == 0 && max_taps <= cbd::kFastMaxTaps;
 }
 
 bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
@@ -184,7 +184,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   // Kernel family.
   int kernel;
   if (force == CBD_KERNEL_AUTO) {
-    if (fast_ok(p, Cg, Kg) && Cg >= 128)
+    if (fast_ok(p, Cg, Kg, max_taps) && Cg >= 128)
       kernel = CBD_KERNEL_NHWC_BF16;
     else if (grouped_ok(p, Cg, Kg, max_taps))
       kernel = CBD_KERNEL_GROUPED;
@@ -192,9 +192,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       kernel = CBD_KERNEL_GENERIC;
   } else {
     kernel = force;
-    if (kernel == CBD_KERNEL_NHWC_BF16 && !fast_ok(p, Cg, Kg)) {
+    if (kernel == CBD_KERNEL_NHWC_BF16 && !fast_ok(p, Cg, Kg, max_taps)) {
       delete pl;
-      return fail(CBD_ERR_UNSUPPORTED, "NHWC bf16 kernel needs NHWC, bf16, K/G % 64 == 0, C/G % 8 == 0");
+      return fail(CBD_ERR_UNSUPPORTED, "NHWC bf16 kernel needs NHWC, bf16, K/G % 64 == 0, C/G % 8 == 0, <= 16 taps per class");
     }
     if (kernel == CBD_KERNEL_GROUPED && !grouped_ok(p, Cg, Kg, max_taps)) {
       delete pl;

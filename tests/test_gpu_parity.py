@@ -196,7 +196,7 @@ def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), 
         if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
                 or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0):
             continue
-        if family == cbd.KERNEL_GROUPED:
+        if family in (cbd.KERNEL_GROUPED, cbd.KERNEL_NHWC_BF16):
             try:
                 if plan_for(p, family).info().kernel != family:
                     continue
