@@ -142,19 +142,26 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
 
   uint32_t dma_off[DMA_PER_TILE];
   lds_char* dma_st = (lds_char*)stage0;
+  int cur_tap = -1;
+  uint32_t a_tap = 0, b_tap[2] = {0, 0};  // per-tap bases, refreshed when the tap changes
   auto prepare_dma = [&](int kt) {
     const int tap = kt / kpt;
     const int k0 = (kt - tap * kpt) * BK;
-    const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
-    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-    const uint32_t a_base = (uint32_t)(((g * a.Kg + k0) * YX + ty * a.X + tx) * a.Cg) * 2u;
+    if (tap != cur_tap) {  // uniform branch, taken once per tap
+      cur_tap = tap;
+      const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
+      const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+      a_tap = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
+#pragma unroll
+      for (int i = 0; i < 2; i++) b_tap[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
+    }
     dma_st = (lds_char*)stage_ptr(kt % NSTAGE);
     // Whole offsets go in the per-lane operand, so the record-count check
     // sees every byte a lane touches.
 #pragma unroll
-    for (int i = 0; i < 2; i++) dma_off[i] = a_lane[i] + a_base;
+    for (int i = 0; i < 2; i++) dma_off[i] = a_lane[i] + a_tap + (uint32_t)k0 * wrow;
 #pragma unroll
-    for (int i = 0; i < 2; i++) dma_off[2 + i] = gtab[tap * BN + b_row[i]] + b_chunk[i] + (uint32_t)k0 * 2u;
+    for (int i = 0; i < 2; i++) dma_off[2 + i] = b_tap[i] + (uint32_t)k0 * 2u;
   };
   auto issue_one = [&](int j) {
     if (j < 2)
