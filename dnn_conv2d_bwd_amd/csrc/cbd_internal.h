@@ -29,7 +29,7 @@ const char* hip_error_name(int err);
 
 // Tile shapes of each kernel family (the planner sizes grids with them).
 constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;
-constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 512, kFastMaxTaps = 16;
+constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 256, kFastMaxTaps = 16;
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
 constexpr int kZeroThreads = 256, kZeroItemsPerThread = 4;
 

@@ -3,11 +3,11 @@
 // BOO listing in fusilli issue #101: extf to f32, mulf/addf, truncf).
 //
 // Same per-residue-class GEMM as the generic family (kern_igemm_generic.hip),
-// specialised for C/G % 8 == 0 and K/G % 64 == 0, laid out for gfx950:
+// specialised for C/G % 8 == 0 and K/G % 32 == 0, laid out for gfx950:
 //   * 256(M = c) x 256(N = positions) workgroup tiles, 32-wide k tiles;
-//     512 threads = 8 waves in 2(M) x 4(N), each wave 128x64 = 4x2 blocks of
-//     v_mfma_f32_32x32x16_bf16; two waves share each SIMD, so one wave's
-//     memory-instruction stalls are covered by the other's MFMAs;
+//     256 threads = 4 waves in 2(M) x 2(N), one per SIMD, each wave
+//     128x128 = 4x4 blocks of v_mfma_f32_32x32x16_bf16 with the 256 f32
+//     accumulators in AGPRs;
 //   * both operands travel global -> LDS by buffer_load ... lds (no VGPR
 //     staging, no VALU, no ds_write): lane l of an instruction fills 16 bytes
 //     at slot l of a 1 KiB LDS block, so the row swizzle is applied by
@@ -16,12 +16,12 @@
 //     operand with ds_read_b128; W rows (k, 256 c = 512 B) stay c-contiguous
 //     and ds_read_b64_tr_b16 transposes 4x4 bf16 blocks on the way out, giving
 //     each lane the k-vector of one channel (MFMA A operand);
-//   * XOR swizzles: dY chunk ^ ((row>>1 ^ row>>3) & 3), W chunk ^ 2*(row & 3),
-//     so fragment reads hit every bank once;
-//   * four 32 KiB LDS stages, loads three k tiles ahead; each wave's four
-//     load instructions of a tile are spread between its MFMAs; one barrier
-//     per k tile (explicit vmcnt waits: the only vector-memory ops in the loop
-//     are these loads);
+//   * bank-conflict-free XOR swizzles for both fragment reads;
+//   * four 32 KiB LDS stages, loads three to four k tiles ahead; one barrier
+//     per k tile, placed between its two k steps, so the fragments of the
+//     next step are always read one step ahead of the MFMAs that use them;
+//     the issue order (one fragment read after each MFMA, one load after
+//     every fourth) is pinned with scheduling barriers;
 //   * per-tap dY gather offsets (position -> byte offset, or out of range for
 //     taps off dY's edge and ragged tiles) and per-position dX offsets are
 //     built once per workgroup into small LDS tables;
@@ -42,27 +42,33 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int BM = kFastBM, BN = kFastBN, BK = kFastBK;  // 256, 256, 32
-constexpr int THREADS = kFastThreads;                    // 512
+constexpr int THREADS = kFastThreads;                    // 256: 4 waves, one per SIMD
 constexpr int NSTAGE = 4;
 constexpr int AROW = BM * 2;                             // 512 B: one k row of the W tile
 constexpr int BROW = BK * 2;                             // 64 B: one position row of the dY tile
 constexpr int ABYTES = BK * AROW;                        // 16 KiB
 constexpr int STAGE = ABYTES + BN * BROW;                // 32 KiB
 constexpr int MAX_TAPS = kFastMaxTaps;                   // gather-table capacity (taps per class)
-constexpr int DMA_PER_TILE = 4;                          // per wave: 2 W + 2 dY instructions
+constexpr int DMA_PER_TILE = 8;                          // per wave: 4 W + 4 dY instructions
 static_assert(THREADS / 64 * DMA_PER_TILE * 1024 == STAGE, "one stage = all waves' loads of a tile");
 static_assert(THREADS >= BN, "one thread per position row builds the tables");
 
 // s_waitcnt immediate: vmcnt <= n, other counters unconstrained (gfx9 encoding).
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
-__device__ inline int swz_w(int row) { return 2 * (row & 3); }                  // 32 chunks/row
-__device__ inline int swz_y(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }  // 4 chunks/row
+// LDS swizzles (16-byte chunk index XOR a function of the row).  gfx950 LDS
+// has 64 four-byte banks; a ds_read_b64(_tr) serves lanes 0-31, then 32-63,
+// 256 bytes per clock, and a ds_read_b128 serves 16 lanes per clock.  With
+// these maps every fragment read below touches each bank once per clock
+// (verified with the SQ_LDS_BANK_CONFLICT counter).
+__device__ inline int swz_w(int row) { return 4 * (row & 3); }  // W rows: 32 chunks
+__device__ inline int swz_y(int row) { return (row >> 2) & 3; }  // dY rows: 4 chunks
 
 __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmArgs a) {
   // Stages as distinct objects: the compiler can then see that fragment reads
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 64-position quarter
+  const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 128-position half
 
   const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
   const SubDesc s = a.sub[dev::find_class(a, t)];
@@ -93,8 +99,12 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int n0 = (rem / a.tiles_m) * BN;
   const int ntaps = s.taps_h * s.taps_w;
 
-  const auto rdy = dev::rsrc(a.dy, a.dy_bytes);
-  const auto rw = dev::rsrc(a.w, a.w_bytes);
+  // Buffer descriptors of dY and W as plain SGPR quads (the loads below are
+  // written in assembly), record count = tensor bytes as in dev::rsrc.
+  const i32x4 dyd = {(int)(uint32_t)(uintptr_t)a.dy, (int)(((uintptr_t)a.dy >> 32) & 0xffff),
+                     (int)a.dy_bytes, 0x00020000};
+  const i32x4 dw = {(int)(uint32_t)(uintptr_t)a.w, (int)(((uintptr_t)a.w >> 32) & 0xffff),
+                    (int)a.w_bytes, 0x00020000};
   const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
 
   // ---- per-workgroup tables (threads 0..255: one position row each)
@@ -121,62 +131,76 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int kpt = a.Kg / BK;
   const int KT = ntaps * kpt;
 
-  // ---- load roles.  W: instruction i (0, 1) of wave w fills k rows
-  // 4w + 2i + (lane >> 5), 16-byte slot lane & 31 holding channel chunk
+  // ---- load roles.  W: instruction i (0..3) of wave w fills k rows
+  // 8w + 2i + (lane >> 5), 16-byte slot lane & 31 holding channel chunk
   // (lane & 31) ^ swz_w(row).  dY: instruction i fills position rows
-  // 16*(2w + i) + (lane >> 2), slot lane & 3 holding k chunk (lane & 3) ^ swz_y(row).
-  uint32_t a_lane[2];
+  // 16*(4w + i) + (lane >> 2), slot lane & 3 holding k chunk (lane & 3) ^ swz_y(row).
+  uint32_t a_lane[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int row = 4 * wave + 2 * i + (lane >> 5);
+  for (int i = 0; i < 4; i++) {
+    const int row = 8 * wave + 2 * i + (lane >> 5);
     const int c = m0 + 8 * ((lane & 31) ^ swz_w(row));
     a_lane[i] = c < a.Cg ? (uint32_t)row * wrow + (uint32_t)c * 2u : dev::kOOB;
   }
-  int b_row[2];
-  uint32_t b_chunk[2];
+  int b_row[4];
+  uint32_t b_chunk[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    b_row[i] = 16 * (2 * wave + i) + (lane >> 2);
+  for (int i = 0; i < 4; i++) {
+    b_row[i] = 16 * (4 * wave + i) + (lane >> 2);
     b_chunk[i] = (uint32_t)(((lane & 3) ^ swz_y(b_row[i])) * 16);
   }
 
   uint32_t dma_off[DMA_PER_TILE];
-  lds_char* dma_st = (lds_char*)stage0;
-  int cur_tap = -1;
-  uint32_t a_tap = 0, b_tap[2] = {0, 0};  // per-tap bases, refreshed when the tap changes
+  int nx_tap = 0, nx_k0 = 0;  // (tap, k offset) of the next tile to prepare
+  uint32_t a_tap = 0, b_tap[4] = {0, 0, 0, 0};  // per-tap bases, refreshed when the tap changes
+  // Load offsets of tile kt.  Tiles past the end get out-of-range offsets:
+  // their loads write zeros into a stage that is no longer read, which keeps
+  // the count of loads in flight the same on every tile.
   auto prepare_dma = [&](int kt) {
-    const int tap = kt / kpt;
-    const int k0 = (kt - tap * kpt) * BK;
-    if (tap != cur_tap) {  // uniform branch, taken once per tap
-      cur_tap = tap;
+    const int tap = nx_tap, k0 = nx_k0;
+    const bool live = kt < KT;
+    if (live && k0 == 0) {  // uniform branch, taken once per tap
       const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
       const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
       a_tap = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
 #pragma unroll
-      for (int i = 0; i < 2; i++) b_tap[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
+      for (int i = 0; i < 4; i++) b_tap[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
     }
-    dma_st = (lds_char*)stage_ptr(kt % NSTAGE);
     // Whole offsets go in the per-lane operand, so the record-count check
     // sees every byte a lane touches.
 #pragma unroll
-    for (int i = 0; i < 2; i++) dma_off[i] = a_lane[i] + a_tap + (uint32_t)k0 * wrow;
+    for (int i = 0; i < 4; i++) dma_off[i] = live ? a_lane[i] + a_tap + (uint32_t)k0 * wrow : dev::kOOB;
 #pragma unroll
-    for (int i = 0; i < 2; i++) dma_off[2 + i] = b_tap[i] + (uint32_t)k0 * 2u;
+    for (int i = 0; i < 4; i++) dma_off[4 + i] = live ? b_tap[i] + (uint32_t)k0 * 2u : dev::kOOB;
+    nx_k0 = k0 + BK == a.Kg ? 0 : k0 + BK;
+    nx_tap = k0 + BK == a.Kg ? tap + 1 : tap;
   };
-  auto issue_one = [&](int j) {
-    if (j < 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(dma_st + (2 * wave + j) * 1024), 16,
-                                               dma_off[j], 0, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rdy, (lds_void*)(dma_st + ABYTES + (2 * wave + j - 2) * 1024),
-                                               16, dma_off[j], 0, 0, 0);
+  // Load j of a tile: 64 lanes x 16 bytes, global -> LDS without VGPRs
+  // (buffer_load ... lds; lane l writes 16 bytes at M0 + 16 l).  Written in
+  // assembly so that the compiler does not add its own conservative vmcnt
+  // waits before fragment reads of other stages: the waits that order these
+  // loads against LDS reads are the explicit ones in the main loop and
+  // before the epilogue.
+  auto issue_one = [&](auto dstc, int j) {
+    constexpr int DS = decltype(dstc)::value;
+    lds_char* dma_st = (lds_char*)(DS == 0 ? stage0 : DS == 1 ? stage1 : DS == 2 ? stage2 : stage3);
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(dma_st + (j < 4 ? (4 * wave + j) * 1024 : ABYTES + (4 * wave + j - 4) * 1024)));
+    const uint32_t voff = dma_off[j];
+    const i32x4 desc = j < 4 ? dw : dyd;
+    // M0 is listed as clobbered; nothing else in this kernel uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
+                 :: "s"(m0v), "v"(voff), "s"(desc) : "memory", "m0");
+#pragma clang diagnostic pop
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < 4; j++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
@@ -197,78 +221,93 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
         a_rd[bm][ks][h] = row * AROW + ((lc ^ swz_w(row)) << 4) + ((jl & 1) << 3);
       }
   }
-  // B: lane reads chunk 2*ks + (lane >> 5) of position row wn*64 + 32*bn + (lane & 31).
-  int b_rd[2][2];
+  // B: lane reads chunk 2*ks + (lane >> 5) of position row wn*128 + 32*bn + (lane & 31).
+  int b_rd[4][2];
 #pragma unroll
-  for (int bn = 0; bn < 2; bn++) {
-    const int row = wn * 64 + bn * 32 + (lane & 31);
+  for (int bn = 0; bn < 4; bn++) {
+    const int row = wn * 128 + bn * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
       b_rd[bn][ks] = ABYTES + row * BROW + (((2 * ks + (lane >> 5)) ^ swz_y(row)) << 4);
   }
 
-  // One k tile: 2 k steps x (4 A fragments, 2 B fragments, 8 MFMAs); the
-  // wave's 4 load instructions for a future tile go after MFMA pairs.
-  auto compute = [&](auto stc, bool dma) {
+  // Read r (0..11) of the fragments of k step ks, in the order the next
+  // k step consumes them: A block 0 (two transposed halves), B blocks 0-3,
+  // then A blocks 1-3.
+  auto read_one = [&](auto stc, int ks, int r, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
     constexpr int ST = decltype(stc)::value;
     lds_char* st = (lds_char*)(ST == 0 ? stage0 : ST == 1 ? stage1 : ST == 2 ? stage2 : stage3);
     const char* sb = ST == 0 ? stage0 : ST == 1 ? stage1 : ST == 2 ? stage2 : stage3;
+    if (r >= 2 && r < 6) {
+      fb[r - 2] = *(const bf16x8*)(sb + b_rd[r - 2][ks]);
+    } else {
+      const int i = r < 2 ? 0 : (r - 4) >> 1, h = r & 1;
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(st + a_rd[i][ks][h]));
+      if (h == 0) { fa[i][0] = v[0]; fa[i][1] = v[1]; fa[i][2] = v[2]; fa[i][3] = v[3]; }
+      else { fa[i][4] = v[0]; fa[i][5] = v[1]; fa[i][6] = v[2]; fa[i][7] = v[3]; }
+    }
+  };
+  // 16 MFMAs on (fa, fb); one fragment read of the next k step after each
+  // of the first 12, one load after every fourth.  The order is pinned
+  // with scheduling barriers.
+  auto half = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], auto rstc, int rks,
+                  bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      bf16x8 fa[4], fb[2];
-#pragma unroll
-      for (int bm = 0; bm < 4; bm++) {
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(st + a_rd[bm][ks][0]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(st + a_rd[bm][ks][1]));
-        fa[bm] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-#pragma unroll
-      for (int bn = 0; bn < 2; bn++) fb[bn] = *(const bf16x8*)(sb + b_rd[bn][ks]);
-#pragma unroll
-      for (int bm = 0; bm < 4; bm++) {
-#pragma unroll
-        for (int bn = 0; bn < 2; bn++)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
-        if (dma && (bm & 1)) issue_one(2 * ks + (bm >> 1));
-      }
+    for (int q = 0; q < 16; q++) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q >> 2], fb[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+      if (q < 12) read_one(rstc, rks, q, ra, rb);
+      if ((q & 3) == 3) issue_one(dstc, j0 + (q >> 2));
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- main loop: tiles kt+1, kt+2 in flight while tile kt computes.
+  // ---- main loop.  Iteration kt: k step 0 of tile kt (fragments already in
+  // registers) issues the second half of tile kt+3's loads; then, once tile
+  // kt+1 has landed and every wave has finished reading tile kt (barrier),
+  // the first fragments of tile kt+1 are read while k step 1 of tile kt
+  // issues the first half of tile kt+4's loads into tile kt's stage.
+  prepare_dma(0);
 #pragma unroll
-  for (int s0 = 0; s0 < NSTAGE - 1; s0++)
-    if (s0 < KT) {
-      prepare_dma(s0);
+  for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 0>(), j);
+  prepare_dma(1);
 #pragma unroll
-      for (int j = 0; j < DMA_PER_TILE; j++) issue_one(j);
-    }
-  auto step = [&](int kt, auto stc) {
-    // This wave's loads of tile kt have landed once at most `later` newer
-    // tiles' loads are outstanding; the barrier extends that to every wave
-    // and guarantees nobody still reads tile kt-1's stage.
-    const int later = (KT - 1 - kt) < (NSTAGE - 2) ? (KT - 1 - kt) : (NSTAGE - 2);
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * DMA_PER_TILE));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA_PER_TILE));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 1>(), j);
+  prepare_dma(2);
+#pragma unroll
+  for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 2>(), j);
+  prepare_dma(3);
+#pragma unroll
+  for (int j = 0; j < DMA_PER_TILE / 2; j++) issue_one(std::integral_constant<int, 3>(), j);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * DMA_PER_TILE + DMA_PER_TILE / 2));
+  __builtin_amdgcn_s_barrier();
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+#pragma unroll
+  for (int r = 0; r < 12; r++) read_one(std::integral_constant<int, 0>(), 0, r, fa0, fb0);
+  auto iter = [&](int kt, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    half(fa0, fb0, stc, 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(), DMA_PER_TILE / 2);
+    prepare_dma(kt + NSTAGE);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE));
     __builtin_amdgcn_s_barrier();
-    const bool dma = kt + NSTAGE - 1 < KT;
-    if (dma) prepare_dma(kt + NSTAGE - 1);  // into the stage of tile kt-1
-    compute(stc, dma);
+    half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0);
   };
   for (int kt = 0; kt < KT; kt += NSTAGE) {
-    step(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < KT) step(kt + 1, std::integral_constant<int, 1>());
-    if (kt + 2 < KT) step(kt + 2, std::integral_constant<int, 2>());
-    if (kt + 3 < KT) step(kt + 3, std::integral_constant<int, 3>());
+    iter(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < KT) iter(kt + 1, std::integral_constant<int, 1>());
+    if (kt + 2 < KT) iter(kt + 2, std::integral_constant<int, 2>());
+    if (kt + 3 < KT) iter(kt + 3, std::integral_constant<int, 3>());
   }
 
+  // The loads past the last tile (zeros into free stages) must land before
+  // the stages are reused for the C tile.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   // ---- epilogue.  C tile [position row][256 channels] bf16 = 128 KiB over
   // the four stages (64 rows each), 16-byte chunk c/8 of row r stored at
   // chunk (c/8) ^ (r & 31).
   __syncthreads();
 #pragma unroll
-  for (int bn = 0; bn < 2; bn++) {
-    const int prow = wn * 64 + bn * 32 + (lane & 31);
+  for (int bn = 0; bn < 4; bn++) {
+    const int prow = wn * 128 + bn * 32 + (lane & 31);
     char* rowp = stage_ptr(prow >> 6) + (prow & 63) * 512;
 #pragma unroll
     for (int bm = 0; bm < 4; bm++) {
