@@ -30,6 +30,7 @@ const char* hip_error_name(int err);
 // Tile shapes of each kernel family (the planner sizes grids with them).
 constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;
 constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 256, kFastMaxTaps = 16;
+constexpr int kFastMaxKTiles = 4096;  // k tiles per tap (K/G / 32): bound of the kernel's tap division
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
 constexpr int kZeroThreads = 256, kZeroItemsPerThread = 4;
 

@@ -81,7 +81,8 @@ cbd_status fail(cbd_status st, const std::string& msg) {
 
 bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
   return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Kg % cbd::kFastBK == 0 &&
-         Cg % 8 == 0 && max_taps <= cbd::kFastMaxTaps;
+         Kg <= (int64_t)cbd::kFastBK * cbd::kFastMaxKTiles && Cg % 8 == 0 &&
+         max_taps <= cbd::kFastMaxTaps;
 }
 
 bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {

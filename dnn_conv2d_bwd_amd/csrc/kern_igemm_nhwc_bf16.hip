@@ -17,11 +17,15 @@
 //     and ds_read_b64_tr_b16 transposes 4x4 bf16 blocks on the way out, giving
 //     each lane the k-vector of one channel (MFMA A operand);
 //   * bank-conflict-free XOR swizzles for both fragment reads;
-//   * four 32 KiB LDS stages, loads three to four k tiles ahead; one barrier
-//     per k tile, placed between its two k steps, so the fragments of the
-//     next step are always read one step ahead of the MFMAs that use them;
-//     the issue order (one fragment read after each MFMA, one load after
-//     every fourth) is pinned with scheduling barriers;
+//   * four 32 KiB LDS stages (W parts at [0, 64 KiB), dY parts above, so
+//     every fragment read is a base register plus a 16-bit immediate);
+//     loads run three to four k tiles ahead; one barrier per k tile, placed
+//     between its two k steps, so the fragments of the next step are always
+//     read one step ahead of the MFMAs that use them;
+//   * a wave issues at most one instruction per four clocks and each VALU
+//     instruction between MFMAs costs MFMA time, so the loop carries only
+//     MFMAs, fragment reads, loads and one add per load offset per tile;
+//     the issue order is pinned with scheduling barriers;
 //   * per-tap dY gather offsets (position -> byte offset, or out of range for
 //     taps off dY's edge and ragged tiles) and per-position dX offsets are
 //     built once per workgroup into small LDS tables;
@@ -51,8 +55,10 @@ constexpr int THREADS = kFastThreads;                    // 256: 4 waves, one pe
 constexpr int NSTAGE = 4;
 constexpr int AROW = BM * 2;                             // 512 B: one k row of the W tile
 constexpr int BROW = BK * 2;                             // 64 B: one position row of the dY tile
-constexpr int ABYTES = BK * AROW;                        // 16 KiB
-constexpr int STAGE = ABYTES + BN * BROW;                // 32 KiB
+constexpr int ABYTES = BK * AROW;                        // 16 KiB: W part of a stage
+constexpr int BBYTES = BN * BROW;                        // 16 KiB: dY part of a stage
+constexpr int STAGE = ABYTES + BBYTES;                   // 32 KiB
+constexpr int BBASE = NSTAGE * ABYTES;                   // dY parts follow the four W parts
 constexpr int MAX_TAPS = kFastMaxTaps;                   // gather-table capacity (taps per class)
 constexpr int DMA_PER_TILE = 8;                          // per wave: 4 W + 4 dY instructions
 static_assert(THREADS / 64 * DMA_PER_TILE * 1024 == STAGE, "one stage = all waves' loads of a tile");
@@ -73,15 +79,13 @@ __device__ inline int swz_y(int row) { return (row >> 2) & 3; }  // dY rows: 4 c
 __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmArgs a) {
   // Stages as distinct objects: the compiler can then see that fragment reads
   // of one stage do not alias the loads in flight into another.
-  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage3[STAGE];
+  // W parts of the four stages at [0, 64 KiB), dY parts at [64, 128 KiB):
+  // every fragment read is then one of a few base registers plus an
+  // immediate below 64 KiB.
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
   __shared__ uint32_t gtab[MAX_TAPS * BN];  // dY byte offset of (tap, position row), channel g*Kg
   __shared__ uint32_t otab[BN];             // dX byte offset of position row, channel g*Cg + m0
-  auto stage_ptr = [&](int st) -> char* {
-    return st == 0 ? stage0 : st == 1 ? stage1 : st == 2 ? stage2 : stage3;
-  };
+  __shared__ uint32_t atab[MAX_TAPS];       // W byte offset of (tap, k row 0), channel g*Cg
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 128-position half
@@ -106,6 +110,13 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const i32x4 dw = {(int)(uint32_t)(uintptr_t)a.w, (int)(((uintptr_t)a.w >> 32) & 0xffff),
                     (int)a.w_bytes, 0x00020000};
   const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+  // Uniform loop bounds, fixed before the divergent table build (values
+  // first defined inside a divergent region would live in VGPRs).
+  const int YX = __builtin_amdgcn_readfirstlane(a.Y * a.X);
+  const uint32_t wrow = __builtin_amdgcn_readfirstlane((uint32_t)(YX * a.Cg) * 2u);  // bytes between k rows of W
+  const int kpt = __builtin_amdgcn_readfirstlane(a.Kg / BK);
+  const int KT = __builtin_amdgcn_readfirstlane(ntaps * kpt);
+  const uint32_t kpt_magic = __builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)kpt + 1u);
 
   // ---- per-workgroup tables (threads 0..255: one position row each)
   if (tid < BN) {
@@ -124,12 +135,13 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
     otab[tid] = pv ? (uint32_t)(((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg + m0) * 2u : dev::kOOB;
   }
+  if (tid < ntaps) {
+    const int jh = tid / s.taps_w, jw = tid - (tid / s.taps_w) * s.taps_w;
+    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+    atab[tid] = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
+  }
   __syncthreads();
 
-  const int YX = a.Y * a.X;
-  const uint32_t wrow = (uint32_t)(YX * a.Cg) * 2u;  // bytes between consecutive k rows of W
-  const int kpt = a.Kg / BK;
-  const int KT = ntaps * kpt;
 
   // ---- load roles.  W: instruction i (0..3) of wave w fills k rows
   // 8w + 2i + (lane >> 5), 16-byte slot lane & 31 holding channel chunk
@@ -150,50 +162,89 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     b_chunk[i] = (uint32_t)(((lane & 3) ^ swz_y(b_row[i])) * 16);
   }
 
-  uint32_t dma_off[DMA_PER_TILE];
-  int nx_tap = 0, nx_k0 = 0;  // (tap, k offset) of the next tile to prepare
-  uint32_t a_tap = 0, b_tap[4] = {0, 0, 0, 0};  // per-tap bases, refreshed when the tap changes
-  // Load offsets of tile kt.  Tiles past the end get out-of-range offsets:
-  // their loads write zeros into a stage that is no longer read, which keeps
-  // the count of loads in flight the same on every tile.
-  auto prepare_dma = [&](int kt) {
-    const int tap = nx_tap, k0 = nx_k0;
-    const bool live = kt < KT;
-    if (live && k0 == 0) {  // uniform branch, taken once per tap
-      const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
-      const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-      a_tap = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
+  // Running load offsets of the next tile to load, one set per operand.
+  // Tiles past the end load with an out-of-range scalar offset (zeros into
+  // a stage that is no longer read), which keeps the count of loads in
+  // flight the same on every tile.
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) b_tap[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
+  for (int i = 0; i < 4; i++) {
+    a_off[i] = a_lane[i] + atab[0];
+    b_off[i] = gtab[b_row[i]] + b_chunk[i];
+  }
+  const uint32_t a_step = (uint32_t)BK * wrow, b_step = (uint32_t)BK * 2u;
+  // Tile t = (tap, k tile) with tap = t / kpt, by multiply-high with a
+  // rounded-up reciprocal (exact for t < 17 kpt, kpt <= 4096: tiles per
+  // class are at most 16 kpt, plus the 4 zero-fill tiles).
+  auto tap_of = [&](int t) -> int { return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic); };
+  uint32_t a_soff = 0, b_soff = 0;
+  // Move a set of offsets from tile t-1 to tile t: one add per lane offset,
+  // except where a new tap starts (uniform branch, once per kpt tiles).
+  // Offsets of tiles past the end are never used to read live data.
+  auto advance_a = [&](int t) {
+    const int tap = tap_of(t);
+    if (t - tap * kpt == 0 && t < KT) {
+      const uint32_t base = atab[tap];
+#pragma unroll
+      for (int i = 0; i < 4; i++) a_off[i] = a_lane[i] + base;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) a_off[i] += a_step;
     }
-    // Whole offsets go in the per-lane operand, so the record-count check
-    // sees every byte a lane touches.
-#pragma unroll
-    for (int i = 0; i < 4; i++) dma_off[i] = live ? a_lane[i] + a_tap + (uint32_t)k0 * wrow : dev::kOOB;
-#pragma unroll
-    for (int i = 0; i < 4; i++) dma_off[4 + i] = live ? b_tap[i] + (uint32_t)k0 * 2u : dev::kOOB;
-    nx_k0 = k0 + BK == a.Kg ? 0 : k0 + BK;
-    nx_tap = k0 + BK == a.Kg ? tap + 1 : tap;
+    a_soff = t < KT ? 0u : dev::kOOB;
   };
-  // Load j of a tile: 64 lanes x 16 bytes, global -> LDS without VGPRs
-  // (buffer_load ... lds; lane l writes 16 bytes at M0 + 16 l).  Written in
-  // assembly so that the compiler does not add its own conservative vmcnt
-  // waits before fragment reads of other stages: the waits that order these
-  // loads against LDS reads are the explicit ones in the main loop and
-  // before the epilogue.
+  auto advance_b = [&](int t) {
+    const int tap = tap_of(t);
+    if (t - tap * kpt == 0 && t < KT) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) b_off[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) b_off[i] += b_step;
+    }
+    b_soff = t < KT ? 0u : dev::kOOB;
+  };
+  // Load j of a tile (j < 4: W, else dY): 64 lanes x 16 bytes, global ->
+  // LDS without VGPRs (buffer_load ... lds; lane l writes 16 bytes at
+  // M0 + 16 l).  Written in assembly so that the compiler does not add its
+  // own conservative vmcnt waits before fragment reads of other stages: the
+  // waits that order these loads against LDS reads are the explicit ones in
+  // the main loop and before the epilogue.  The destination stage is a
+  // compile-time constant and M0 a scalar sum.
+  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)wave * 4096u);
+  const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_char*)smem;
   auto issue_one = [&](auto dstc, int j) {
     constexpr int DS = decltype(dstc)::value;
-    lds_char* dma_st = (lds_char*)(DS == 0 ? stage0 : DS == 1 ? stage1 : DS == 2 ? stage2 : stage3);
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(dma_st + (j < 4 ? (4 * wave + j) * 1024 : ABYTES + (4 * wave + j - 4) * 1024)));
-    const uint32_t voff = dma_off[j];
+        smem_base + wbase + (uint32_t)(j < 4 ? DS * ABYTES + j * 1024 : BBASE + DS * BBYTES + (j - 4) * 1024));
+    const uint32_t voff = j < 4 ? a_off[j] : b_off[j - 4];
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(j < 4 ? a_soff : b_soff);
     const i32x4 desc = j < 4 ? dw : dyd;
     // M0 is listed as clobbered; nothing else in this kernel uses M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
-                 :: "s"(m0v), "v"(voff), "s"(desc) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_nop 0"
+                 :: "s"(m0v), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
 #pragma clang diagnostic pop
+  };
+  // The same load split in two: M0 is written one MFMA ahead of the load
+  // that reads it, which covers the M0 -> LDS-load wait state without an
+  // s_nop.  Nothing else writes M0 in between (nothing else in this kernel
+  // uses M0).
+  auto set_m0 = [&](auto dstc, int j) {
+    constexpr int DS = decltype(dstc)::value;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        smem_base + wbase + (uint32_t)(j < 4 ? DS * ABYTES + j * 1024 : BBASE + DS * BBYTES + (j - 4) * 1024));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0" :: "s"(m0v) : "memory", "m0");
+#pragma clang diagnostic pop
+  };
+  auto load_m0 = [&](int j) {
+    const uint32_t voff = j < 4 ? a_off[j] : b_off[j - 4];
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(j < 4 ? a_soff : b_soff);
+    const i32x4 desc = j < 4 ? dw : dyd;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(desc), "s"(soff) : "memory");
   };
 
   f32x16 acc[4][4];
@@ -228,7 +279,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     const int row = wn * 128 + bn * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
-      b_rd[bn][ks] = ABYTES + row * BROW + (((2 * ks + (lane >> 5)) ^ swz_y(row)) << 4);
+      b_rd[bn][ks] = BBASE + row * BROW + (((2 * ks + (lane >> 5)) ^ swz_y(row)) << 4);
   }
 
   // Read r (0..11) of the fragments of k step ks, in the order the next
@@ -236,8 +287,8 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // then A blocks 1-3.
   auto read_one = [&](auto stc, int ks, int r, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
     constexpr int ST = decltype(stc)::value;
-    lds_char* st = (lds_char*)(ST == 0 ? stage0 : ST == 1 ? stage1 : ST == 2 ? stage2 : stage3);
-    const char* sb = ST == 0 ? stage0 : ST == 1 ? stage1 : ST == 2 ? stage2 : stage3;
+    lds_char* st = (lds_char*)smem + ST * ABYTES;
+    const char* sb = smem + ST * BBYTES;
     if (r >= 2 && r < 6) {
       fb[r - 2] = *(const bf16x8*)(sb + b_rd[r - 2][ks]);
     } else {
@@ -248,34 +299,41 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     }
   };
   // 16 MFMAs on (fa, fb); one fragment read of the next k step after each
-  // of the first 12, one load after every fourth.  The order is pinned
-  // with scheduling barriers.
+  // of the first 12, one load after every fourth, and the offset update of
+  // the operand loaded in the previous half after the second.  The order is
+  // pinned with scheduling barriers: a wave issues at most one instruction
+  // per four clocks, so everything besides the MFMAs has to be spread thin.
   auto half = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], auto rstc, int rks,
-                  bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0) {
+                  bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0, auto&& advance) {
 #pragma unroll
     for (int q = 0; q < 16; q++) {
       acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q >> 2], fb[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
       if (q < 12) read_one(rstc, rks, q, ra, rb);
-      if ((q & 3) == 3) issue_one(dstc, j0 + (q >> 2));
+      if ((q & 3) == 2) set_m0(dstc, j0 + (q >> 2));
+      if ((q & 3) == 3) load_m0(j0 + (q >> 2));
+      if (q == 1) advance();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- main loop.  Iteration kt: k step 0 of tile kt (fragments already in
-  // registers) issues the second half of tile kt+3's loads; then, once tile
-  // kt+1 has landed and every wave has finished reading tile kt (barrier),
-  // the first fragments of tile kt+1 are read while k step 1 of tile kt
-  // issues the first half of tile kt+4's loads into tile kt's stage.
-  prepare_dma(0);
+  // registers) issues the dY loads of tile kt+3; then, once tile kt+1 has
+  // landed and every wave has finished reading tile kt (barrier), the first
+  // fragments of tile kt+1 are read while k step 1 of tile kt issues the W
+  // loads of tile kt+4 into tile kt's stage.  Prologue: tiles 0-2 whole and
+  // the W loads of tile 3.
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 0>(), j);
-  prepare_dma(1);
+  advance_a(1);
+  advance_b(1);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 1>(), j);
-  prepare_dma(2);
+  advance_a(2);
+  advance_b(2);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 2>(), j);
-  prepare_dma(3);
+  advance_a(3);
+  advance_b(3);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE / 2; j++) issue_one(std::integral_constant<int, 3>(), j);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * DMA_PER_TILE + DMA_PER_TILE / 2));
@@ -285,11 +343,12 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   for (int r = 0; r < 12; r++) read_one(std::integral_constant<int, 0>(), 0, r, fa0, fb0);
   auto iter = [&](int kt, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    half(fa0, fb0, stc, 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(), DMA_PER_TILE / 2);
-    prepare_dma(kt + NSTAGE);
+    half(fa0, fb0, stc, 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(),
+         DMA_PER_TILE / 2, [&]() { advance_a(kt + NSTAGE); });
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE));
     __builtin_amdgcn_s_barrier();
-    half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0);
+    half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0,
+         [&]() { advance_b(kt + NSTAGE); });
   };
   for (int kt = 0; kt < KT; kt += NSTAGE) {
     iter(kt, std::integral_constant<int, 0>());
@@ -308,7 +367,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
 #pragma unroll
   for (int bn = 0; bn < 4; bn++) {
     const int prow = wn * 128 + bn * 32 + (lane & 31);
-    char* rowp = stage_ptr(prow >> 6) + (prow & 63) * 512;
+    char* rowp = smem + prow * 512;
 #pragma unroll
     for (int bm = 0; bm < 4; bm++) {
 #pragma unroll
@@ -328,7 +387,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
 #pragma unroll 4
     for (int it = 0; it < BN / (THREADS / 32); it++) {
       const int prow = it * (THREADS / 32) + (tid >> 5);
-      const char* rowp = stage_ptr(prow >> 6) + (prow & 63) * 512;
+      const char* rowp = smem + prow * 512;
       const u32x4 v = *(const u32x4*)(rowp + ((ch ^ (prow & 31)) << 4));
       const uint32_t base = otab[prow];
       __builtin_amdgcn_raw_buffer_store_b128(u4{v[0], v[1], v[2], v[3]}, rdx,

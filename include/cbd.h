@@ -80,8 +80,9 @@ typedef struct cbd_plan_s cbd_plan_t; /* opaque; immutable once created */
 typedef enum {
   CBD_KERNEL_AUTO = -1,
   CBD_KERNEL_GENERIC = 0,   /* any layout / dtype: gathered 64x64 tiles, f32 MFMA */
-  CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 64 == 0, C/G % 8 == 0:
-                               256x256x64 tiles, bf16 MFMA, double-buffered LDS */
+  CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 32 == 0, K/G <= 131072,
+                               C/G % 8 == 0, at most 16 taps per class:
+                               256x256x32 tiles, bf16 MFMA, 4-stage LDS */
   CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G in {1,2,4,8}, G | 256:
                                direct per-group accumulation, filter in registers */
 } cbd_kernel;

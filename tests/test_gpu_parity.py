@@ -179,7 +179,7 @@ def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), 
         if family == cbd.KERNEL_NHWC_BF16:
             g = rng.choice([1, 1, 2])
             cg = 8 * rng.randint(1, 40)
-            kg = 64 * rng.randint(1, 3)
+            kg = 32 * rng.randint(1, 6)
             layout, dtype = NHWC, "bf16"
         elif family == cbd.KERNEL_GROUPED:
             cg = rng.choice([1, 2, 4, 8])
