@@ -24,6 +24,7 @@ SOURCES = [
     "kern_igemm_generic.hip",
     "kern_igemm_nhwc_bf16.hip",
     "kern_grouped_direct.hip",
+    "kern_grouped_rows.hip",
     "kern_zero_fill.hip",
 ]
 

@@ -56,7 +56,10 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
     int err = 0;
     switch (info.kernel) {
       case CBD_KERNEL_NHWC_BF16: err = cbd::launch_nhwc_bf16(a, info.grid_main, stream); break;
-      case CBD_KERNEL_GROUPED: err = cbd::launch_grouped(a, plan->prob.dtype, info.grid_main, stream); break;
+      case CBD_KERNEL_GROUPED:
+        err = a.grp_lds > 0 ? cbd::launch_grouped_rows(a, plan->prob.dtype, info.grid_main, stream)
+                            : cbd::launch_grouped(a, plan->prob.dtype, info.grid_main, stream);
+        break;
       default: err = cbd::launch_generic(a, plan->prob.layout, plan->prob.dtype, info.grid_main, stream); break;
     }
     if (err) {

@@ -38,8 +38,8 @@ struct GemmArgs {
   int32_t tiles_m;     // GEMM-M tiles per group
   int32_t tile_n;      // GEMM-N extent of one tile (positions)
   int32_t xcd_remap;   // 1: give each XCD a contiguous range of logical tiles
-  int32_t iters;       // grouped kernel: positions per thread
-  int32_t pad_;
+  int32_t iters;       // grouped direct kernel: positions per thread
+  int32_t grp_lds;     // grouped row kernel: LDS bytes per workgroup (0: direct kernel)
   const void* dy;
   const void* w;
   void* dx;

@@ -212,14 +212,25 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     threads = cbd::kGroupedThreads;
   }
 
-  // Grouped kernel: positions per thread so that the grid is ~2048 workgroups.
+  // Grouped kernels.  Row kernel (C/G <= 4): one workgroup per output row
+  // of a class, the row's dY rows staged in LDS.  Direct kernel otherwise:
+  // positions per thread so that the grid is ~2048 workgroups.
   int64_t iters = 1;
   int64_t slots = 0;
+  int64_t grp_lds = 0;
   if (kernel == CBD_KERNEL_GROUPED) {
     slots = cbd::kGroupedThreads / p.g;
-    int64_t total_pos = 0;
-    for (const auto& s : subs) total_pos += s.n;
-    iters = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(total_pos, slots * 2048)));
+    const int64_t pixb = p.c * es;
+    int64_t need = 0;
+    for (const auto& s : subs)
+      need = std::max<int64_t>(need, s.taps_h * (s.pos_w + aw.delta * (s.taps_w - 1)) * pixb);
+    if (Cg <= 4 && pixb % 16 == 0 && need <= cbd::kGroupedRowLds) {
+      grp_lds = need;
+    } else {
+      int64_t total_pos = 0;
+      for (const auto& s : subs) total_pos += s.n;
+      iters = std::max<int64_t>(1, std::min<int64_t>(64, ceil_div(total_pos, slots * 2048)));
+    }
   }
 
   // Tiles per class (contiguous ranges of the logical grid, in LPT order).
@@ -232,7 +243,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     s.id = (int32_t)i;
     s.tile_begin = tile;
     if (kernel == CBD_KERNEL_GROUPED)
-      s.tiles = ceil_div(s.n, slots * iters);
+      s.tiles = grp_lds > 0 ? p.n * s.pos_h : ceil_div(s.n, slots * iters);
     else
       s.tiles = p.g * tiles_m * ceil_div(s.n, bn);
     tile += s.tiles;
@@ -277,11 +288,12 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.num_sub = (int32_t)subs.size();
   a.total_tiles = (int32_t)tile;
   a.tiles_m = (int32_t)tiles_m;
-  a.tile_n = (int32_t)(kernel == CBD_KERNEL_GROUPED ? slots * iters : bn);
+  a.tile_n = (int32_t)(kernel == CBD_KERNEL_GROUPED ? (grp_lds > 0 ? subs[0].pos_w : slots * iters) : bn);
   // XCD-contiguous tile ranges pay when one panel is shared by many tiles;
   // with unequal K they would also hand the long tiles to a few XCDs.
   a.xcd_remap = (kernel != CBD_KERNEL_GROUPED && equal_k && tile >= 64) ? 1 : 0;
   a.iters = (int32_t)iters;
+  a.grp_lds = (int32_t)grp_lds;
   for (size_t i = 0; i < subs.size(); i++) {
     cbd::SubDesc& d = a.sub[i];
     const cbd_subgemm_t& s = subs[i];
