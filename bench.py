@@ -39,10 +39,15 @@ METRIC = "conv bwd-data useful TFLOP/s + µs/call on 1 MI355X, % of MFMA/HBM roo
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 2.4 GHz * 4096 dense bf16 flop/clk/CU
 PEAK_F32_TFLOPS = 157.3     # 256 CU * 2.4 GHz * 256 f32 MFMA flop/clk/CU
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = {0: "kern_igemm_generic.hip", 1: "kern_igemm_nhwc_bf16.hip",
-              2: "kern_grouped_direct.hip"}
-KERNEL_SYMBOL = {0: "igemm_generic_kernel", 1: "igemm_nhwc_bf16_kernel",
-                 2: "grouped_direct_kernel"}
+# (kernel family, row variant) -> source file and kernel symbol
+KERNEL_SRC = {(0, 0): "kern_igemm_generic.hip", (1, 0): "kern_igemm_nhwc_bf16.hip",
+              (2, 0): "kern_grouped_direct.hip", (2, 1): "kern_grouped_rows.hip"}
+KERNEL_SYMBOL = {(0, 0): "igemm_generic_kernel", (1, 0): "igemm_nhwc_bf16_kernel",
+                 (2, 0): "grouped_direct_kernel", (2, 1): "grouped_rows_kernel"}
+# Bound of each workload problem (dense-contraction rows on MFMA, the rest on
+# HBM; the small fp32 rows are launch-latency bound in practice).
+LATENCY_BOUND = ("c1", "c2-14-1", "c2-14-3", "c2-15-1", "c2-15-3", "c2-16-1", "c2-16-3")
+HBM_BOUND = ("c3b", "c5-s2", "c5-s1")
 
 
 def describe(p):
@@ -64,11 +69,15 @@ def algorithmic_bytes(p, info):
     return es * (dy_used + p.k * (p.c // p.g) * p.y * p.x + p.n * p.c * p.hi * p.wi)
 
 
-def read_traffic(kernel_id):
+def kernel_key(info):
+    return (info.kernel, 1 if info.lds_dynamic > 0 else 0)
+
+
+def read_traffic(key):
     """HBM bytes per launch recorded under profiles/ for this kernel, if the
     kernel source still matches the one the counters were taken on."""
-    src = os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", KERNEL_SRC[kernel_id])
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_SRC[kernel_id].split('.')[0]}_traffic.txt")
+    src = os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", KERNEL_SRC[key])
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_SRC[key].split('.')[0]}_traffic.txt")
     if not os.path.exists(path):
         return None
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -139,6 +148,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain copy of this size (rocprofv3 counter scaling)")
     ap.add_argument("--force-kernel", type=int, default=-1)
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line per workload problem: warm and cold (caches "
+                         "flushed) µs/call and the roofline fraction; not the bench line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -154,6 +166,9 @@ def main():
     from cbd_inputs import draw, problem_by_name, seed_for
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.all:
+        all_problems(args)
+        return
     p = problem_by_name(args.problem)
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
@@ -191,7 +206,7 @@ def main():
 
     flops = info.useful_flops
     alg_bytes = algorithmic_bytes(p, info)
-    if info.kernel == cbd.KERNEL_GROUPED or p.name in ("c3b",):
+    if p.name in HBM_BOUND:
         roof = {"bound": "hbm", "achieved": round(alg_bytes / launch_s / 1e9, 2),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
@@ -199,8 +214,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops / launch_s / 1e12, 2), "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = read_traffic(info.kernel)
-    roof["kernel"] = KERNEL_SYMBOL[info.kernel]
+    roof["traffic"] = read_traffic(kernel_key(info))
+    roof["kernel"] = KERNEL_SYMBOL[kernel_key(info)]
     roof["launch_us_mean"] = round(launch_s * 1e6, 3)
     roof["launches_per_step"] = info.launches
 
@@ -230,6 +245,73 @@ def main():
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def all_problems(args):
+    """Every workload problem: warm = back-to-back calls under one event pair;
+    cold = calls each preceded (outside its event pair) by a 512 MiB write that
+    evicts L2 and the MALL.  Fractions are of the problem's own roofline."""
+    import numpy as np
+    import torch
+
+    import dnn_conv2d_bwd_amd as cbd
+    from cbd_inputs import PROBLEMS, draw, seed_for
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for p in PROBLEMS:
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                      (p.dh, p.dw), p.layout, dt)
+        info = pl.info()
+        sh = pl.shapes()
+        tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+        dy_d = torch.from_numpy(draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)).to(tdt).cuda()
+        w_d = torch.from_numpy(draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)).to(tdt).cuda()
+        dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
+        for _ in range(10):
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm = e0.elapsed_time(e1) * 1e3 / args.steps
+        cold = []
+        for _ in range(50):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        cold = np.array(cold)
+        flops, nbytes = info.useful_flops, algorithmic_bytes(p, info)
+        if p.name in HBM_BOUND:
+            bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+            ach = lambda us: nbytes / us / 1e3
+        else:
+            bound = "mfma"
+            peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+            unit = "TFLOP/s"
+            ach = lambda us: flops / us / 1e6
+        med = float(np.median(cold))
+        print(json.dumps({
+            "problem": p.name, "workload": describe(p), "kernel": KERNEL_SYMBOL[kernel_key(info)],
+            "launches": info.launches, "grid": info.grid_main,
+            "useful_gflop": round(flops / 1e9, 5), "executed_gmac": round(info.executed_macs / 1e9, 5),
+            "alg_mbytes": round(nbytes / 1e6, 3),
+            "us_warm": round(warm, 2), "us_cold_median": round(med, 2),
+            "us_cold_p10": round(float(np.percentile(cold, 10)), 2),
+            "us_cold_p90": round(float(np.percentile(cold, 90)), 2),
+            "bound": bound + (" (launch latency in practice)" if p.name in LATENCY_BOUND else ""),
+            "achieved_warm": round(ach(warm), 2), "achieved_cold": round(ach(med), 2),
+            "unit": unit, "peak": peak,
+            "frac_warm": round(ach(warm) / peak, 4), "frac_cold": round(ach(med) / peak, 4)}),
+            flush=True)
 
 
 if __name__ == "__main__":

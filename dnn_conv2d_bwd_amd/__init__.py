@@ -61,7 +61,7 @@ class PlanInfo(ctypes.Structure):
                 ("threads_main", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("grid_main", ctypes.c_int64), ("grid_zero", ctypes.c_int64),
                 ("useful_flops", ctypes.c_int64), ("executed_macs", ctypes.c_int64),
-                ("zero_elems", ctypes.c_int64)]
+                ("zero_elems", ctypes.c_int64), ("lds_dynamic", ctypes.c_int64)]
 
 
 class SubGemm(ctypes.Structure):

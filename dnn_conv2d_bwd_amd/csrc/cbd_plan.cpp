@@ -345,6 +345,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.useful_flops = 2 * p.n * p.c * Kg * Ho * Wo * p.y * p.x;
   info.executed_macs = exec;
   info.zero_elems = zero_elems;
+  info.lds_dynamic = grp_lds;
 
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);

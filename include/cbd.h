@@ -140,6 +140,9 @@ typedef struct {
   int64_t executed_macs;    /* sum over sub-GEMMs of G*M*N*K (valid-tap MACs
                                plus those of taps falling off dY's edge) */
   int64_t zero_elems;       /* dX elements written by the zero-fill launch */
+  int64_t lds_dynamic;      /* dynamic LDS bytes per workgroup of the main
+                               launch (grouped family: > 0 selects the row
+                               kernel, 0 the direct kernel) */
 } cbd_plan_info_t;
 
 typedef struct {
