@@ -248,9 +248,11 @@ def main():
 
 
 def all_problems(args):
-    """Every workload problem: warm = back-to-back calls under one event pair;
-    cold = calls each preceded (outside its event pair) by a 512 MiB write that
-    evicts L2 and the MALL.  Fractions are of the problem's own roofline."""
+    """Every workload problem: warm = back-to-back calls under one event pair
+    (host launch cost included: small problems are bounded by it); graph = the
+    same calls replayed from a captured HIP graph (GPU time only); cold = calls
+    each preceded (outside its event pair) by a 512 MiB write that evicts L2
+    and the MALL.  Fractions are of the problem's own roofline."""
     import numpy as np
     import torch
 
@@ -289,6 +291,27 @@ def all_problems(args):
             torch.cuda.synchronize()
             cold.append(a.elapsed_time(b) * 1e3)
         cold = np.array(cold)
+        # GPU time without host launch cost: 50 calls captured in a HIP graph
+        # (the calls launch kernels only: no allocation, copy or memset).
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            cbd.run(pl, dy_d, w_d, dx_d, stream=cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(50):
+                    cbd.run(pl, dy_d, w_d, dx_d, stream=cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(4):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = g0.elapsed_time(g1) * 1e3 / 200
         flops, nbytes = info.useful_flops, algorithmic_bytes(p, info)
         if p.name in HBM_BOUND:
             bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
@@ -304,13 +327,15 @@ def all_problems(args):
             "launches": info.launches, "grid": info.grid_main,
             "useful_gflop": round(flops / 1e9, 5), "executed_gmac": round(info.executed_macs / 1e9, 5),
             "alg_mbytes": round(nbytes / 1e6, 3),
-            "us_warm": round(warm, 2), "us_cold_median": round(med, 2),
+            "us_warm": round(warm, 2), "us_graph": round(us_graph, 2),
+            "us_cold_median": round(med, 2),
             "us_cold_p10": round(float(np.percentile(cold, 10)), 2),
             "us_cold_p90": round(float(np.percentile(cold, 90)), 2),
             "bound": bound + (" (launch latency in practice)" if p.name in LATENCY_BOUND else ""),
-            "achieved_warm": round(ach(warm), 2), "achieved_cold": round(ach(med), 2),
-            "unit": unit, "peak": peak,
-            "frac_warm": round(ach(warm) / peak, 4), "frac_cold": round(ach(med) / peak, 4)}),
+            "achieved_warm": round(ach(warm), 2), "achieved_graph": round(ach(us_graph), 2),
+            "achieved_cold": round(ach(med), 2), "unit": unit, "peak": peak,
+            "frac_warm": round(ach(warm) / peak, 4), "frac_graph": round(ach(us_graph) / peak, 4),
+            "frac_cold": round(ach(med) / peak, 4)}),
             flush=True)
 
 

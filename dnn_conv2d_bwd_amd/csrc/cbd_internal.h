@@ -29,7 +29,7 @@ int launch_zero_fill(const ZeroArgs& z, int64_t grid, void* stream);
 const char* hip_error_name(int err);
 
 // Tile shapes of each kernel family (the planner sizes grids with them).
-constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;
+constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;  // tiles 64 or 32
 constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 256, kFastMaxTaps = 16;
 constexpr int kFastMaxKTiles = 4096;  // k tiles per tap (K/G / 32): bound of the kernel's tap division
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;

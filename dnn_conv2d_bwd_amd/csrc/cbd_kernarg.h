@@ -37,6 +37,7 @@ struct GemmArgs {
   int32_t total_tiles;
   int32_t tiles_m;     // GEMM-M tiles per group
   int32_t tile_n;      // GEMM-N extent of one tile (positions)
+  int32_t tile_m;      // GEMM-M extent of one tile (channels)
   int32_t xcd_remap;   // 1: give each XCD a contiguous range of logical tiles
   int32_t iters;       // grouped direct kernel: positions per thread
   int32_t grp_lds;     // grouped row kernel: LDS bytes per workgroup (0: direct kernel)

@@ -205,7 +205,14 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
 
   int64_t bm = 0, bn = 0, bk = 0, threads = 0;
   if (kernel == CBD_KERNEL_GENERIC) {
-    bm = cbd::kGenericBM; bn = cbd::kGenericBN; bk = cbd::kGenericBK; threads = cbd::kGenericThreads;
+    // 32-wide tiles where 64 would be mostly padding (C/G <= 32) or would
+    // leave CUs idle (fewer workgroups than CUs).
+    bm = Cg <= 32 ? 32 : cbd::kGenericBM;
+    bk = cbd::kGenericBK;
+    threads = cbd::kGenericThreads;
+    int64_t grid64 = 0;
+    for (const auto& s : subs) grid64 += p.g * ceil_div(Cg, bm) * ceil_div(s.n, cbd::kGenericBN);
+    bn = grid64 < 256 ? 32 : cbd::kGenericBN;
   } else if (kernel == CBD_KERNEL_NHWC_BF16) {
     bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;
   } else {
@@ -289,6 +296,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.total_tiles = (int32_t)tile;
   a.tiles_m = (int32_t)tiles_m;
   a.tile_n = (int32_t)(kernel == CBD_KERNEL_GROUPED ? (grp_lds > 0 ? subs[0].pos_w : slots * iters) : bn);
+  a.tile_m = (int32_t)bm;
   // XCD-contiguous tile ranges pay when one panel is shared by many tiles;
   // with unequal K they would also hand the long tiles to a few XCDs.
   a.xcd_remap = (kernel != CBD_KERNEL_GROUPED && equal_k && tile >= 64) ? 1 : 0;

@@ -1,6 +1,7 @@
 // kern_igemm_generic.hip -- implicit-GEMM backward-data for any layout and
-// dtype (the fallback family).  One launch covers every stride-residue class:
-// each workgroup decodes (class, group, M-tile, N-tile) from its id.
+// dtype (the fallback family, and the family of the small fp32 problems).
+// One launch covers every stride-residue class: each workgroup decodes
+// (class, group, M-tile, N-tile) from its id.
 //
 // Per class (i_h, i_w) and group g the GEMM is
 //   M = C/G (dX channel c), N = N*pos_h*pos_w (dX positions of the class's
@@ -14,11 +15,17 @@
 // backward-data strategy of MIOpen PR #272 names); here the ids are
 // workgroup ranges of one grid.
 //
-// Tiles 64(M) x 64(N) x 16(K), 256 threads = 4 waves in 2x2, each wave
-// 32x32 via v_mfma_f32_16x16x4_f32.  Operands are gathered element-wise with
-// buffer loads (out-of-range -> 0: padding, ragged tiles, taps off dY's
-// edge), converted to f32 and staged in LDS.  bf16 products are exact in
-// f32, so this matches a bf16 MFMA's arithmetic up to summation order.
+// The problems this family serves are small: a workgroup's time is the
+// chain of global-load latencies along K, not MFMA work.  So the K loop is
+// split across the 4 waves of a workgroup (wave w takes k tiles w, w+4, ...),
+// each wave computes the whole BM x BN tile from its own LDS staging area
+// with v_mfma_f32_16x16x4_f32 and keeps the next tile's gathers in flight
+// (register double buffer; no workgroup barrier inside the loop), and the
+// four partial tiles are summed in a fixed order through LDS at the end
+// (deterministic).  Tiles are 64 or 32 on each side, chosen by the planner
+// (smaller tiles when the grid would leave CUs idle).  Operands are gathered
+// element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
+// taps off dY's edge) and converted to f32; bf16 products are exact in f32.
 #include "cbd_device.h"
 #include "cbd_internal.h"
 
@@ -26,6 +33,13 @@ namespace cbd {
 namespace {
 
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// Pins a select: keeps the compiler from turning `cond ? off : kOOB` into a
+// branch around the load (which would also force vmcnt(0) at the joins).
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 template <int DT>
 __device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
@@ -45,16 +59,20 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
   }
 }
 
-template <int DT, int LAYOUT>
-__global__ __launch_bounds__(kGenericThreads) void igemm_generic_kernel(const GemmArgs a) {
-  constexpr int BM = kGenericBM, BN = kGenericBN, BK = kGenericBK;
+template <int DT, int LAYOUT, int BM, int BN>
+__global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const GemmArgs a) {
+  constexpr int BK = kGenericBK;            // 16
+  constexpr int NW = kGenericThreads / 64;  // 4 waves, each its own k tiles
+  constexpr int MB = BM / 16, NB = BN / 16;
+  constexpr int AE = BK * BM / 64, BE = BK * BN / 64;  // gathers per lane per tile
+  constexpr int STG = BK * (BM + BN);                  // staging floats per wave
+  constexpr int RED = 2 * BM * BN;                     // two partial tiles at a time
+  constexpr int LDSF = NW * STG > RED ? NW * STG : RED;
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
-  constexpr int NPIX = LAYOUT == 0 ? 1 : 4;  // dY positions each thread gathers
-  __shared__ float As[BK][BM];
-  __shared__ float Bs[BK][BN];
+  __shared__ float lds[LDSF];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
 
   const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
   const SubDesc s = a.sub[dev::find_class(a, t)];
@@ -73,141 +91,173 @@ __global__ __launch_bounds__(kGenericThreads) void igemm_generic_kernel(const Ge
   const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
 
   const int YX = a.Y * a.X;
-  const int HoWo = a.Ho * a.Wo;
+  const int kpt = (a.Kg + BK - 1) / BK;
+  const int KT = s.taps_h * s.taps_w * kpt;
 
-  // A (filter) gather: column m = tid & 63, rows kk = (tid >> 6) + 4*i.
-  const int am = tid & 63;
-  const int ac = m0 + am;
+  // Gather roles.  A: channel m0 + lane % BM, k rows lane / BM + (64/BM)*e.
+  // B: position n0 + lane % BN, k rows lane / BN + (64/BN)*e.
+  const int ac = m0 + lane % BM;
   const bool ac_ok = ac < a.Cg;
-  // B (dY) gather: NCHW walks positions across lanes (w is contiguous),
-  // NHWC walks k across lanes (channels are contiguous).
-  int pn[NPIX], pth[NPIX], ptw[NPIX];
-  bool pok[NPIX];
+  const int ak = lane / BM, bk = lane / BN;
+  const int bp = n0 + lane % BN;
+  const bool bp_ok = bp < npos;
+  const int bpp = bp_ok ? bp : 0;
+  const int pn = bpp / npix_img;
+  const int prr = bpp - pn * npix_img;
+  const int pth = prr / s.pos_w, ptw = prr - (prr / s.pos_w) * s.pos_w;
+  // element strides along k
+  const int a_ks = LAYOUT == 0 ? a.Cg * YX : YX * a.Cg;
+  const int b_ks = LAYOUT == 0 ? a.Ho * a.Wo : 1;
+
+  auto gather = [&](int kt, float (&av)[AE], float (&bv)[BE]) {
+    const bool live = kt < KT;
+    const int ktc = live ? kt : 0;
+    const int tap = ktc / kpt;
+    const int k0 = (ktc - tap * kpt) * BK;
+    const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
+    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+    const int ho = pth + s.beta_h - a.delta_h * jh, wo = ptw + s.beta_w - a.delta_w * jw;
+    const bool bok = live && bp_ok && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
+    const int abase = LAYOUT == 0 ? ((g * a.Kg) * a.Cg + ac) * YX + ty * a.X + tx
+                                  : ((g * a.Kg) * YX + ty * a.X + tx) * a.Cg + ac;
+    const int bbase = LAYOUT == 0 ? ((pn * a.K + g * a.Kg) * a.Ho + ho) * a.Wo + wo
+                                  : ((pn * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg;
 #pragma unroll
-  for (int j = 0; j < NPIX; j++) {
-    const int p = n0 + (LAYOUT == 0 ? (tid & 63) : (tid >> 4) + 16 * j);
-    pok[j] = p < npos;
-    const int pp = pok[j] ? p : 0;
-    pn[j] = pp / npix_img;
-    const int rr = pp - pn[j] * npix_img;
-    pth[j] = rr / s.pos_w;
-    ptw[j] = rr - pth[j] * s.pos_w;
+    for (int e = 0; e < AE; e++) {
+      const int k = k0 + ak + (64 / BM) * e;
+      const bool ok = live && ac_ok && k < a.Kg;
+      av[e] = load_elem<DT>(rw, opaque(ok ? (uint32_t)(abase + k * a_ks) * ES : dev::kOOB));
+    }
+#pragma unroll
+    for (int e = 0; e < BE; e++) {
+      const int k = k0 + bk + (64 / BN) * e;
+      const bool ok = bok && k < a.Kg;
+      bv[e] = load_elem<DT>(rdy, opaque(ok ? (uint32_t)(bbase + k * b_ks) * ES : dev::kOOB));
+    }
+  };
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; i++)
+#pragma unroll
+    for (int j = 0; j < NB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float* As = lds + wave * STG;  // [BK][BM]
+  float* Bs = As + BK * BM;      // [BK][BN]
+  auto compute = [&](const float (&av)[AE], const float (&bv)[BE]) {
+#pragma unroll
+    for (int e = 0; e < AE; e++) As[(ak + (64 / BM) * e) * BM + lane % BM] = av[e];
+#pragma unroll
+    for (int e = 0; e < BE; e++) Bs[(bk + (64 / BN) * e) * BN + lane % BN] = bv[e];
+    // Only this wave uses its staging area and a wave's LDS operations run
+    // in order: waiting for its own writes is enough, no barrier.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+#pragma unroll
+    for (int ks = 0; ks < BK / 4; ks++) {
+      const int kr = 4 * ks + (lane >> 4);
+      float x[MB], y[NB];
+#pragma unroll
+      for (int bm = 0; bm < MB; bm++) x[bm] = As[kr * BM + bm * 16 + (lane & 15)];
+#pragma unroll
+      for (int bn = 0; bn < NB; bn++) y[bn] = Bs[kr * BN + bn * 16 + (lane & 15)];
+#pragma unroll
+      for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+        for (int bn = 0; bn < NB; bn++)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bm], y[bn], acc[bm][bn], 0, 0, 0);
+    }
+  };
+
+  // Wave-strided K loop, two tiles of gathers in flight.
+  float a0[AE], b0[BE], a1[AE], b1[BE];
+  gather(wave, a0, b0);
+  for (int kt = wave; kt < KT; kt += 2 * NW) {
+    gather(kt + NW, a1, b1);
+    compute(a0, b0);
+    if (kt + NW >= KT) break;
+    gather(kt + 2 * NW, a0, b0);
+    compute(a1, b1);
   }
 
-  f32x4 acc[2][2];
+  // Cross-wave sum in a fixed order, (w0 + w2) + (w1 + w3), through LDS
+  // (reusing the staging area; two partial tiles at a time).
+  auto red_at = [&](int slot, int bm, int bn, int v) -> float& {
+    return lds[(slot * BM + bm * 16 + 4 * (lane >> 4) + v) * BN + bn * 16 + (lane & 15)];
+  };
+  __syncthreads();
+  if (wave >= 2) {
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+    for (int bm = 0; bm < MB; bm++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int jh = 0; jh < s.taps_h; jh++) {
-    for (int jw = 0; jw < s.taps_w; jw++) {
-      const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-      const int dho = s.beta_h - a.delta_h * jh, dwo = s.beta_w - a.delta_w * jw;
-      // dY element offset of channel g*Kg (k added per element), or -1.
-      int boff[NPIX];
+      for (int bn = 0; bn < NB; bn++)
 #pragma unroll
-      for (int j = 0; j < NPIX; j++) {
-        const int ho = pth[j] + dho, wo = ptw[j] + dwo;
-        const bool ok = pok[j] && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
-        const int o = LAYOUT == 0 ? ((pn[j] * a.K + g * a.Kg) * a.Ho + ho) * a.Wo + wo
-                                  : ((pn[j] * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg;
-        boff[j] = ok ? o : -1;
-      }
-      for (int k0 = 0; k0 < a.Kg; k0 += BK) {
-        float av[4], bv[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int k = k0 + (tid >> 6) + 4 * i;
-          const int o = LAYOUT == 0 ? ((g * a.Kg + k) * a.Cg + ac) * YX + ty * a.X + tx
-                                    : ((g * a.Kg + k) * YX + ty * a.X + tx) * a.Cg + ac;
-          av[i] = load_elem<DT>(rw, (ac_ok && k < a.Kg) ? (uint32_t)o * ES : dev::kOOB);
-        }
-        if constexpr (LAYOUT == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int k = k0 + (tid >> 6) + 4 * i;
-            const bool ok = boff[0] >= 0 && k < a.Kg;
-            bv[i] = load_elem<DT>(rdy, ok ? (uint32_t)(boff[0] + k * HoWo) * ES : dev::kOOB);
-          }
-        } else {
-          const int k = k0 + (tid & 15);
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            const bool ok = boff[j] >= 0 && k < a.Kg;
-            bv[j] = load_elem<DT>(rdy, ok ? (uint32_t)(boff[j] + k) * ES : dev::kOOB);
-          }
-        }
-        __syncthreads();  // previous tile's MFMAs are done with LDS
-#pragma unroll
-        for (int i = 0; i < 4; i++) As[(tid >> 6) + 4 * i][am] = av[i];
-        if constexpr (LAYOUT == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; i++) Bs[(tid >> 6) + 4 * i][tid & 63] = bv[i];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; j++) Bs[tid & 15][(tid >> 4) + 16 * j] = bv[j];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < BK / 4; ks++) {
-          const int kr = 4 * ks + (lane >> 4);
-#pragma unroll
-          for (int bm = 0; bm < 2; bm++) {
-            const float x = As[kr][wm * 32 + bm * 16 + (lane & 15)];
-#pragma unroll
-            for (int bn = 0; bn < 2; bn++) {
-              const float y = Bs[kr][wn * 32 + bn * 16 + (lane & 15)];
-              acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[bm][bn], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
+        for (int v = 0; v < 4; v++) red_at(wave - 2, bm, bn, v) = acc[bm][bn][v];
   }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+      for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[bm][bn][v] += red_at(wave, bm, bn, v);
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+      for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) red_at(wave, bm, bn, v) = acc[bm][bn][v];
+  }
+  __syncthreads();
 
-  // Epilogue: lane holds rows 4*(lane>>4)+v, column lane&15 of each 16x16 block.
+  // Epilogue: thread -> position n0 + tid % BN, channels tid / BN + (256/BN)*i.
+  const int p = n0 + tid % BN;
+  const bool pv = p < npos;
+  const int pp = pv ? p : 0;
+  const int n = pp / npix_img;
+  const int rr = pp - n * npix_img;
+  const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
+  const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
+  const int pbase = LAYOUT == 0 ? (n * a.C + g * a.Cg) * a.Hi * a.Wi + hi * a.Wi + wi
+                                : ((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg;
+  const int cstride = LAYOUT == 0 ? a.Hi * a.Wi : 1;
 #pragma unroll
-  for (int bn = 0; bn < 2; bn++) {
-    const int p = n0 + wn * 32 + bn * 16 + (lane & 15);
-    const bool pv = p < npos;
-    const int pp = pv ? p : 0;
-    const int n = pp / npix_img;
-    const int rr = pp - n * npix_img;
-    const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
-    const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
-    const int pbase = LAYOUT == 0 ? (n * a.C + g * a.Cg) * a.Hi * a.Wi + hi * a.Wi + wi
-                                  : ((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg;
-    const int cstride = LAYOUT == 0 ? a.Hi * a.Wi : 1;
-#pragma unroll
-    for (int bm = 0; bm < 2; bm++) {
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int c = m0 + wm * 32 + bm * 16 + 4 * (lane >> 4) + v;
-        const bool ok = pv && c < a.Cg;
-        store_elem<DT>(rdx, ok ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB,
-                       acc[bm][bn][v]);
-      }
-    }
+  for (int i = 0; i < BM * BN / kGenericThreads; i++) {
+    const int m = tid / BN + (kGenericThreads / BN) * i;
+    const float v = lds[m * BN + tid % BN] + lds[(BM + m) * BN + tid % BN];
+    const int c = m0 + m;
+    store_elem<DT>(rdx, (pv && c < a.Cg) ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB, v);
   }
 }
 
-template <int DT, int LAYOUT>
+template <int DT, int LAYOUT, int BM, int BN>
 int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT>,
+  return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN>,
                               dim3((unsigned)grid), dim3(kGenericThreads), args, 0,
                               (hipStream_t)stream);
+}
+
+template <int DT, int LAYOUT>
+int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
+  if (a.tile_m == 64 && a.tile_n == 64) return launch_one<DT, LAYOUT, 64, 64>(a, grid, stream);
+  if (a.tile_m == 32 && a.tile_n == 64) return launch_one<DT, LAYOUT, 32, 64>(a, grid, stream);
+  if (a.tile_m == 64 && a.tile_n == 32) return launch_one<DT, LAYOUT, 64, 32>(a, grid, stream);
+  if (a.tile_m == 32 && a.tile_n == 32) return launch_one<DT, LAYOUT, 32, 32>(a, grid, stream);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream) {
   if (dtype == CBD_F32)
-    return layout == CBD_LAYOUT_NCHW ? launch_one<0, 0>(a, grid, stream)
-                                     : launch_one<0, 1>(a, grid, stream);
-  return layout == CBD_LAYOUT_NCHW ? launch_one<1, 0>(a, grid, stream)
-                                   : launch_one<1, 1>(a, grid, stream);
+    return layout == CBD_LAYOUT_NCHW ? launch_tiles<0, 0>(a, grid, stream)
+                                     : launch_tiles<0, 1>(a, grid, stream);
+  return layout == CBD_LAYOUT_NCHW ? launch_tiles<1, 0>(a, grid, stream)
+                                   : launch_tiles<1, 1>(a, grid, stream);
 }
 
 }  // namespace cbd

@@ -243,3 +243,36 @@ def test_fuzz_random_values(family, seed, count):
         run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
         ok, info = check(p, run, oracle.bwd_data(p, dy, w))
         assert ok, (p, info)
+
+
+# ------------------------------------------------------------ graph capture ---
+
+@pytest.mark.parametrize("name", ["c3b", "c4", "c5-s2"])
+def test_graph_replay_matches_eager(name):
+    """cbd_run is capturable (kernel launches only): every replay of a captured
+    graph, with eager work and synchronisation between replays, reproduces the
+    eager result bit for bit (c3b includes the zero-fill launch)."""
+    p = by_name(name)
+    print(f"[graph] {name}", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p)
+    dy_d, w_d = to_device(dy, p), to_device(w, p)
+    tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+    dx = torch.empty(pl.shapes()["dx"], dtype=tdt, device="cuda")
+    cbd.run(pl, dy_d, w_d, dx)
+    torch.cuda.synchronize()
+    want = dx.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            cbd.run(pl, dy_d, w_d, dx, stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        dx.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx.view(torch.int16 if p.dtype == "bf16" else torch.int32),
+                           want.view(torch.int16 if p.dtype == "bf16" else torch.int32)), (name, rep)
