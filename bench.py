@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain copy of this size (rocprofv3 counter scaling)")
     ap.add_argument("--force-kernel", type=int, default=-1)
+    ap.add_argument("--no-split", action="store_true",
+                    help="time the zero-insertion form (comparison baseline) instead of the "
+                         "residue split")
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload problem: warm and cold (caches "
                          "flushed) µs/call and the roofline fraction; not the bench line")
@@ -172,7 +175,8 @@ def main():
     p = problem_by_name(args.problem)
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
-                  (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel)
+                  (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
+                  no_split=args.no_split)
     info = pl.info()
     sh = pl.shapes()
     dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
@@ -234,6 +238,7 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic (seeded SplitMix64 / Box-Muller operands, no dataset)",
         "config": {"workload": describe(p), "problem": p.name,
+                   "form": "zero-insertion (no residue split)" if args.no_split else "residue split",
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
                    "useful_gflop": round(flops / 1e9, 4),

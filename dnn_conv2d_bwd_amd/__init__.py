@@ -50,7 +50,8 @@ class Problem(ctypes.Structure):
 
 
 class PlanOptions(ctypes.Structure):
-    _fields_ = [("force_kernel", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("force_kernel", ctypes.c_int32), ("no_split", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -144,10 +145,10 @@ def make_problem(n, g, c, k, hi, wi, y, x, stride=1, pad=0, dil=1, layout="nchw"
 class Plan:
     """Owns a cbd_plan_t; immutable; safe to run from several streams."""
 
-    def __init__(self, problem: Problem, force_kernel: int = KERNEL_AUTO):
+    def __init__(self, problem: Problem, force_kernel: int = KERNEL_AUTO, no_split: bool = False):
         self.problem = problem
         h = ctypes.c_void_p()
-        opts = PlanOptions(force_kernel)
+        opts = PlanOptions(force_kernel, 1 if no_split else 0)
         _check(_lib.cbd_plan_ex(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(h)),
                "cbd_plan")
         self._h = h
@@ -196,10 +197,11 @@ class Plan:
 
 
 def plan(n=None, g=1, c=None, k=None, hi=None, wi=None, y=None, x=None, stride=1, pad=0, dil=1,
-         layout="nchw", dtype="f32", force_kernel=KERNEL_AUTO, problem=None) -> Plan:
+         layout="nchw", dtype="f32", force_kernel=KERNEL_AUTO, problem=None,
+         no_split=False) -> Plan:
     if problem is None:
         problem = make_problem(n, g, c, k, hi, wi, y, x, stride, pad, dil, layout, dtype)
-    return Plan(problem, force_kernel)
+    return Plan(problem, force_kernel, no_split)
 
 
 def _torch_dtype(dt):

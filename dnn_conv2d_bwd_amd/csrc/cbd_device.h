@@ -47,6 +47,17 @@ __device__ inline int logical_tile(int b, int total, int remap) {
   return x * q + (x < r ? x : r) + idx;
 }
 
+// dY index read by tap j of class position t along one axis.  Residue split:
+// t + beta - delta*j.  Zero-insertion form (no_split): t is the dX index
+// itself and the term exists only where t + pad - j*dil is a non-negative
+// multiple of the stride; otherwise -1 (out of range: the load reads 0).
+__device__ inline int dy_index(int no_split, int t, int beta, int delta, int j, int pad, int dil,
+                               int str) {
+  if (!no_split) return t + beta - delta * j;
+  const int num = t + pad - j * dil;
+  return (num >= 0 && num % str == 0) ? num / str : -1;
+}
+
 // Class owning logical tile t (tile_begin ascends with the class index).
 __device__ inline int find_class(const GemmArgs& a, int t) {
   int r = 0;

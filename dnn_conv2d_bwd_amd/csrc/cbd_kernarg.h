@@ -39,6 +39,8 @@ struct GemmArgs {
   int32_t tile_n;      // GEMM-N extent of one tile (positions)
   int32_t tile_m;      // GEMM-M extent of one tile (channels)
   int32_t xcd_remap;   // 1: give each XCD a contiguous range of logical tiles
+  int32_t no_split;    // 1: zero-insertion form (one class, all taps, all positions)
+  int32_t str_h, str_w, pad_h, pad_w, dil_h, dil_w;  // the problem's own (no_split)
   int32_t iters;       // grouped direct kernel: positions per thread
   int32_t grp_lds;     // grouped row kernel: LDS bytes per workgroup (0: direct kernel)
   const void* dy;

@@ -99,9 +99,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   *out_plan = nullptr;
   const cbd_problem p = *problem;
   int32_t force = CBD_KERNEL_AUTO;
+  bool no_split = false;
   if (options) {
-    for (int i = 0; i < 7; i++)
+    for (int i = 0; i < 6; i++)
       if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->no_split != 0 && options->no_split != 1)
+      return fail(CBD_ERR_INVALID_ARG, "options.no_split must be 0 or 1");
+    no_split = options->no_split == 1;
     force = options->force_kernel;
     if (force < CBD_KERNEL_AUTO || force > CBD_KERNEL_GROUPED)
       return fail(CBD_ERR_INVALID_ARG, "unknown force_kernel");
@@ -151,7 +155,26 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   std::vector<cbd_subgemm_t> subs;
   int64_t max_taps = 0;
   std::vector<char> reached((size_t)(p.stride_h * p.stride_w), 0);
-  for (const AxisClass& ch : ah.classes) {
+  if (no_split) {
+    // Zero-insertion form: one "class" over all dX positions with all taps;
+    // the kernels test each (position, tap) term for stride divisibility.
+    cbd_subgemm_t s;
+    std::memset(&s, 0, sizeof(s));
+    s.taps_h = (int32_t)p.y;
+    s.taps_w = (int32_t)p.x;
+    s.tstep_h = s.tstep_w = 1;
+    s.delta_h = (int32_t)p.dil_h;
+    s.delta_w = (int32_t)p.dil_w;
+    s.pos_h = p.hi;
+    s.pos_w = p.wi;
+    s.m = Cg;
+    s.n = p.n * p.hi * p.wi;
+    s.k = Kg * p.y * p.x;
+    subs.push_back(s);
+    std::fill(reached.begin(), reached.end(), 1);
+    max_taps = p.y * p.x;
+  }
+  for (const AxisClass& ch : (no_split ? std::vector<AxisClass>() : ah.classes)) {
     for (const AxisClass& cw : aw.classes) {
       if (ch.taps * cw.taps == 0 || ch.pos * cw.pos == 0) continue;
       cbd_subgemm_t s;
@@ -187,7 +210,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   if (force == CBD_KERNEL_AUTO) {
     if (fast_ok(p, Cg, Kg, max_taps) && Cg >= 128)
       kernel = CBD_KERNEL_NHWC_BF16;
-    else if (grouped_ok(p, Cg, Kg, max_taps))
+    else if (!no_split && grouped_ok(p, Cg, Kg, max_taps))
       kernel = CBD_KERNEL_GROUPED;
     else
       kernel = CBD_KERNEL_GENERIC;
@@ -196,6 +219,10 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     if (kernel == CBD_KERNEL_NHWC_BF16 && !fast_ok(p, Cg, Kg, max_taps)) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "NHWC bf16 kernel needs NHWC, bf16, K/G % 64 == 0, C/G % 8 == 0, <= 16 taps per class");
+    }
+    if (kernel == CBD_KERNEL_GROUPED && no_split) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "the grouped kernels have no zero-insertion (no_split) mode");
     }
     if (kernel == CBD_KERNEL_GROUPED && !grouped_ok(p, Cg, Kg, max_taps)) {
       delete pl;
@@ -286,9 +313,15 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.Cg = (int32_t)Cg; a.Kg = (int32_t)Kg;
   a.Hi = (int32_t)p.hi; a.Wi = (int32_t)p.wi; a.Ho = (int32_t)Ho; a.Wo = (int32_t)Wo;
   a.Y = (int32_t)p.y; a.X = (int32_t)p.x;
-  a.Sh = p.stride_h; a.Sw = p.stride_w;
-  a.tstep_h = (int32_t)ah.T; a.tstep_w = (int32_t)aw.T;
+  // no_split: positions are dX positions themselves (S = 1 in the position
+  // map), every tap (T = 1); the true stride, pad and dilation go alongside.
+  a.Sh = no_split ? 1 : p.stride_h; a.Sw = no_split ? 1 : p.stride_w;
+  a.tstep_h = no_split ? 1 : (int32_t)ah.T; a.tstep_w = no_split ? 1 : (int32_t)aw.T;
   a.delta_h = (int32_t)ah.delta; a.delta_w = (int32_t)aw.delta;
+  a.no_split = no_split ? 1 : 0;
+  a.str_h = p.stride_h; a.str_w = p.stride_w;
+  a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+  a.dil_h = p.dil_h; a.dil_w = p.dil_w;
   a.dy_bytes = (uint32_t)(p.n * p.k * Ho * Wo * es);
   a.w_bytes = (uint32_t)(p.k * Cg * p.y * p.x * es);
   a.dx_bytes = (uint32_t)(p.n * p.c * p.hi * p.wi * es);

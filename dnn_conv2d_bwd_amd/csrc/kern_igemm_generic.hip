@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
     const int k0 = (ktc - tap * kpt) * BK;
     const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
     const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-    const int ho = pth + s.beta_h - a.delta_h * jh, wo = ptw + s.beta_w - a.delta_w * jw;
+    const int ho = dev::dy_index(a.no_split, pth, s.beta_h, a.delta_h, jh, a.pad_h, a.dil_h, a.str_h);
+    const int wo = dev::dy_index(a.no_split, ptw, s.beta_w, a.delta_w, jw, a.pad_w, a.dil_w, a.str_w);
     const bool bok = live && bp_ok && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
     const int abase = LAYOUT == 0 ? ((g * a.Kg) * a.Cg + ac) * YX + ty * a.X + tx
                                   : ((g * a.Kg) * YX + ty * a.X + tx) * a.Cg + ac;

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
     for (int tap = 0; tap < ntaps; tap++) {
       const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
-      const int ho = th + s.beta_h - a.delta_h * jh, wo = tw + s.beta_w - a.delta_w * jw;
+      const int ho = dev::dy_index(a.no_split, th, s.beta_h, a.delta_h, jh, a.pad_h, a.dil_h, a.str_h);
+      const int wo = dev::dy_index(a.no_split, tw, s.beta_w, a.delta_w, jw, a.pad_w, a.dil_w, a.str_w);
       const bool ok = pv && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
       gtab[tap * BN + tid] = ok ? (uint32_t)(((n * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg) * 2u : dev::kOOB;
     }

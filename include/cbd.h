@@ -89,7 +89,15 @@ typedef enum {
 
 typedef struct {
   int32_t force_kernel; /* cbd_kernel; CBD_KERNEL_AUTO lets the planner choose */
-  int32_t reserved[7];  /* must be zero */
+  int32_t no_split;     /* 1: the zero-insertion form instead of the residue
+                           split, as a comparison baseline (the BOO listing
+                           of fusilli issue #101 convolves a zero-inserted
+                           dY): one GEMM over every dX position and all Y*X
+                           taps, where a term whose dY index is not a
+                           multiple of the stride (an inserted zero) reads 0.
+                           Executes up to S_h*S_w times the MACs; generic and
+                           NHWC bf16 families only (grouped: UNSUPPORTED). */
+  int32_t reserved[6];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a

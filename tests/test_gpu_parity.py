@@ -276,3 +276,64 @@ def test_graph_replay_matches_eager(name):
         torch.cuda.synchronize()
         assert torch.equal(dx.view(torch.int16 if p.dtype == "bf16" else torch.int32),
                            want.view(torch.int16 if p.dtype == "bf16" else torch.int32)), (name, rep)
+
+
+# ------------------------------------------------- zero-insertion baseline ---
+
+def plan_no_split(p, force=cbd.KERNEL_AUTO):
+    dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+    return cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                    (p.dh, p.dw), p.layout, dt, force_kernel=force, no_split=True)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2-14-3", "c3a", "c3b", "c5-s2"])
+def test_no_split_vs_oracle(name):
+    """The zero-insertion comparison mode computes the same dX."""
+    p = by_name(name)
+    print(f"[no-split] {name}", flush=True)
+    dy, w = operands(p)
+    run = GpuRun(p, plan_no_split(p), to_device(dy, p), to_device(w, p))()
+    ok, info = check(p, run, oracle.bwd_data(p, dy, w))
+    assert ok, info
+    assert run.guards_intact()
+
+
+def test_no_split_c4_integer_exact():
+    """Headline problem in the zero-insertion form on the large-tile kernel:
+    bit-exact against its two-GEMM form on integer data."""
+    p = by_name("c4")
+    print("[no-split] c4", flush=True)
+    dy, w = operands(p, "int")
+    pl = plan_no_split(p)
+    assert pl.info().kernel == cbd.KERNEL_NHWC_BF16
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    got = run.result_f32()
+    ref = np.empty(got.shape, dtype=np.float64)
+    for r in range(2):
+        ref[:, 0, r::2, :] = (dy[:, 0].reshape(-1, p.k).astype(np.float64)
+                              @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
+    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, ref))
+    assert np.array_equal(got, want.reshape(got.shape))
+    assert run.guards_intact()
+
+
+@pytest.mark.parametrize("family,seed,count", [
+    (cbd.KERNEL_GENERIC, 31, 60),
+    (cbd.KERNEL_NHWC_BF16, 32, 25),
+])
+def test_fuzz_no_split_integer_exact(family, seed, count):
+    for i, p in enumerate(fuzz_problems(seed, count, family=family)):
+        print(f"[fuzz-no-split] family={family} i={i} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(3000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(3000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
+        try:
+            pl = plan_no_split(p, family)
+        except cbd.CbdError:
+            continue  # e.g. more than 16 taps for the large-tile kernel
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        want = exact_expected_bits(p, oracle.bwd_data(p, dy, w))
+        want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), p
+        assert run.guards_intact(), p

@@ -165,6 +165,36 @@ def test_forced_kernels():
     assert e.value.status == 2
 
 
+def test_no_split_plans():
+    """Zero-insertion comparison mode: one sub-GEMM over all dX positions and
+    all taps, no zero regions, MACs = N*C*(K/G)*Hi*Wi*Y*X."""
+    for q in PROBLEMS:
+        dt = cbd.F32 if q.dtype == "f32" else cbd.BF16
+        pl = cbd.plan(q.n, q.g, q.c, q.k, q.hi, q.wi, q.y, q.x, (q.sh, q.sw), (q.ph, q.pw),
+                      (q.dh, q.dw), q.layout, dt, no_split=True)
+        inf = pl.info()
+        assert inf.num_subgemms == 1 and inf.num_zero_regions == 0 and inf.launches == 1
+        assert inf.kernel != cbd.KERNEL_GROUPED
+        assert inf.executed_macs == q.n * q.c * (q.k // q.g) * q.hi * q.wi * q.y * q.x
+        (s,) = pl.subgemms()
+        assert (s.pos_h, s.pos_w, s.taps_h, s.taps_w) == (q.hi, q.wi, q.y, q.x)
+        assert s.tile_begin == 0 and s.tiles == inf.grid_main
+    c4 = [q for q in PROBLEMS if q.name == "c4"][0]
+    split = plan_of(c4).info().executed_macs
+    assert cbd.plan(problem=cbd.make_problem(c4.n, 1, c4.c, c4.k, c4.hi, c4.wi, c4.y, c4.x,
+                                             (c4.sh, c4.sw), 0, 1, "nhwc", "bf16"),
+                    no_split=True).info().executed_macs == 2 * split
+    c5 = [q for q in PROBLEMS if q.name == "c5-s1"][0]
+    with pytest.raises(cbd.CbdError) as e:
+        cbd.plan(c5.n, c5.g, c5.c, c5.k, c5.hi, c5.wi, c5.y, c5.x, 1, 1, 1, "nhwc", "bf16",
+                 force_kernel=cbd.KERNEL_GROUPED, no_split=True)
+    assert e.value.status == 2
+    bad = cbd.PlanOptions(cbd.KERNEL_AUTO, 2)
+    h = ctypes.c_void_p()
+    prob = cbd.make_problem(2, 1, 8, 8, 8, 8, 3, 3, 2, 1, 1, "nchw", "f32")
+    assert cbd._lib.cbd_plan_ex(ctypes.byref(prob), ctypes.byref(bad), ctypes.byref(h)) == 1
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("n", 0, 1), ("g", 3, 1), ("c", -1, 1), ("stride_h", 0, 1), ("pad_w", -1, 1),
     ("dil_w", 0, 1), ("layout", 7, 1), ("dtype", 9, 1), ("y", 40, 1),
