@@ -58,6 +58,46 @@ __device__ inline int dy_index(int no_split, int t, int beta, int delta, int j, 
   return (num >= 0 && num % str == 0) ? num / str : -1;
 }
 
+// Zero-fill work item `item` (regions reg[0..nreg), item_begin ascending):
+// one element (NCHW, or NHWC rows not a multiple of 16 bytes) or one
+// 16-byte chunk of an NHWC pixel row of an unreached dX phase lattice.
+__device__ inline void zero_item(__amdgpu_buffer_rsrc_t rdx, int layout, int esize, int chunk, int C,
+                                 int Hi, int Wi, int Sh, int Sw, const ZeroDesc* reg, int nreg,
+                                 int64_t item) {
+  int r = 0;
+  for (int i = 1; i < nreg; i++)
+    if (reg[i].item_begin <= item) r = i;
+  const ZeroDesc d = reg[r];
+  int64_t li = item - d.item_begin;
+  uint32_t off;
+  if (layout == 1) {
+    const int64_t per_pos = (int64_t)C * esize / chunk;
+    const int64_t cidx = li % per_pos;
+    int64_t pos = li / per_pos;
+    const int64_t b = pos % d.pos_w;
+    pos /= d.pos_w;
+    const int64_t a = pos % d.pos_h;
+    const int64_t n = pos / d.pos_h;
+    const int64_t hi = d.phase_h + (int64_t)Sh * a, wi = d.phase_w + (int64_t)Sw * b;
+    off = (uint32_t)((((n * Hi + hi) * Wi + wi) * C) * esize + cidx * chunk);
+  } else {
+    const int64_t b = li % d.pos_w;
+    li /= d.pos_w;
+    const int64_t a = li % d.pos_h;
+    const int64_t nc = li / d.pos_h;
+    const int64_t hi = d.phase_h + (int64_t)Sh * a, wi = d.phase_w + (int64_t)Sw * b;
+    off = (uint32_t)(((nc * Hi + hi) * Wi + wi) * esize);
+  }
+  if (chunk == 16) {
+    typedef uint32_t u4z __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(u4z{0u, 0u, 0u, 0u}, rdx, off, 0, 0);
+  } else if (chunk == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(0u, rdx, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rdx, off, 0, 0);
+  }
+}
+
 // Class owning logical tile t (tile_begin ascends with the class index).
 __device__ inline int find_class(const GemmArgs& a, int t) {
   int r = 0;

@@ -23,6 +23,26 @@ struct SubDesc {
   int32_t tile_begin;  // first logical workgroup of this class
 };
 
+// One dX phase lattice (phase_h + Sh*a, phase_w + Sw*b) that no tap reaches.
+struct ZeroDesc {
+  int32_t phase_h, phase_w;
+  int32_t pos_h, pos_w;
+  int64_t item_begin;  // first work item of this region
+};
+
+// Zero-fill folded into the main launch as extra workgroups (generic family,
+// at most kMaxFusedZero regions): workgroup total_tiles + i clears work items
+// 256*i .. 256*i + 255 exactly as the standalone zero-fill kernel would.
+constexpr int kMaxFusedZero = 4;
+struct FusedZero {
+  int32_t num_regions;  // 0: nothing folded in
+  int32_t layout, esize, chunk;
+  int32_t C, Hi, Wi, Sh, Sw;
+  int32_t pad_;
+  int64_t total_items;
+  ZeroDesc reg[kMaxFusedZero];
+};
+
 struct GemmArgs {
   // problem (element counts; every tensor is < 2^31 bytes)
   int32_t N, G, C, K, Cg, Kg;
@@ -46,15 +66,10 @@ struct GemmArgs {
   const void* dy;
   const void* w;
   void* dx;
+  FusedZero fz;
   SubDesc sub[kMaxSub];
 };
 
-// One dX phase lattice (phase_h + Sh*a, phase_w + Sw*b) that no tap reaches.
-struct ZeroDesc {
-  int32_t phase_h, phase_w;
-  int32_t pos_h, pos_w;
-  int64_t item_begin;  // first work item of this region
-};
 
 struct ZeroArgs {
   int32_t N, C, Hi, Wi, Sh, Sw;

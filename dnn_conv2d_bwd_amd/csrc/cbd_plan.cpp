@@ -370,6 +370,24 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     return fail(CBD_ERR_UNSUPPORTED, "zero-fill grid too large");
   }
 
+  // Generic family with few zero regions: fold the zero-fill into the main
+  // launch as extra workgroups (one launch instead of two).
+  int64_t grid_zero = ceil_div(items, cbd::kZeroThreads);
+  int64_t grid_main = tile;
+  std::memset(&a.fz, 0, sizeof(a.fz));
+  if (kernel == CBD_KERNEL_GENERIC && items > 0 && (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
+      cbd::kZeroThreads == cbd::kGenericThreads &&
+      (tile + grid_zero) * cbd::kGenericThreads < (int64_t(1) << 32)) {
+    cbd::FusedZero& f = a.fz;
+    f.num_regions = z.num_regions;
+    f.layout = z.layout; f.esize = z.esize; f.chunk = z.chunk;
+    f.C = z.C; f.Hi = z.Hi; f.Wi = z.Wi; f.Sh = z.Sh; f.Sw = z.Sw;
+    f.total_items = items;
+    for (size_t i = 0; i < zeros.size(); i++) f.reg[i] = z.reg[i];
+    grid_main = tile + grid_zero;
+    grid_zero = 0;
+  }
+
   cbd_plan_info_t& info = pl->info;
   info.ho = Ho;
   info.wo = Wo;
@@ -380,9 +398,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.tile_n = (int32_t)a.tile_n;
   info.tile_k = (int32_t)bk;
   info.threads_main = (int32_t)threads;
-  info.grid_main = tile;
-  info.grid_zero = ceil_div(items, cbd::kZeroThreads);
-  info.launches = (tile > 0 ? 1 : 0) + (items > 0 ? 1 : 0);
+  info.grid_main = grid_main;
+  info.grid_zero = grid_zero;
+  info.launches = (grid_main > 0 ? 1 : 0) + (grid_zero > 0 ? 1 : 0);
   info.useful_flops = 2 * p.n * p.c * Kg * Ho * Wo * p.y * p.x;
   info.executed_macs = exec;
   info.zero_elems = zero_elems;

@@ -74,6 +74,15 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
 
+  if ((int)blockIdx.x >= a.total_tiles) {  // zero-fill folded into this launch
+    const FusedZero& z = a.fz;
+    const int64_t item = (int64_t)(blockIdx.x - a.total_tiles) * kGenericThreads + tid;
+    if (item < z.total_items)
+      dev::zero_item(dev::rsrc(a.dx, a.dx_bytes), z.layout, z.esize, z.chunk, z.C, z.Hi, z.Wi,
+                     z.Sh, z.Sw, z.reg, z.num_regions, item);
+    return;
+  }
+
   const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   const int npix_img = s.pos_h * s.pos_w;

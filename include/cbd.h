@@ -142,8 +142,10 @@ typedef struct {
   int32_t tile_m, tile_n, tile_k;
   int32_t threads_main;     /* workgroup size of the main launch */
   int32_t launches;         /* kernels per cbd_run (1 or 2) */
-  int64_t grid_main;        /* workgroups of the main launch */
-  int64_t grid_zero;        /* workgroups of the zero-fill launch (0 if none) */
+  int64_t grid_main;        /* workgroups of the main launch (generic family:
+                               includes the zero-fill workgroups folded into it) */
+  int64_t grid_zero;        /* workgroups of a separate zero-fill launch (0 if
+                               none or folded into the main launch) */
   int64_t useful_flops;     /* 2*N*C*(K/G)*Ho*Wo*Y*X */
   int64_t executed_macs;    /* sum over sub-GEMMs of G*M*N*K (valid-tap MACs
                                plus those of taps falling off dY's edge) */
