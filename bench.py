@@ -148,6 +148,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain copy of this size (rocprofv3 counter scaling)")
     ap.add_argument("--force-kernel", type=int, default=-1)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="override the problem's batch N (e.g. one GPU's share of a "
+                         "batch-sharded job)")
     ap.add_argument("--no-split", action="store_true",
                     help="time the zero-insertion form (comparison baseline) instead of the "
                          "residue split")
@@ -173,6 +176,8 @@ def main():
         all_problems(args)
         return
     p = problem_by_name(args.problem)
+    if args.batch:
+        p = p.with_(n=args.batch)
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                   (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
