@@ -41,9 +41,11 @@ PEAK_F32_TFLOPS = 157.3     # 256 CU * 2.4 GHz * 256 f32 MFMA flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 # (kernel family, row variant) -> source file and kernel symbol
 KERNEL_SRC = {(0, 0): "kern_igemm_generic.hip", (1, 0): "kern_igemm_nhwc_bf16.hip",
-              (2, 0): "kern_grouped_direct.hip", (2, 1): "kern_grouped_rows.hip"}
+              (2, 0): "kern_grouped_direct.hip", (2, 1): "kern_grouped_rows.hip",
+              (2, 2): "kern_grouped_pipe.hip"}
 KERNEL_SYMBOL = {(0, 0): "igemm_generic_kernel", (1, 0): "igemm_nhwc_bf16_kernel",
-                 (2, 0): "grouped_direct_kernel", (2, 1): "grouped_rows_kernel"}
+                 (2, 0): "grouped_direct_kernel", (2, 1): "grouped_rows_kernel",
+                 (2, 2): "grouped_pipe_kernel"}
 # Bound of each workload problem (dense-contraction rows on MFMA, the rest on
 # HBM; the small fp32 rows are launch-latency bound in practice).
 LATENCY_BOUND = ("c1", "c2-14-1", "c2-14-3", "c2-15-1", "c2-15-3", "c2-16-1", "c2-16-3")
@@ -70,7 +72,7 @@ def algorithmic_bytes(p, info):
 
 
 def kernel_key(info):
-    return (info.kernel, 1 if info.lds_dynamic > 0 else 0)
+    return (info.kernel, 2 if info.rows_per_wg > 0 else 1 if info.lds_dynamic > 0 else 0)
 
 
 def read_traffic(key):
@@ -151,6 +153,9 @@ def main():
     ap.add_argument("--batch", type=int, default=0,
                     help="override the problem's batch N (e.g. one GPU's share of a "
                          "batch-sharded job)")
+    ap.add_argument("--rows-per-wg", type=int, default=0,
+                    help="grouped problems: output rows per workgroup of the pipelined row "
+                         "kernel (0 automatic, -1 the one-row kernel)")
     ap.add_argument("--no-split", action="store_true",
                     help="time the zero-insertion form (comparison baseline) instead of the "
                          "residue split")
@@ -181,7 +186,7 @@ def main():
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                   (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
-                  no_split=args.no_split)
+                  no_split=args.no_split, rows_per_wg=args.rows_per_wg)
     info = pl.info()
     sh = pl.shapes()
     dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
@@ -246,6 +251,7 @@ def main():
                    "form": "zero-insertion (no residue split)" if args.no_split else "residue split",
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
+                   "rows_per_wg": info.rows_per_wg,
                    "useful_gflop": round(flops / 1e9, 4),
                    "executed_gmac": round(info.executed_macs / 1e9, 4),
                    "alg_mbytes": round(alg_bytes / 1e6, 3)},

@@ -25,6 +25,7 @@ SOURCES = [
     "kern_igemm_nhwc_bf16.hip",
     "kern_grouped_direct.hip",
     "kern_grouped_rows.hip",
+    "kern_grouped_pipe.hip",
     "kern_zero_fill.hip",
 ]
 

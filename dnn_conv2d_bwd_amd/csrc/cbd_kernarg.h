@@ -63,6 +63,7 @@ struct GemmArgs {
   int32_t str_h, str_w, pad_h, pad_w, dil_h, dil_w;  // the problem's own (no_split)
   int32_t iters;       // grouped direct kernel: positions per thread
   int32_t grp_lds;     // grouped row kernel: LDS bytes per workgroup (0: direct kernel)
+  int32_t grp_rows;    // grouped pipelined kernel: output rows per workgroup (0: other kernels)
   const void* dy;
   const void* w;
   void* dx;

@@ -100,9 +100,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   const cbd_problem p = *problem;
   int32_t force = CBD_KERNEL_AUTO;
   bool no_split = false;
+  int32_t rows_opt = 0;
   if (options) {
-    for (int i = 0; i < 6; i++)
+    for (int i = 0; i < 5; i++)
       if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->rows_per_wg < -1 || options->rows_per_wg > (1 << 20))
+      return fail(CBD_ERR_INVALID_ARG, "options.rows_per_wg must be -1, 0 or a row count");
+    rows_opt = options->rows_per_wg;
     if (options->no_split != 0 && options->no_split != 1)
       return fail(CBD_ERR_INVALID_ARG, "options.no_split must be 0 or 1");
     no_split = options->no_split == 1;
@@ -246,19 +250,40 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     threads = cbd::kGroupedThreads;
   }
 
-  // Grouped kernels.  Row kernel (C/G <= 4): one workgroup per output row
-  // of a class, the row's dY rows staged in LDS.  Direct kernel otherwise:
-  // positions per thread so that the grid is ~2048 workgroups.
+  // Grouped kernels (C/G <= 4 and 16-byte pixels first):
+  //  * pipelined kernel (taps one dY row apart): a workgroup walks R output
+  //    rows of one class and image with a ring of taps_h + 1 dY rows (each
+  //    padded to 4 KiB) in LDS; R is sized so that the grid is about one
+  //    round of resident workgroups;
+  //  * row kernel: one workgroup per output row of a class, the row's dY
+  //    rows staged in LDS;
+  //  * direct kernel otherwise: positions per thread so that the grid is
+  //    ~2048 workgroups.
   int64_t iters = 1;
   int64_t slots = 0;
   int64_t grp_lds = 0;
+  int64_t grp_rows = 0;
   if (kernel == CBD_KERNEL_GROUPED) {
     slots = cbd::kGroupedThreads / p.g;
     const int64_t pixb = p.c * es;
-    int64_t need = 0;
-    for (const auto& s : subs)
-      need = std::max<int64_t>(need, s.taps_h * (s.pos_w + aw.delta * (s.taps_w - 1)) * pixb);
-    if (Cg <= 4 && pixb % 16 == 0 && need <= cbd::kGroupedRowLds) {
+    int64_t need = 0, ring = 0, total_rows = 0, max_pos_h = 0;
+    for (const auto& s : subs) {
+      const int64_t rowb = (s.pos_w + aw.delta * (s.taps_w - 1)) * pixb;
+      need = std::max<int64_t>(need, s.taps_h * rowb);
+      ring = std::max<int64_t>(ring, (s.taps_h + 1) * ceil_div(rowb, 4096) * 4096);
+      total_rows += p.n * s.pos_h;
+      max_pos_h = std::max<int64_t>(max_pos_h, s.pos_h);
+    }
+    const bool row_ok = Cg <= 4 && pixb % 16 == 0;
+    if (row_ok && rows_opt >= 0 && ah.delta == 1 && ring > 0 && ring <= cbd::kGroupedRowLds) {
+      if (rows_opt > 0) {
+        grp_rows = std::min<int64_t>(rows_opt, max_pos_h);
+      } else {
+        const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / ring);
+        grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(total_rows, resident)));
+      }
+      grp_lds = ring;
+    } else if (row_ok && need <= cbd::kGroupedRowLds) {
       grp_lds = need;
     } else {
       int64_t total_pos = 0;
@@ -277,7 +302,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     s.id = (int32_t)i;
     s.tile_begin = tile;
     if (kernel == CBD_KERNEL_GROUPED)
-      s.tiles = grp_lds > 0 ? p.n * s.pos_h : ceil_div(s.n, slots * iters);
+      s.tiles = grp_rows > 0  ? p.n * ceil_div(s.pos_h, grp_rows)
+                : grp_lds > 0 ? p.n * s.pos_h
+                              : ceil_div(s.n, slots * iters);
     else
       s.tiles = p.g * tiles_m * ceil_div(s.n, bn);
     tile += s.tiles;
@@ -335,6 +362,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.xcd_remap = (kernel != CBD_KERNEL_GROUPED && equal_k && tile >= 64) ? 1 : 0;
   a.iters = (int32_t)iters;
   a.grp_lds = (int32_t)grp_lds;
+  a.grp_rows = (int32_t)grp_rows;
   for (size_t i = 0; i < subs.size(); i++) {
     cbd::SubDesc& d = a.sub[i];
     const cbd_subgemm_t& s = subs[i];
@@ -405,6 +433,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.executed_macs = exec;
   info.zero_elems = zero_elems;
   info.lds_dynamic = grp_lds;
+  info.rows_per_wg = grp_rows;
 
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);

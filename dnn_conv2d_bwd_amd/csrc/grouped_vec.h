@@ -1,0 +1,87 @@
+// grouped_vec.h -- small helpers shared by the grouped row kernels: one
+// group's channels at one pixel as a vector of 2..16 bytes (LDS read,
+// buffer load, buffer store), and the row -> XCD dealing.
+#pragma once
+#include "cbd_device.h"
+
+namespace cbd {
+namespace grp {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int BYTES>
+struct Vec {
+  static constexpr int W = BYTES >= 4 ? BYTES / 4 : 1;
+  uint32_t w[W];
+};
+
+// p is aligned to BYTES (a group's channels start at a multiple of their
+// size inside a 16-byte-aligned pixel row), so 8 and 16 bytes are single
+// ds_read_b64 / ds_read_b128.
+template <int BYTES>
+__device__ inline Vec<BYTES> lds_vec(const char* p) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  Vec<BYTES> v;
+  if constexpr (BYTES == 2) {
+    v.w[0] = *(const uint16_t*)p;
+  } else if constexpr (BYTES == 4) {
+    v.w[0] = *(const uint32_t*)p;
+  } else if constexpr (BYTES == 8) {
+    const u2 x = *(const u2*)p;
+    v.w[0] = x[0];
+    v.w[1] = x[1];
+  } else {
+    const u4 x = *(const u4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; i++) v.w[i] = x[i];
+  }
+  return v;
+}
+
+template <int BYTES>
+__device__ inline Vec<BYTES> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  Vec<BYTES> v;
+  if constexpr (BYTES == 2) {
+    v.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else if constexpr (BYTES == 4) {
+    v.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (BYTES == 8) {
+    auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v.w[0] = x[0];
+    v.w[1] = x[1];
+  } else {
+    auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; j++) v.w[j] = x[j];
+  }
+  return v;
+}
+
+template <int BYTES>
+__device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const Vec<BYTES>& v) {
+  if constexpr (BYTES == 2) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, off, 0, 0);
+  } else if constexpr (BYTES == 4) {
+    __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, off, 0, 0);
+  } else if constexpr (BYTES == 8) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    u2 x = {v.w[0], v.w[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
+  } else {
+    u4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+  }
+}
+
+// Logical row of hardware workgroup b: workgroups go round-robin to the 8
+// XCDs; XCD x gets logical rows 64r + 8x .. 64r + 8x + 7 in order.
+__device__ inline int chunked_row(int b, int total) {
+  const int full = total & ~63;
+  if (b >= full) return b;
+  const int r = b >> 6, i = b & 63;
+  return (r << 6) + ((i & 7) << 3) + (i >> 3);
+}
+
+}  // namespace grp
+}  // namespace cbd

@@ -18,74 +18,12 @@
 //     dY rows shared by neighbouring output rows meet in one L2.
 #include "cbd_device.h"
 #include "cbd_internal.h"
+#include "grouped_vec.h"
 
 namespace cbd {
 namespace {
 
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-template <int BYTES>
-struct Vec {
-  static constexpr int W = BYTES >= 4 ? BYTES / 4 : 1;
-  uint32_t w[W];
-};
-
-template <int BYTES>
-__device__ inline Vec<BYTES> lds_vec(const char* p) {
-  Vec<BYTES> v;
-  if constexpr (BYTES == 2) {
-    v.w[0] = *(const uint16_t*)p;
-  } else {
-#pragma unroll
-    for (int i = 0; i < Vec<BYTES>::W; i++) v.w[i] = ((const uint32_t*)p)[i];
-  }
-  return v;
-}
-
-template <int BYTES>
-__device__ inline Vec<BYTES> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  Vec<BYTES> v;
-  if constexpr (BYTES == 2) {
-    v.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  } else if constexpr (BYTES == 4) {
-    v.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  } else if constexpr (BYTES == 8) {
-    auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    v.w[0] = x[0];
-    v.w[1] = x[1];
-  } else {
-    auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; j++) v.w[j] = x[j];
-  }
-  return v;
-}
-
-template <int BYTES>
-__device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const Vec<BYTES>& v) {
-  if constexpr (BYTES == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, off, 0, 0);
-  } else if constexpr (BYTES == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, off, 0, 0);
-  } else if constexpr (BYTES == 8) {
-    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-    u2 x = {v.w[0], v.w[1]};
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
-  } else {
-    u4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
-  }
-}
-
-// Logical row of hardware workgroup b: workgroups go round-robin to the 8
-// XCDs; XCD x gets logical rows 64r + 8x .. 64r + 8x + 7 in order.
-__device__ inline int chunked_row(int b, int total) {
-  const int full = total & ~63;
-  if (b >= full) return b;
-  const int r = b >> 6, i = b & 63;
-  return (r << 6) + ((i & 7) << 3) + (i >> 3);
-}
+using namespace grp;
 
 template <int DT, int CG>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_rows_kernel(const GemmArgs a) {

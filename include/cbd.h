@@ -83,8 +83,11 @@ typedef enum {
   CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 32 == 0, K/G <= 131072,
                                C/G % 8 == 0, at most 16 taps per class:
                                256x256x32 tiles, bf16 MFMA, 4-stage LDS */
-  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G in {1,2,4,8}, G | 256:
-                               direct per-group accumulation, filter in registers */
+  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G in {1,2,4,8}, G | 256, at most
+                               9 taps per class: per-group accumulation, filter
+                               in registers; dY rows streamed through an LDS
+                               ring when C/G <= 4, a pixel is a multiple of 16
+                               bytes and a class's taps are one dY row apart */
 } cbd_kernel;
 
 typedef struct {
@@ -97,7 +100,12 @@ typedef struct {
                            multiple of the stride (an inserted zero) reads 0.
                            Executes up to S_h*S_w times the MACs; generic and
                            NHWC bf16 families only (grouped: UNSUPPORTED). */
-  int32_t reserved[6];  /* must be zero */
+  int32_t rows_per_wg;  /* grouped family, pipelined row kernel: output rows
+                           per workgroup (0: the planner's choice; larger than
+                           a class's rows: clamped); -1: never the pipelined
+                           kernel (row or direct kernel instead).  Other
+                           families ignore it. */
+  int32_t reserved[5];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
@@ -151,8 +159,9 @@ typedef struct {
                                plus those of taps falling off dY's edge) */
   int64_t zero_elems;       /* dX elements written by the zero-fill launch */
   int64_t lds_dynamic;      /* dynamic LDS bytes per workgroup of the main
-                               launch (grouped family: > 0 selects the row
-                               kernel, 0 the direct kernel) */
+                               launch (grouped family: 0 for the direct kernel) */
+  int64_t rows_per_wg;      /* grouped family: output rows per workgroup of the
+                               pipelined row kernel (0: another kernel) */
 } cbd_plan_info_t;
 
 typedef struct {

@@ -245,6 +245,45 @@ def test_fuzz_random_values(family, seed, count):
         assert ok, (p, info)
 
 
+# Grouped family: the pipelined row kernel with several rows per workgroup
+# (the automatic choice gives tiny problems one row each), and the one-row
+# kernel it replaces (rows_per_wg = -1).
+@pytest.mark.parametrize("seed,count", [(15, 80), (16, 40)])
+def test_fuzz_grouped_rows_per_wg(seed, count):
+    rng = random.Random(seed + 1000)
+    for i, p in enumerate(fuzz_problems(seed, count, family=cbd.KERNEL_GROUPED)):
+        rows = rng.choice([-1, 1, 2, 3, 5, 64])
+        pl = plan_for(p, cbd.KERNEL_GROUPED, rows)
+        inf = pl.info()
+        print(f"[fuzz-rows] i={i} rows={rows} got={inf.rows_per_wg} lds={inf.lds_dynamic} {p}",
+              flush=True)
+        if rows == -1:
+            assert inf.rows_per_wg == 0
+        sh = oracle.shapes(p)
+        dy = small_ints(3000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(3000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        want = exact_expected_bits(p, oracle.bwd_data(p, dy, w))
+        want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), (p, rows)
+        assert run.guards_intact(), (p, rows)
+
+
+@pytest.mark.parametrize("name", ["c5-s2", "c5-s1"])
+@pytest.mark.parametrize("rows", [-1, 1, 3, 56])
+def test_grouped_workload_rows_per_wg(name, rows):
+    p = by_name(name)
+    print(f"[rows] {name} rows={rows}", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p, cbd.KERNEL_AUTO, rows)
+    assert pl.info().kernel == cbd.KERNEL_GROUPED
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    ok, info = check(p, run, oracle.bwd_data(p, dy, w))
+    assert ok, info
+    assert run.guards_intact()
+
+
 # ------------------------------------------------------------ graph capture ---
 
 @pytest.mark.parametrize("name", ["c3b", "c4", "c5-s2"])
