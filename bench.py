@@ -42,10 +42,10 @@ PEAK_HBM_GBS = 8000.0
 # (kernel family, row variant) -> source file and kernel symbol
 KERNEL_SRC = {(0, 0): "kern_igemm_generic.hip", (1, 0): "kern_igemm_nhwc_bf16.hip",
               (2, 0): "kern_grouped_direct.hip", (2, 1): "kern_grouped_rows.hip",
-              (2, 2): "kern_grouped_pipe.hip"}
+              (2, 2): "kern_grouped_pipe.hip", (2, 3): "kern_grouped_mfma.hip"}
 KERNEL_SYMBOL = {(0, 0): "igemm_generic_kernel", (1, 0): "igemm_nhwc_bf16_kernel",
                  (2, 0): "grouped_direct_kernel", (2, 1): "grouped_rows_kernel",
-                 (2, 2): "grouped_pipe_kernel"}
+                 (2, 2): "grouped_pipe_kernel", (2, 3): "grouped_mfma_kernel"}
 # Bound of each workload problem (dense-contraction rows on MFMA, the rest on
 # HBM; the small fp32 rows are launch-latency bound in practice).
 LATENCY_BOUND = ("c1", "c2-14-1", "c2-14-3", "c2-15-1", "c2-15-3", "c2-16-1", "c2-16-3")
@@ -72,14 +72,16 @@ def algorithmic_bytes(p, info):
 
 
 def kernel_key(info):
-    return (info.kernel, 2 if info.rows_per_wg > 0 else 1 if info.lds_dynamic > 0 else 0)
+    return (info.kernel, info.variant)
 
 
-def read_traffic(key):
-    """HBM bytes per launch recorded under profiles/ for this kernel, if the
-    kernel source still matches the one the counters were taken on."""
+def read_traffic(key, problem):
+    """HBM bytes per launch recorded under profiles/ for this kernel on this
+    problem, if the kernel source still matches the one the counters were
+    taken on."""
     src = os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", KERNEL_SRC[key])
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_SRC[key].split('.')[0]}_traffic.txt")
+    name = KERNEL_SYMBOL[key][:-len("_kernel")]
+    path = os.path.join(ROOT, "profiles", f"{name}_{problem}_traffic.txt")
     if not os.path.exists(path):
         return None
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -156,6 +158,10 @@ def main():
     ap.add_argument("--rows-per-wg", type=int, default=0,
                     help="grouped problems: output rows per workgroup of the pipelined row "
                          "kernel (0 automatic, -1 the one-row kernel)")
+    ap.add_argument("--cols-per-wg", type=int, default=0,
+                    help="grouped MFMA kernel: positions of a row per workgroup (0 automatic)")
+    ap.add_argument("--grouped-dot", action="store_true",
+                    help="grouped problems: dot-product instructions instead of 4x4x4 MFMA")
     ap.add_argument("--no-split", action="store_true",
                     help="time the zero-insertion form (comparison baseline) instead of the "
                          "residue split")
@@ -186,7 +192,8 @@ def main():
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                   (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
-                  no_split=args.no_split, rows_per_wg=args.rows_per_wg)
+                  no_split=args.no_split, rows_per_wg=args.rows_per_wg,
+                  grouped_dot=args.grouped_dot, cols_per_wg=args.cols_per_wg)
     info = pl.info()
     sh = pl.shapes()
     dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
@@ -228,7 +235,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops / launch_s / 1e12, 2), "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = read_traffic(kernel_key(info))
+    roof["traffic"] = read_traffic(kernel_key(info), p.name) if not (args.batch or args.no_split) else None
     roof["kernel"] = KERNEL_SYMBOL[kernel_key(info)]
     roof["launch_us_mean"] = round(launch_s * 1e6, 3)
     roof["launches_per_step"] = info.launches
@@ -251,7 +258,7 @@ def main():
                    "form": "zero-insertion (no residue split)" if args.no_split else "residue split",
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
-                   "rows_per_wg": info.rows_per_wg,
+                   "rows_per_wg": info.rows_per_wg, "cols_per_wg": info.cols_per_wg,
                    "useful_gflop": round(flops / 1e9, 4),
                    "executed_gmac": round(info.executed_macs / 1e9, 4),
                    "alg_mbytes": round(alg_bytes / 1e6, 3)},

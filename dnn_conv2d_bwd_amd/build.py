@@ -26,6 +26,7 @@ SOURCES = [
     "kern_grouped_direct.hip",
     "kern_grouped_rows.hip",
     "kern_grouped_pipe.hip",
+    "kern_grouped_mfma.hip",
     "kern_zero_fill.hip",
 ]
 

@@ -57,7 +57,8 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
     switch (info.kernel) {
       case CBD_KERNEL_NHWC_BF16: err = cbd::launch_nhwc_bf16(a, info.grid_main, stream); break;
       case CBD_KERNEL_GROUPED:
-        err = a.grp_rows > 0  ? cbd::launch_grouped_pipe(a, plan->prob.dtype, info.grid_main, stream)
+        err = a.grp_mfma      ? cbd::launch_grouped_mfma(a, info.grid_main, stream)
+              : a.grp_rows > 0  ? cbd::launch_grouped_pipe(a, plan->prob.dtype, info.grid_main, stream)
               : a.grp_lds > 0 ? cbd::launch_grouped_rows(a, plan->prob.dtype, info.grid_main, stream)
                               : cbd::launch_grouped(a, plan->prob.dtype, info.grid_main, stream);
         break;

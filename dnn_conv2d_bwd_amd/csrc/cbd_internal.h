@@ -26,6 +26,7 @@ int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream);
 int launch_grouped(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_pipe(const GemmArgs& a, int dtype, int64_t grid, void* stream);
+int launch_grouped_mfma(const GemmArgs& a, int64_t grid, void* stream);
 int launch_zero_fill(const ZeroArgs& z, int64_t grid, void* stream);
 const char* hip_error_name(int err);
 
@@ -34,8 +35,8 @@ constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads
 constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 256, kFastMaxTaps = 16;
 constexpr int kFastMaxKTiles = 4096;  // k tiles per tap (K/G / 32): bound of the kernel's tap division
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
-constexpr int kGroupedRowLds = 64 * 1024;  // row kernels: staged dY rows per workgroup
-constexpr int kLdsPerCu = 160 * 1024;       // gfx950 LDS per compute unit
+constexpr int kGroupedRowLds = 64 * 1024;  // one-row kernel: staged dY rows per workgroup
+constexpr int kLdsPerCu = 160 * 1024;       // gfx950 LDS per compute unit (also the per-workgroup limit)
 constexpr int kZeroThreads = 256, kZeroItemsPerThread = 4;
 
 }  // namespace cbd

@@ -63,7 +63,9 @@ struct GemmArgs {
   int32_t str_h, str_w, pad_h, pad_w, dil_h, dil_w;  // the problem's own (no_split)
   int32_t iters;       // grouped direct kernel: positions per thread
   int32_t grp_lds;     // grouped row kernel: LDS bytes per workgroup (0: direct kernel)
-  int32_t grp_rows;    // grouped pipelined kernel: output rows per workgroup (0: other kernels)
+  int32_t grp_rows;    // grouped pipelined kernels: output rows per workgroup (0: other kernels)
+  int32_t grp_mfma;    // 1: the pipelined kernel on 4x4x4 MFMA (bf16, C/G = 4, G in {32, 64})
+  int32_t grp_cols;    // MFMA pipelined kernel: positions per column block of a row
   const void* dy;
   const void* w;
   void* dx;

@@ -101,9 +101,17 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int32_t force = CBD_KERNEL_AUTO;
   bool no_split = false;
   int32_t rows_opt = 0;
+  bool grouped_dot = false;
+  int32_t cols_opt = 0;
   if (options) {
-    for (int i = 0; i < 5; i++)
+    for (int i = 0; i < 3; i++)
       if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->cols_per_wg < 0 || options->cols_per_wg > (1 << 20))
+      return fail(CBD_ERR_INVALID_ARG, "options.cols_per_wg must be 0 or a position count");
+    cols_opt = options->cols_per_wg;
+    if (options->grouped_dot != 0 && options->grouped_dot != 1)
+      return fail(CBD_ERR_INVALID_ARG, "options.grouped_dot must be 0 or 1");
+    grouped_dot = options->grouped_dot == 1;
     if (options->rows_per_wg < -1 || options->rows_per_wg > (1 << 20))
       return fail(CBD_ERR_INVALID_ARG, "options.rows_per_wg must be -1, 0 or a row count");
     rows_opt = options->rows_per_wg;
@@ -251,10 +259,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   }
 
   // Grouped kernels (C/G <= 4 and 16-byte pixels first):
-  //  * pipelined kernel (taps one dY row apart): a workgroup walks R output
+  //  * pipelined kernels (taps one dY row apart): a workgroup walks R output
   //    rows of one class and image with a ring of taps_h + 1 dY rows (each
   //    padded to 4 KiB) in LDS; R is sized so that the grid is about one
-  //    round of resident workgroups;
+  //    round of resident workgroups.  bf16 with 4 channels per group and
+  //    32 or 64 groups runs the products on 4x4x4 MFMA (its slots also hold
+  //    3 columns past the row, read by a partial quad of positions), the
+  //    rest on dot-product instructions;
   //  * row kernel: one workgroup per output row of a class, the row's dY
   //    rows staged in LDS;
   //  * direct kernel otherwise: positions per thread so that the grid is
@@ -262,25 +273,58 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int64_t iters = 1;
   int64_t slots = 0;
   int64_t grp_lds = 0;
-  int64_t grp_rows = 0;
+  int64_t grp_rows = 0, grp_cols = 0;
+  bool grp_mfma = false;
   if (kernel == CBD_KERNEL_GROUPED) {
     slots = cbd::kGroupedThreads / p.g;
     const int64_t pixb = p.c * es;
-    int64_t need = 0, ring = 0, total_rows = 0, max_pos_h = 0;
+    const bool mfma_ok = !grouped_dot && p.dtype == CBD_BF16 && Cg == 4 && (p.g == 32 || p.g == 64);
+    int64_t need = 0, ring_dot = 0, max_pos_h = 0, max_pos_w = 0;
     for (const auto& s : subs) {
       const int64_t rowb = (s.pos_w + aw.delta * (s.taps_w - 1)) * pixb;
       need = std::max<int64_t>(need, s.taps_h * rowb);
-      ring = std::max<int64_t>(ring, (s.taps_h + 1) * ceil_div(rowb, 4096) * 4096);
-      total_rows += p.n * s.pos_h;
+      ring_dot = std::max<int64_t>(ring_dot, (s.taps_h + 1) * ceil_div(rowb, 4096) * 4096);
       max_pos_h = std::max<int64_t>(max_pos_h, s.pos_h);
+      max_pos_w = std::max<int64_t>(max_pos_w, s.pos_w);
     }
+    // MFMA kernel, column blocks of cb positions: ring slots of cb + span + 3
+    // columns (whole KiB) plus the output row buffer.
+    auto lds_mfma = [&](int64_t cb) {
+      int64_t r = 0;
+      for (const auto& s : subs) {
+        const int64_t seg = std::min<int64_t>(cb, s.pos_w);
+        const int64_t rowb = (seg + aw.delta * (s.taps_w - 1) + 3) * pixb;
+        r = std::max<int64_t>(r, (s.taps_h + 1) * ceil_div(rowb, 1024) * 1024 + 4 * ceil_div(seg, 4) * pixb);
+      }
+      return r;
+    };
     const bool row_ok = Cg <= 4 && pixb % 16 == 0;
-    if (row_ok && rows_opt >= 0 && ah.delta == 1 && ring > 0 && ring <= cbd::kGroupedRowLds) {
+    const bool pipe_ok = row_ok && rows_opt >= 0 && ah.delta == 1 && !subs.empty();
+    int64_t ring = ring_dot;
+    if (pipe_ok && mfma_ok) {
+      // Whole rows unless that leaves fewer than 3 workgroups per compute
+      // unit; then the widest multiple of 4 that fits (or the forced width).
+      int64_t cb = 4 * ceil_div(max_pos_w, 4);
+      if (cols_opt > 0) {
+        cb = std::min<int64_t>(cb, 4 * ceil_div(cols_opt, 4));
+      } else {
+        for (int64_t k = 2; lds_mfma(cb) > cbd::kLdsPerCu / 3 && cb > 4; k++)
+          cb = 4 * ceil_div(max_pos_w, 4 * k);
+      }
+      if (lds_mfma(cb) <= cbd::kLdsPerCu) {
+        grp_mfma = true;
+        grp_cols = cb;
+        ring = lds_mfma(cb);
+      }
+    }
+    if (pipe_ok && ring <= cbd::kLdsPerCu) {
+      int64_t units = 0;  // (image, class row, column block)
+      for (const auto& s : subs) units += p.n * s.pos_h * (grp_mfma ? ceil_div(s.pos_w, grp_cols) : 1);
       if (rows_opt > 0) {
         grp_rows = std::min<int64_t>(rows_opt, max_pos_h);
       } else {
         const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / ring);
-        grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(total_rows, resident)));
+        grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(units, resident)));
       }
       grp_lds = ring;
     } else if (row_ok && need <= cbd::kGroupedRowLds) {
@@ -302,7 +346,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     s.id = (int32_t)i;
     s.tile_begin = tile;
     if (kernel == CBD_KERNEL_GROUPED)
-      s.tiles = grp_rows > 0  ? p.n * ceil_div(s.pos_h, grp_rows)
+      s.tiles = grp_mfma      ? p.n * ceil_div(s.pos_h, grp_rows) * ceil_div(s.pos_w, grp_cols)
+                : grp_rows > 0  ? p.n * ceil_div(s.pos_h, grp_rows)
                 : grp_lds > 0 ? p.n * s.pos_h
                               : ceil_div(s.n, slots * iters);
     else
@@ -363,6 +408,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.iters = (int32_t)iters;
   a.grp_lds = (int32_t)grp_lds;
   a.grp_rows = (int32_t)grp_rows;
+  a.grp_mfma = grp_mfma ? 1 : 0;
+  a.grp_cols = (int32_t)grp_cols;
   for (size_t i = 0; i < subs.size(); i++) {
     cbd::SubDesc& d = a.sub[i];
     const cbd_subgemm_t& s = subs[i];
@@ -434,6 +481,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.zero_elems = zero_elems;
   info.lds_dynamic = grp_lds;
   info.rows_per_wg = grp_rows;
+  info.cols_per_wg = grp_cols;
+  info.variant = kernel != CBD_KERNEL_GROUPED ? 0 : grp_mfma ? 3 : grp_rows > 0 ? 2 : grp_lds > 0 ? 1 : 0;
 
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);

@@ -103,8 +103,7 @@ __device__ __forceinline__ void pipe_rows(const GemmArgs& a, const SubDesc& s, c
 
   // Copy dY row ho (zeros off the edge) into its ring slot: each wave issues
   // exactly ni instructions of 64 lanes x 16 bytes.
-  auto copy_row = [&](int ho) {
-    const int sl = ((ho % q.nslot) + q.nslot) % q.nslot;
+  auto copy_row = [&](int ho, int sl) {
     const bool hok = ho >= 0 && ho < a.Ho;
     const int rpix = (q.n * a.Ho + ho) * a.Wo;
     for (int i = 0; i < q.ni; i++) {
@@ -159,8 +158,14 @@ __device__ __forceinline__ void pipe_rows(const GemmArgs& a, const SubDesc& s, c
     }
   }
 
+  // Ring slot of dY row h: h mod nslot.  top = slot of row th + beta_h,
+  // advanced by one (cyclically) per output row.
+  int top = (q.th0 + s.beta_h) % q.nslot;
+  if (top < 0) top += q.nslot;
+  auto back = [&](int j) { return top - j < 0 ? top - j + q.nslot : top - j; };  // slot of row th+beta_h-j
+
   // Prologue: the taps_h rows of the first output row.
-  for (int jh = s.taps_h - 1; jh >= 0; jh--) copy_row(q.th0 + s.beta_h - jh);
+  for (int jh = s.taps_h - 1; jh >= 0; jh--) copy_row(q.th0 + s.beta_h - jh, back(jh));
 
   for (int th = q.th0; th < q.th1; th++) {
     // This wave's copies of row th + beta_h (and older) have landed and its
@@ -168,15 +173,13 @@ __device__ __forceinline__ void pipe_rows(const GemmArgs& a, const SubDesc& s, c
     // wave.  The memory clobber keeps the compiler from moving LDS reads
     // across it.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (th + 1 < q.th1) copy_row(th + 1 + s.beta_h);
+    const int next = top + 1 == q.nslot ? 0 : top + 1;
+    if (th + 1 < q.th1) copy_row(th + 1 + s.beta_h, next);
     const int hi = s.phase_h + a.Sh * th;
     const uint32_t xrow = (uint32_t)((q.n * a.Hi + hi) * a.Wi) * (uint32_t)q.pixb + (uint32_t)(q.g * VB);
     int soff[NT];
 #pragma unroll
-    for (int tp = 0; tp < NT; tp++) {
-      const int ho = th + s.beta_h - jhs[tp];
-      soff[tp] = (((ho % q.nslot) + q.nslot) % q.nslot) * q.slotb + qoff[tp];
-    }
+    for (int tp = 0; tp < NT; tp++) soff[tp] = back(jhs[tp]) * q.slotb + qoff[tp];
     if constexpr (PAIR) {
       // Two positions per pass (tw and tw + slots; the second clamped to a
       // valid column and its store dropped when past the row's end).
@@ -209,6 +212,7 @@ __device__ __forceinline__ void pipe_rows(const GemmArgs& a, const SubDesc& s, c
         store_vec<VB>(rdx, xrow + ((uint32_t)(s.phase_w + a.Sw * tw) << q.pshift), pack_out<DT, CG>(acc0));
       }
     }
+    top = next;
   }
 }
 

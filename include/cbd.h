@@ -105,7 +105,13 @@ typedef struct {
                            a class's rows: clamped); -1: never the pipelined
                            kernel (row or direct kernel instead).  Other
                            families ignore it. */
-  int32_t reserved[5];  /* must be zero */
+  int32_t grouped_dot;  /* grouped family: 1 keeps the pipelined kernel on
+                           dot-product instructions where it would use the
+                           4x4x4 MFMA (a comparison switch); 0 or 1 */
+  int32_t cols_per_wg;  /* grouped family, MFMA pipelined kernel: positions of a
+                           row per workgroup, rounded up to a multiple of 4
+                           (0: the planner's choice) */
+  int32_t reserved[3];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
@@ -161,7 +167,14 @@ typedef struct {
   int64_t lds_dynamic;      /* dynamic LDS bytes per workgroup of the main
                                launch (grouped family: 0 for the direct kernel) */
   int64_t rows_per_wg;      /* grouped family: output rows per workgroup of the
-                               pipelined row kernel (0: another kernel) */
+                               pipelined row kernels (0: another kernel) */
+  int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernel: positions
+                               per column block of a row (0: other kernels) */
+  int64_t variant;          /* kernel within the family; grouped: 0 direct,
+                               1 one row per workgroup, 2 pipelined rows on
+                               dot-product instructions, 3 pipelined rows on
+                               4x4x4 MFMA (bf16, C/G = 4, G = 32 or 64);
+                               other families: 0 */
 } cbd_plan_info_t;
 
 typedef struct {

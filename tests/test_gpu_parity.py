@@ -271,17 +271,57 @@ def test_fuzz_grouped_rows_per_wg(seed, count):
 
 
 @pytest.mark.parametrize("name", ["c5-s2", "c5-s1"])
-@pytest.mark.parametrize("rows", [-1, 1, 3, 56])
-def test_grouped_workload_rows_per_wg(name, rows):
+@pytest.mark.parametrize("rows,dot,cols", [(-1, False, 0), (1, False, 0), (3, False, 0),
+                                           (56, False, 0), (1, True, 0), (3, True, 0),
+                                           (56, True, 0), (0, False, 8), (5, False, 12),
+                                           (2, False, 56)])
+def test_grouped_workload_rows_per_wg(name, rows, dot, cols):
     p = by_name(name)
-    print(f"[rows] {name} rows={rows}", flush=True)
+    print(f"[rows] {name} rows={rows} dot={dot} cols={cols}", flush=True)
     dy, w = operands(p)
-    pl = plan_for(p, cbd.KERNEL_AUTO, rows)
-    assert pl.info().kernel == cbd.KERNEL_GROUPED
+    pl = plan_for(p, cbd.KERNEL_AUTO, rows, dot, cols)
+    inf = pl.info()
+    assert inf.kernel == cbd.KERNEL_GROUPED
+    assert inf.variant == (1 if rows == -1 else 2 if dot else 3)
     run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
     ok, info = check(p, run, oracle.bwd_data(p, dy, w))
     assert ok, info
     assert run.guards_intact()
+
+
+# The 4x4x4-MFMA pipelined kernel: bf16, 4 channels per group, 32 or 64
+# groups, random geometry and rows per workgroup; integer-exact.
+@pytest.mark.parametrize("seed,count", [(17, 60)])
+def test_fuzz_grouped_mfma(seed, count):
+    rng = random.Random(seed)
+    done = 0
+    while done < count:
+        g = rng.choice([32, 64])
+        p = Problem("fuzz", rng.randint(1, 3), g, 4 * g, 4 * g, rng.randint(1, 40),
+                    rng.randint(1, 40), rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 3),
+                    rng.randint(1, 3), rng.randint(0, 2), rng.randint(0, 2), rng.randint(1, 2),
+                    rng.randint(1, 2), NHWC, "bf16", "u", "u", 0, 0)
+        if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
+                or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0):
+            continue
+        rows = rng.choice([0, 1, 2, 5, 64])
+        cols = rng.choice([0, 0, 4, 8, 13])
+        try:
+            pl = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols)
+        except cbd.CbdError:
+            continue
+        if pl.info().variant != 3:
+            continue
+        print(f"[fuzz-mfma] i={done} rows={rows} cols={cols} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(4000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(4000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
+        assert run.guards_intact(), (p, rows, cols)
+        done += 1
 
 
 # ------------------------------------------------------------ graph capture ---
