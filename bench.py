@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--no-split", action="store_true",
                     help="time the zero-insertion form (comparison baseline) instead of the "
                          "residue split")
+    ap.add_argument("--grouped-sweep", action="store_true",
+                    help="time the ResNeXt-style grouped sweep (32 shapes), one JSON line each")
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload problem: warm and cold (caches "
                          "flushed) µs/call and the roofline fraction; not the bench line")
@@ -185,6 +187,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.all:
         all_problems(args)
+        return
+    if args.grouped_sweep:
+        grouped_sweep(args)
         return
     p = problem_by_name(args.problem)
     if args.batch:
@@ -268,6 +273,45 @@ def main():
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def grouped_sweep(args):
+    """Each grouped-sweep shape: 10 warm-up calls, then args.steps calls
+    under one event pair; algorithmic bytes per µs against the HBM roofline
+    (every shape has arithmetic intensity far below the bf16 ridge)."""
+    import torch
+
+    import dnn_conv2d_bwd_amd as cbd
+    from cbd_inputs import GROUPED_SWEEP, draw, seed_for
+
+    stream = torch.cuda.current_stream()
+    for p in GROUPED_SWEEP:
+        pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                      (p.dh, p.dw), p.layout, cbd.BF16)
+        info = pl.info()
+        sh = pl.shapes()
+        dy_d = torch.from_numpy(draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)).to(torch.bfloat16).cuda()
+        w_d = torch.from_numpy(draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)).to(torch.bfloat16).cuda()
+        dx_d = torch.empty(sh["dx"], dtype=torch.bfloat16, device="cuda")
+        for _ in range(10):
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.steps
+        nbytes = algorithmic_bytes(p, info)
+        gbs = nbytes / us / 1e3
+        print(json.dumps({
+            "problem": p.name, "workload": describe(p), "kernel": cbd.KERNEL_NAMES[info.kernel],
+            "variant": info.variant, "grid": info.grid_main, "us_warm": round(us, 3),
+            "useful_tflops": round(info.useful_flops / us / 1e6, 3),
+            "alg_mbytes": round(nbytes / 1e6, 3), "gbs": round(gbs, 1),
+            "roofline": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+        del dy_d, w_d, dx_d
 
 
 def all_problems(args):

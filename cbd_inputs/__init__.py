@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .problems import PROBLEMS, Problem, problem_by_name, seed_for  # noqa: F401
+from .problems import GROUPED_SWEEP, PROBLEMS, Problem, problem_by_name, seed_for  # noqa: F401
 
 _GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)

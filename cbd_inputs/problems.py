@@ -93,8 +93,22 @@ PROBLEMS += [
 ]
 
 
+# A ResNeXt-style grouped sweep (32 groups; 4, 8, 16 or 32 channels per
+# group; 56, 28, 14 or 7 pixels square; 3x3, pad 1, stride 1 or 2; bf16
+# NHWC, N=32): a synthetic second workload standing in for the resnext
+# configurations that MIOpen PR #272 asks about without listing them.
+# Config 6, variant = running index (seeds as above).
+GROUPED_SWEEP = []
+for _cg in (4, 8, 16, 32):
+    for _hw in (56, 28, 14, 7):
+        for _s in (1, 2):
+            GROUPED_SWEEP.append(_mk(f"gs-c{_cg}-{_hw}-s{_s}", 6, len(GROUPED_SWEEP), 32, 32,
+                                     32 * _cg, 32 * _cg, _hw, _hw, 3, 3, (_s, _s), (1, 1), NHWC,
+                                     "bf16", "n1", "n0.05"))
+
+
 def problem_by_name(name: str) -> Problem:
-    for p in PROBLEMS:
+    for p in PROBLEMS + GROUPED_SWEEP:
         if p.name == name:
             return p
     raise KeyError(name)

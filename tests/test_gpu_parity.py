@@ -12,6 +12,7 @@ every output against its two-GEMM form (fp64 numpy matmul; that reduction
 is pinned against the oracle in test_oracle_pins.py).
 """
 import random
+import zlib
 
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ import torch
 
 import dnn_conv2d_bwd_amd as cbd
 import oracle
-from cbd_inputs import PROBLEMS, small_ints, uniform
+from cbd_inputs import GROUPED_SWEEP, PROBLEMS, small_ints, uniform
 from cbd_inputs.problems import NCHW, NHWC, Problem
 
 from parity import GpuRun, check, check_bf16, check_f32, exact_expected_bits, operands, \
@@ -322,6 +323,27 @@ def test_fuzz_grouped_mfma(seed, count):
         assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
         assert run.guards_intact(), (p, rows, cols)
         done += 1
+
+
+# The grouped sweep (32 groups x 4..32 channels, 56..7 pixels, stride 1/2),
+# at batch 4, on 3000 sampled outputs of each shape.
+@pytest.mark.parametrize("name", [p.name for p in GROUPED_SWEEP])
+def test_grouped_sweep_sampled(name):
+    p = [q for q in GROUPED_SWEEP if q.name == name][0].with_(n=4)
+    print(f"[sweep] {name} n=4", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p)
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    bits = run.result_bits()  # NHWC
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    cnt = 3000
+    pts = np.stack([rng.integers(0, p.n, cnt), rng.integers(0, p.c, cnt),
+                    rng.integers(0, p.hi, cnt), rng.integers(0, p.wi, cnt)], axis=1)
+    ref = oracle.bwd_data_at(p, dy, w, pts)
+    got = bits[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ok, info = check_bf16(got, ref)
+    assert ok, (name, info)
+    assert run.guards_intact()
 
 
 # ------------------------------------------------------------ graph capture ---
