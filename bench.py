@@ -158,6 +158,11 @@ def main():
     ap.add_argument("--rows-per-wg", type=int, default=0,
                     help="grouped problems: output rows per workgroup of the pipelined row "
                          "kernel (0 automatic, -1 the one-row kernel)")
+    ap.add_argument("--ksplit", type=int, default=0,
+                    help="large-tile kernel: split each tile's K loop over this many workgroups "
+                         "(f32 workspace + finalising kernel)")
+    ap.add_argument("--per-class", action="store_true",
+                    help="one main launch per residue class (ablation of the single launch)")
     ap.add_argument("--cols-per-wg", type=int, default=0,
                     help="grouped MFMA kernel: positions of a row per workgroup (0 automatic)")
     ap.add_argument("--grouped-dot", action="store_true",
@@ -198,7 +203,8 @@ def main():
     pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                   (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
                   no_split=args.no_split, rows_per_wg=args.rows_per_wg,
-                  grouped_dot=args.grouped_dot, cols_per_wg=args.cols_per_wg)
+                  grouped_dot=args.grouped_dot, cols_per_wg=args.cols_per_wg,
+                  ksplit=args.ksplit, per_class=args.per_class)
     info = pl.info()
     sh = pl.shapes()
     dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
@@ -207,13 +213,15 @@ def main():
     dy_d = torch.from_numpy(dy).to(tdt).cuda()
     w_d = torch.from_numpy(w).to(tdt).cuda()
     dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
+    ws = (torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
+          if pl.workspace_size() else None)
     stream = torch.cuda.current_stream()
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib << 20, 5)
 
     for _ in range(args.warmup):
-        cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -222,7 +230,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
+        cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -264,6 +272,7 @@ def main():
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
                    "rows_per_wg": info.rows_per_wg, "cols_per_wg": info.cols_per_wg,
+                   "ksplit": info.ksplit, "launches": info.launches,
                    "useful_gflop": round(flops / 1e9, 4),
                    "executed_gmac": round(info.executed_macs / 1e9, 4),
                    "alg_mbytes": round(alg_bytes / 1e6, 3)},

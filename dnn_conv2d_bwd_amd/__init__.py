@@ -35,8 +35,9 @@ STATUS = {0: "CBD_OK", 1: "CBD_ERR_INVALID_ARG", 2: "CBD_ERR_UNSUPPORTED", 3: "C
           4: "CBD_ERR_NO_MEMORY"}
 
 # Every symbol include/cbd.h declares.
-EXPORTS = ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_plan_destroy", "cbd_status_string",
-           "cbd_last_error", "cbd_plan_info", "cbd_plan_subgemm", "cbd_plan_zero_region")
+EXPORTS = ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_plan_workspace_size",
+           "cbd_plan_destroy", "cbd_status_string", "cbd_last_error", "cbd_plan_info",
+           "cbd_plan_subgemm", "cbd_plan_zero_region")
 
 
 class Problem(ctypes.Structure):
@@ -52,7 +53,8 @@ class Problem(ctypes.Structure):
 class PlanOptions(ctypes.Structure):
     _fields_ = [("force_kernel", ctypes.c_int32), ("no_split", ctypes.c_int32),
                 ("rows_per_wg", ctypes.c_int32), ("grouped_dot", ctypes.c_int32),
-                ("cols_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("cols_per_wg", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("per_class", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -65,6 +67,7 @@ class PlanInfo(ctypes.Structure):
                 ("useful_flops", ctypes.c_int64), ("executed_macs", ctypes.c_int64),
                 ("zero_elems", ctypes.c_int64), ("lds_dynamic", ctypes.c_int64),
                 ("rows_per_wg", ctypes.c_int64), ("cols_per_wg", ctypes.c_int64),
+                ("ksplit", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("variant", ctypes.c_int64)]
 
 
@@ -87,12 +90,14 @@ class ZeroRegion(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m dnn_conv2d_bwd_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python dnn_conv2d_bwd_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     L.cbd_plan.argtypes = [P(Problem), P(ctypes.c_void_p)]
     L.cbd_plan_ex.argtypes = [P(Problem), P(PlanOptions), P(ctypes.c_void_p)]
     L.cbd_run.argtypes = [ctypes.c_void_p] * 5
+    L.cbd_run_ws.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_uint64, ctypes.c_void_p]
+    L.cbd_plan_workspace_size.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64)]
     L.cbd_plan_destroy.argtypes = [ctypes.c_void_p]
     L.cbd_plan_destroy.restype = None
     L.cbd_status_string.argtypes = [ctypes.c_int]
@@ -101,7 +106,8 @@ def _load():
     L.cbd_plan_info.argtypes = [ctypes.c_void_p, P(PlanInfo)]
     L.cbd_plan_subgemm.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(SubGemm)]
     L.cbd_plan_zero_region.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ZeroRegion)]
-    for f in ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_plan_info", "cbd_plan_subgemm",
+    for f in ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_plan_workspace_size",
+              "cbd_plan_info", "cbd_plan_subgemm",
               "cbd_plan_zero_region"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -149,11 +155,12 @@ class Plan:
     """Owns a cbd_plan_t; immutable; safe to run from several streams."""
 
     def __init__(self, problem: Problem, force_kernel: int = KERNEL_AUTO, no_split: bool = False,
-                 rows_per_wg: int = 0, grouped_dot: bool = False, cols_per_wg: int = 0):
+                 rows_per_wg: int = 0, grouped_dot: bool = False, cols_per_wg: int = 0,
+                 ksplit: int = 0, per_class: bool = False):
         self.problem = problem
         h = ctypes.c_void_p()
         opts = PlanOptions(force_kernel, 1 if no_split else 0, rows_per_wg, 1 if grouped_dot else 0,
-                           cols_per_wg)
+                           cols_per_wg, ksplit, 1 if per_class else 0)
         _check(_lib.cbd_plan_ex(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(h)),
                "cbd_plan")
         self._h = h
@@ -161,6 +168,12 @@ class Plan:
     @property
     def handle(self):
         return self._h
+
+    def workspace_size(self) -> int:
+        """Device workspace bytes cbd_run_ws needs (0: none)."""
+        out = ctypes.c_uint64()
+        _check(_lib.cbd_plan_workspace_size(self._h, ctypes.byref(out)), "cbd_plan_workspace_size")
+        return int(out.value)
 
     def info(self) -> PlanInfo:
         out = PlanInfo()
@@ -203,10 +216,12 @@ class Plan:
 
 def plan(n=None, g=1, c=None, k=None, hi=None, wi=None, y=None, x=None, stride=1, pad=0, dil=1,
          layout="nchw", dtype="f32", force_kernel=KERNEL_AUTO, problem=None,
-         no_split=False, rows_per_wg=0, grouped_dot=False, cols_per_wg=0) -> Plan:
+         no_split=False, rows_per_wg=0, grouped_dot=False, cols_per_wg=0, ksplit=0,
+         per_class=False) -> Plan:
     if problem is None:
         problem = make_problem(n, g, c, k, hi, wi, y, x, stride, pad, dil, layout, dtype)
-    return Plan(problem, force_kernel, no_split, rows_per_wg, grouped_dot, cols_per_wg)
+    return Plan(problem, force_kernel, no_split, rows_per_wg, grouped_dot, cols_per_wg, ksplit,
+                per_class)
 
 
 def _torch_dtype(dt):
@@ -226,8 +241,10 @@ def _check_tensor(t, shape, dt, name):
         raise ValueError(f"{name} must be contiguous with shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def run(p: Plan, dy, w, dx, stream=None) -> None:
-    """dx <- conv_bwd_data(dy, w) on `stream` (default: torch's current stream)."""
+def run(p: Plan, dy, w, dx, stream=None, workspace=None) -> None:
+    """dx <- conv_bwd_data(dy, w) on `stream` (default: torch's current stream).
+    workspace: a device tensor of at least p.workspace_size() bytes, for
+    split-K plans (cbd_run_ws); None otherwise."""
     import torch
 
     sh = p.shapes()
@@ -238,8 +255,17 @@ def run(p: Plan, dy, w, dx, stream=None) -> None:
     if stream is None:
         stream = torch.cuda.current_stream(dx.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    _check(_lib.cbd_run(p.handle, ctypes.c_void_p(dy.data_ptr()), ctypes.c_void_p(w.data_ptr()),
-                        ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(handle)), "cbd_run")
+    if workspace is None:
+        _check(_lib.cbd_run(p.handle, ctypes.c_void_p(dy.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                            ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(handle)), "cbd_run")
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        _check(_lib.cbd_run_ws(p.handle, ctypes.c_void_p(dy.data_ptr()),
+                               ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(dx.data_ptr()),
+                               ctypes.c_void_p(workspace.data_ptr()),
+                               ctypes.c_uint64(workspace.numel() * workspace.element_size()),
+                               ctypes.c_void_p(handle)), "cbd_run_ws")
 
 
 def run_raw(p: Plan, dy_ptr: int, w_ptr: int, dx_ptr: int, stream_handle: int = 0) -> int:

@@ -1,6 +1,6 @@
 """Build libcbd.so (planner, C ABI and gfx950 kernels) in-tree with hipcc.
 
-    python -m dnn_conv2d_bwd_amd.build
+    python dnn_conv2d_bwd_amd/build.py
 
 Objects go to _build/ at the repository root; the shared library lands next
 to this file so it travels with the source tree.

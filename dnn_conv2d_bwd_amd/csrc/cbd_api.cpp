@@ -32,11 +32,34 @@ extern "C" const char* cbd_status_string(cbd_status s) {
   return "CBD_ERR_UNKNOWN";
 }
 
-extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
-                              void* stream) {
+namespace {
+
+cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                    void* workspace, uint64_t workspace_bytes, void* stream) {
   if (!plan || !dy || !w || !dx) {
     cbd::set_error("NULL plan or tensor pointer");
     return CBD_ERR_INVALID_ARG;
+  }
+  const uint64_t need = (uint64_t)plan->info.workspace_bytes;
+  if (need > 0) {
+    if (!workspace) {
+      cbd::set_error("the plan splits K and needs a workspace (cbd_run_ws)");
+      return CBD_ERR_INVALID_ARG;
+    }
+    if (workspace_bytes < need) {
+      cbd::set_error("workspace smaller than cbd_plan_workspace_size");
+      return CBD_ERR_INVALID_ARG;
+    }
+    if ((uintptr_t)workspace & 255u) {
+      cbd::set_error("workspace must be 256-byte aligned");
+      return CBD_ERR_UNSUPPORTED;
+    }
+    if (overlap(workspace, need, dx, plan->gemm.dx_bytes) ||
+        overlap(workspace, need, dy, plan->gemm.dy_bytes) ||
+        overlap(workspace, need, w, plan->gemm.w_bytes)) {
+      cbd::set_error("workspace overlaps a tensor");
+      return CBD_ERR_INVALID_ARG;
+    }
   }
   if (((uintptr_t)dy | (uintptr_t)w | (uintptr_t)dx) & 15u) {
     cbd::set_error("tensor pointers must be 16-byte aligned");
@@ -53,20 +76,43 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
     a.dy = dy;
     a.w = w;
     a.dx = dx;
+    a.ws = need > 0 ? workspace : nullptr;
+    auto launch_main = [&](const cbd::GemmArgs& args, int64_t grid) -> int {
+      switch (info.kernel) {
+        case CBD_KERNEL_NHWC_BF16: return cbd::launch_nhwc_bf16(args, grid, stream);
+        case CBD_KERNEL_GROUPED:
+          return args.grp_mfma      ? cbd::launch_grouped_mfma(args, grid, stream)
+                 : args.grp_rows > 0 ? cbd::launch_grouped_pipe(args, plan->prob.dtype, grid, stream)
+                 : args.grp_lds > 0  ? cbd::launch_grouped_rows(args, plan->prob.dtype, grid, stream)
+                                     : cbd::launch_grouped(args, plan->prob.dtype, grid, stream);
+        default: return cbd::launch_generic(args, plan->prob.layout, plan->prob.dtype, grid, stream);
+      }
+    };
     int err = 0;
-    switch (info.kernel) {
-      case CBD_KERNEL_NHWC_BF16: err = cbd::launch_nhwc_bf16(a, info.grid_main, stream); break;
-      case CBD_KERNEL_GROUPED:
-        err = a.grp_mfma      ? cbd::launch_grouped_mfma(a, info.grid_main, stream)
-              : a.grp_rows > 0  ? cbd::launch_grouped_pipe(a, plan->prob.dtype, info.grid_main, stream)
-              : a.grp_lds > 0 ? cbd::launch_grouped_rows(a, plan->prob.dtype, info.grid_main, stream)
-                              : cbd::launch_grouped(a, plan->prob.dtype, info.grid_main, stream);
-        break;
-      default: err = cbd::launch_generic(a, plan->prob.layout, plan->prob.dtype, info.grid_main, stream); break;
+    if (plan->per_class) {
+      // One launch per class (an ablation of the single launch): the class
+      // alone in the descriptor table, its tiles numbered from 0.
+      for (size_t i = 0; i < plan->subs.size() && !err; i++) {
+        cbd::GemmArgs c = a;
+        c.sub[0] = a.sub[i];
+        c.sub[0].tile_begin = 0;
+        c.num_sub = 1;
+        c.total_tiles = (int32_t)plan->subs[i].tiles;
+        err = launch_main(c, plan->subs[i].tiles);
+      }
+    } else {
+      err = launch_main(a, info.grid_main);
     }
     if (err) {
       cbd::set_error(std::string("main kernel launch failed: ") + cbd::hip_error_name(err));
       return CBD_ERR_HIP;
+    }
+    if (a.ksplit > 1) {
+      const int ferr = cbd::launch_splitk_finalize(a, plan->grid_finalize, stream);
+      if (ferr) {
+        cbd::set_error(std::string("split-K finalising launch failed: ") + cbd::hip_error_name(ferr));
+        return CBD_ERR_HIP;
+      }
     }
   }
   if (info.grid_zero > 0) {
@@ -79,5 +125,26 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
     }
   }
   cbd::set_error("");
+  return CBD_OK;
+}
+
+}  // namespace
+
+extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                              void* stream) {
+  return run_impl(plan, dy, w, dx, nullptr, 0, stream);
+}
+
+extern "C" cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                                 void* workspace, uint64_t workspace_bytes, void* stream) {
+  return run_impl(plan, dy, w, dx, workspace, workspace_bytes, stream);
+}
+
+extern "C" cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* bytes) {
+  if (!plan || !bytes) {
+    cbd::set_error("NULL plan or output");
+    return CBD_ERR_INVALID_ARG;
+  }
+  *bytes = (uint64_t)plan->info.workspace_bytes;
   return CBD_OK;
 }

@@ -13,6 +13,8 @@ struct cbd_plan_s {
   std::vector<cbd_zero_region_t> zeros;
   cbd::GemmArgs gemm;                    // pointers filled per run
   cbd::ZeroArgs zero;
+  int64_t grid_finalize = 0;             // split-K finalising launch (0: none)
+  bool per_class = false;                // one main launch per class (ablation)
 };
 
 namespace cbd {
@@ -23,6 +25,7 @@ void set_error(const std::string& msg);
 // Launchers (defined next to their kernels).  Each returns 0 or a hipError_t.
 int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream);
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream);
+int launch_splitk_finalize(const GemmArgs& a, int64_t grid, void* stream);
 int launch_grouped(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_pipe(const GemmArgs& a, int dtype, int64_t grid, void* stream);

@@ -103,9 +103,16 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int32_t rows_opt = 0;
   bool grouped_dot = false;
   int32_t cols_opt = 0;
+  int32_t ksplit_opt = 0;
+  bool per_class = false;
   if (options) {
-    for (int i = 0; i < 3; i++)
-      if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->reserved[0]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->per_class != 0 && options->per_class != 1)
+      return fail(CBD_ERR_INVALID_ARG, "options.per_class must be 0 or 1");
+    per_class = options->per_class == 1;
+    if (options->ksplit < 0 || options->ksplit > 64)
+      return fail(CBD_ERR_INVALID_ARG, "options.ksplit must be 0..64");
+    ksplit_opt = options->ksplit;
     if (options->cols_per_wg < 0 || options->cols_per_wg > (1 << 20))
       return fail(CBD_ERR_INVALID_ARG, "options.cols_per_wg must be 0 or a position count");
     cols_opt = options->cols_per_wg;
@@ -336,6 +343,23 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     }
   }
 
+  // Split-K (large-tile kernel only): S workgroups per tile, each at least
+  // one k tile of every class.
+  int64_t ksplit = 1;
+  if (ksplit_opt >= 2) {
+    if (kernel != CBD_KERNEL_NHWC_BF16) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "ksplit needs the NHWC bf16 (large-tile) kernel");
+    }
+    if (per_class) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "ksplit and per_class do not combine");
+    }
+    ksplit = ksplit_opt;
+    for (const auto& s : subs) ksplit = std::min<int64_t>(ksplit, s.k / cbd::kFastBK);
+    ksplit = std::max<int64_t>(ksplit, 1);
+  }
+
   // Tiles per class (contiguous ranges of the logical grid, in LPT order).
   int64_t tile = 0;
   int64_t tiles_m = kernel == CBD_KERNEL_GROUPED ? 1 : ceil_div(Cg, bm);
@@ -351,7 +375,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
                 : grp_lds > 0 ? p.n * s.pos_h
                               : ceil_div(s.n, slots * iters);
     else
-      s.tiles = p.g * tiles_m * ceil_div(s.n, bn);
+      s.tiles = p.g * tiles_m * ceil_div(s.n, bn) * ksplit;
     tile += s.tiles;
     if (s.k != subs[0].k) equal_k = false;
     exec += p.g * s.m * s.n * s.k;
@@ -410,6 +434,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_rows = (int32_t)grp_rows;
   a.grp_mfma = grp_mfma ? 1 : 0;
   a.grp_cols = (int32_t)grp_cols;
+  a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
+  a.ws = nullptr;
+  pl->grid_finalize = ksplit > 1 ? tile / ksplit * (cbd::kFastBN / 8) : 0;
   for (size_t i = 0; i < subs.size(); i++) {
     cbd::SubDesc& d = a.sub[i];
     const cbd_subgemm_t& s = subs[i];
@@ -450,7 +477,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int64_t grid_zero = ceil_div(items, cbd::kZeroThreads);
   int64_t grid_main = tile;
   std::memset(&a.fz, 0, sizeof(a.fz));
-  if (kernel == CBD_KERNEL_GENERIC && items > 0 && (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
+  if (kernel == CBD_KERNEL_GENERIC && !per_class && items > 0 &&
+      (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
       cbd::kZeroThreads == cbd::kGenericThreads &&
       (tile + grid_zero) * cbd::kGenericThreads < (int64_t(1) << 32)) {
     cbd::FusedZero& f = a.fz;
@@ -475,13 +503,17 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.threads_main = (int32_t)threads;
   info.grid_main = grid_main;
   info.grid_zero = grid_zero;
-  info.launches = (grid_main > 0 ? 1 : 0) + (grid_zero > 0 ? 1 : 0);
+  info.launches = (grid_main > 0 ? (per_class ? (int32_t)subs.size() : 1) : 0) + (grid_zero > 0 ? 1 : 0) +
+                  (ksplit > 1 ? 1 : 0);
+  pl->per_class = per_class;
   info.useful_flops = 2 * p.n * p.c * Kg * Ho * Wo * p.y * p.x;
   info.executed_macs = exec;
   info.zero_elems = zero_elems;
   info.lds_dynamic = grp_lds;
   info.rows_per_wg = grp_rows;
   info.cols_per_wg = grp_cols;
+  info.ksplit = ksplit;
+  info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
   info.variant = kernel != CBD_KERNEL_GROUPED ? 0 : grp_mfma ? 3 : grp_rows > 0 ? 2 : grp_lds > 0 ? 1 : 0;
 
   pl->subs = std::move(subs);

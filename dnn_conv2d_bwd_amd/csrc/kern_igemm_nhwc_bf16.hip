@@ -47,6 +47,7 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -76,6 +77,10 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) <
 __device__ inline int swz_w(int row) { return 4 * (row & 3); }  // W rows: 32 chunks
 __device__ inline int swz_y(int row) { return (row >> 2) & 3; }  // dY rows: 4 chunks
 
+// SPLIT: the K loop of each tile is split over a.ksplit workgroups that
+// write f32 partial tiles (a separate instance, so that the plain kernel
+// carries none of its registers).
+template <bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmArgs a) {
   // Stages as distinct objects: the compiler can then see that fragment reads
   // of one stage do not alias the loads in flight into another.
@@ -96,7 +101,12 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int npos = a.N * npix_img;
   const int tiles_n = (npos + BN - 1) / BN;
   const int per_group = a.tiles_m * tiles_n;
-  const int local = t - s.tile_begin;
+  // With the K loop split over S workgroups (S = a.ksplit > 1), the S
+  // workgroups of a tile are consecutive: split = t mod S (class ranges
+  // start at multiples of S).
+  const int S = SPLIT ? a.ksplit : 1;
+  const int split = (t - s.tile_begin) % S;
+  const int local = (t - s.tile_begin) / S;
   const int g = local / per_group;
   const int rem = local - g * per_group;
   const int m0 = (rem % a.tiles_m) * BM;
@@ -115,7 +125,12 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int YX = __builtin_amdgcn_readfirstlane(a.Y * a.X);
   const uint32_t wrow = __builtin_amdgcn_readfirstlane((uint32_t)(YX * a.Cg) * 2u);  // bytes between k rows of W
   const int kpt = __builtin_amdgcn_readfirstlane(a.Kg / BK);
-  const int KT = __builtin_amdgcn_readfirstlane(ntaps * kpt);
+  // This workgroup's k tiles: [kb, ke) of the class's ntaps * kpt (tile t =
+  // tap t / kpt, k rows 32 (t mod kpt) ...); the planner keeps S <= ntaps*kpt.
+  const int KTall = __builtin_amdgcn_readfirstlane(ntaps * kpt);
+  const int kb = __builtin_amdgcn_readfirstlane(split * KTall / S);
+  const int ke = __builtin_amdgcn_readfirstlane((split + 1) * KTall / S);
+  const int KT = ke - kb;  // k tiles of this workgroup
   const uint32_t kpt_magic = __builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)kpt + 1u);
 
   // ---- per-workgroup tables (threads 0..255: one position row each)
@@ -167,16 +182,19 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // Tiles past the end load with an out-of-range scalar offset (zeros into
   // a stage that is no longer read), which keeps the count of loads in
   // flight the same on every tile.
+  const uint32_t a_step = (uint32_t)BK * wrow, b_step = (uint32_t)BK * 2u;
+  // First tile kb: tap kb / kpt, k tile kb mod kpt within it.
+  const int tap0 = __builtin_amdgcn_readfirstlane(kb / kpt);
+  const uint32_t r0 = (uint32_t)(kb - tap0 * kpt);
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    a_off[i] = a_lane[i] + atab[0];
-    b_off[i] = gtab[b_row[i]] + b_chunk[i];
+    a_off[i] = a_lane[i] + atab[tap0] + r0 * a_step;
+    b_off[i] = gtab[tap0 * BN + b_row[i]] + b_chunk[i] + r0 * b_step;
   }
-  const uint32_t a_step = (uint32_t)BK * wrow, b_step = (uint32_t)BK * 2u;
   // Tile t = (tap, k tile) with tap = t / kpt, by multiply-high with a
   // rounded-up reciprocal (exact for t < 17 kpt, kpt <= 4096: tiles per
-  // class are at most 16 kpt, plus the 4 zero-fill tiles).
+  // class are at most 16 kpt, plus the 4 tiles loaded past the end).
   auto tap_of = [&](int t) -> int { return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic); };
   uint32_t a_soff = 0, b_soff = 0;
   // Move a set of offsets from tile t-1 to tile t: one add per lane offset,
@@ -184,7 +202,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // Offsets of tiles past the end are never used to read live data.
   auto advance_a = [&](int t) {
     const int tap = tap_of(t);
-    if (t - tap * kpt == 0 && t < KT) {
+    if (t - tap * kpt == 0 && t < ke) {
       const uint32_t base = atab[tap];
 #pragma unroll
       for (int i = 0; i < 4; i++) a_off[i] = a_lane[i] + base;
@@ -192,18 +210,18 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
 #pragma unroll
       for (int i = 0; i < 4; i++) a_off[i] += a_step;
     }
-    a_soff = t < KT ? 0u : dev::kOOB;
+    a_soff = t < ke ? 0u : dev::kOOB;
   };
   auto advance_b = [&](int t) {
     const int tap = tap_of(t);
-    if (t - tap * kpt == 0 && t < KT) {
+    if (t - tap * kpt == 0 && t < ke) {
 #pragma unroll
       for (int i = 0; i < 4; i++) b_off[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 4; i++) b_off[i] += b_step;
     }
-    b_soff = t < KT ? 0u : dev::kOOB;
+    b_soff = t < ke ? 0u : dev::kOOB;
   };
   // Load j of a tile (j < 4: W, else dY): 64 lanes x 16 bytes, global ->
   // LDS without VGPRs (buffer_load ... lds; lane l writes 16 bytes at
@@ -325,16 +343,16 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // the W loads of tile 3.
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 0>(), j);
-  advance_a(1);
-  advance_b(1);
+  advance_a(kb + 1);
+  advance_b(kb + 1);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 1>(), j);
-  advance_a(2);
-  advance_b(2);
+  advance_a(kb + 2);
+  advance_b(kb + 2);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE; j++) issue_one(std::integral_constant<int, 2>(), j);
-  advance_a(3);
-  advance_b(3);
+  advance_a(kb + 3);
+  advance_b(kb + 3);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE / 2; j++) issue_one(std::integral_constant<int, 3>(), j);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * DMA_PER_TILE + DMA_PER_TILE / 2));
@@ -345,11 +363,11 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   auto iter = [&](int kt, auto stc) {
     constexpr int ST = decltype(stc)::value;
     half(fa0, fb0, stc, 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(),
-         DMA_PER_TILE / 2, [&]() { advance_a(kt + NSTAGE); });
+         DMA_PER_TILE / 2, [&]() { advance_a(kb + kt + NSTAGE); });
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE));
     __builtin_amdgcn_s_barrier();
     half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0,
-         [&]() { advance_b(kt + NSTAGE); });
+         [&]() { advance_b(kb + kt + NSTAGE); });
   };
   for (int kt = 0; kt < KT; kt += NSTAGE) {
     iter(kt, std::integral_constant<int, 0>());
@@ -361,6 +379,46 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // The loads past the last tile (zeros into free stages) must land before
   // the stages are reused for the C tile.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  if constexpr (SPLIT) {
+    // ---- split-K epilogue: the f32 partial tile goes to the workspace,
+    // block t (256 KiB, [position row][256 channels]), for the finalising
+    // kernel to sum.  Through LDS in two halves of 128 rows (the waves of
+    // one position half at a time), 16-byte chunk q of row r stored at
+    // chunk q ^ (r & 31); then 1 KiB rows out with 16-byte stores.
+    char* const ws = (char*)a.ws + (size_t)t * (BM * BN * 4);
+    const auto rws = dev::rsrc(ws, BM * BN * 4);
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      __syncthreads();
+      if (wn == h) {
+#pragma unroll
+        for (int bn = 0; bn < 4; bn++) {
+          const int prow = bn * 32 + (lane & 31);  // row within the half
+          char* rowp = smem + prow * 1024;
+#pragma unroll
+          for (int bm = 0; bm < 4; bm++) {
+#pragma unroll
+            for (int qq = 0; qq < 4; qq++) {
+              const int c = wm * 128 + bm * 32 + 8 * qq + 4 * (lane >> 5);
+              const f32x4 v = {acc[bm][bn][4 * qq + 0], acc[bm][bn][4 * qq + 1],
+                               acc[bm][bn][4 * qq + 2], acc[bm][bn][4 * qq + 3]};
+              *(f32x4*)(rowp + (((c >> 2) ^ (prow & 31)) << 4)) = v;
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int it = 0; it < 128 * 64 / THREADS; it++) {
+        const int row = it * (THREADS / 64) + (tid >> 6), q = tid & 63;
+        const u32x4 v = *(const u32x4*)(smem + row * 1024 + ((q ^ (row & 31)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(u4{v[0], v[1], v[2], v[3]}, rws,
+                                               (uint32_t)((h * 128 + row) * 1024 + q * 16), 0, 0);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue.  C tile [position row][256 channels] bf16 = 128 KiB over
   // the four stages (64 rows each), 16-byte chunk c/8 of row r stored at
   // chunk (c/8) ^ (r & 31).
@@ -397,12 +455,64 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   }
 }
 
+// Finalising kernel of a split-K launch: dX = bf16(sum of the S partial
+// tiles in the workspace, in split order).  Workgroup = 8 position rows of
+// one tile; thread = 8 channels (two 16-byte loads per partial, one 16-byte
+// store).
+__global__ __launch_bounds__(256) void splitk_finalize_kernel(const GemmArgs a) {
+  const int S = a.ksplit;
+  const int T = blockIdx.x / (BN / 8);  // tile (its workgroups in the main launch: T*S ...)
+  const int row = (blockIdx.x % (BN / 8)) * 8 + (threadIdx.x >> 5);
+  const int q = threadIdx.x & 31;
+  const int t0 = T * S;
+  const SubDesc s = a.sub[dev::find_class(a, t0)];
+  const int npix_img = s.pos_h * s.pos_w;
+  const int npos = a.N * npix_img;
+  const int tiles_n = (npos + BN - 1) / BN;
+  const int per_group = a.tiles_m * tiles_n;
+  const int local = (t0 - s.tile_begin) / S;
+  const int g = local / per_group;
+  const int rem = local - g * per_group;
+  const int m0 = (rem % a.tiles_m) * BM;
+  const int n0 = (rem / a.tiles_m) * BN;
+  const int p = n0 + row;
+  const int c = m0 + 8 * q;
+  if (p >= npos || c >= a.Cg) return;
+
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const char* blk = (const char*)a.ws + (size_t)t0 * (BM * BN * 4) + row * 1024 + q * 32;
+  for (int sp = 0; sp < S; sp++) {
+    const f32x4 lo = *(const f32x4*)(blk + (size_t)sp * (BM * BN * 4));
+    const f32x4 hi = *(const f32x4*)(blk + (size_t)sp * (BM * BN * 4) + 16);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[i] += lo[i];
+      v[4 + i] += hi[i];
+    }
+  }
+  const int n = p / npix_img;
+  const int rr = p - n * npix_img;
+  const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
+  const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
+  const uint32_t off = (uint32_t)(((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg + c) * 2u;
+  const u4 o = {dev::bf16_pack2(v[0], v[1]), dev::bf16_pack2(v[2], v[3]), dev::bf16_pack2(v[4], v[5]),
+                dev::bf16_pack2(v[6], v[7])};
+  __builtin_amdgcn_raw_buffer_store_b128(o, dev::rsrc(a.dx, a.dx_bytes), off, 0, 0);
+}
+
 }  // namespace
+
+int launch_splitk_finalize(const GemmArgs& a, int64_t grid, void* stream) {
+  void* args[] = {const_cast<GemmArgs*>(&a)};
+  return (int)hipLaunchKernel((const void*)&splitk_finalize_kernel, dim3((unsigned)grid), dim3(256),
+                              args, 0, (hipStream_t)stream);
+}
 
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&igemm_nhwc_bf16_kernel, dim3((unsigned)grid),
-                              dim3(THREADS), args, 0, (hipStream_t)stream);
+  const void* k = a.ksplit > 1 ? (const void*)&igemm_nhwc_bf16_kernel<true>
+                               : (const void*)&igemm_nhwc_bf16_kernel<false>;
+  return (int)hipLaunchKernel(k, dim3((unsigned)grid), dim3(THREADS), args, 0, (hipStream_t)stream);
 }
 
 }  // namespace cbd

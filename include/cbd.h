@@ -111,7 +111,18 @@ typedef struct {
   int32_t cols_per_wg;  /* grouped family, MFMA pipelined kernel: positions of a
                            row per workgroup, rounded up to a multiple of 4
                            (0: the planner's choice) */
-  int32_t reserved[3];  /* must be zero */
+  int32_t ksplit;       /* large-tile (NHWC bf16) kernel: split each tile's K
+                           loop over this many workgroups (0 or 1: no split;
+                           at most 64; clamped to the k tiles of the
+                           shortest class).  Partial tiles go to a caller
+                           workspace as f32 and a second kernel sums them
+                           in split order and writes dX: such a plan runs
+                           only through cbd_run_ws.  For grids too small to
+                           fill the GPU (e.g. one GPU's batch shard). */
+  int32_t per_class;    /* 1: one main launch per residue class instead of one
+                           for all (an ablation of the single launch; not
+                           with ksplit); 0 or 1 */
+  int32_t reserved[1];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
@@ -137,6 +148,22 @@ cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* optio
 cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                    void* stream);
 
+/* As cbd_run, for plans that need a workspace (cbd_plan_workspace_size > 0,
+ * i.e. options.ksplit >= 2; plans that need none accept any workspace,
+ * including NULL).  workspace is a DEVICE buffer of at least that many bytes,
+ * 256-byte aligned, owned by the caller, not overlapping dy, w or dx; its
+ * contents are scratch (no initialisation needed, overwritten).  The plan's
+ * calls on one stream may share a workspace; concurrent calls on different
+ * streams need one each.  Errors: as cbd_run, plus INVALID_ARG for a missing,
+ * small or overlapping workspace and UNSUPPORTED for a misaligned one. */
+cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                      void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace cbd_run_ws needs for this plan (0: none; then
+ * cbd_run suffices, and cbd_run on a plan that needs one fails with
+ * INVALID_ARG). */
+cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* bytes);
+
 /* Free a plan.  NULL is allowed. */
 void cbd_plan_destroy(cbd_plan_t* plan);
 
@@ -155,7 +182,7 @@ typedef struct {
   int32_t kernel;           /* cbd_kernel of the main launch */
   int32_t tile_m, tile_n, tile_k;
   int32_t threads_main;     /* workgroup size of the main launch */
-  int32_t launches;         /* kernels per cbd_run (1 or 2) */
+  int32_t launches;         /* kernels per cbd_run (1 to 3) */
   int64_t grid_main;        /* workgroups of the main launch (generic family:
                                includes the zero-fill workgroups folded into it) */
   int64_t grid_zero;        /* workgroups of a separate zero-fill launch (0 if
@@ -170,6 +197,8 @@ typedef struct {
                                pipelined row kernels (0: another kernel) */
   int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernel: positions
                                per column block of a row (0: other kernels) */
+  int64_t ksplit;           /* workgroups per tile of a split-K plan (1: none) */
+  int64_t workspace_bytes;  /* device workspace cbd_run_ws needs (0: none) */
   int64_t variant;          /* kernel within the family; grouped: 0 direct,
                                1 one row per workgroup, 2 pipelined rows on
                                dot-product instructions, 3 pipelined rows on

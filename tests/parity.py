@@ -36,11 +36,13 @@ def operands(p, kind="dist"):
     return dy, w
 
 
-def plan_for(p, force=cbd.KERNEL_AUTO, rows_per_wg=0, grouped_dot=False, cols_per_wg=0):
+def plan_for(p, force=cbd.KERNEL_AUTO, rows_per_wg=0, grouped_dot=False, cols_per_wg=0, ksplit=0,
+             per_class=False):
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     return cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                     (p.dh, p.dw), p.layout, dt, force_kernel=force, rows_per_wg=rows_per_wg,
-                    grouped_dot=grouped_dot, cols_per_wg=cols_per_wg)
+                    grouped_dot=grouped_dot, cols_per_wg=cols_per_wg, ksplit=ksplit,
+                    per_class=per_class)
 
 
 def torch_dtype(p):
@@ -54,8 +56,9 @@ def to_device(a, p):
 class GpuRun:
     """Allocates a sentinel-filled dX with guard bands and runs a plan."""
 
-    def __init__(self, p, pl, dy_d, w_d):
+    def __init__(self, p, pl, dy_d, w_d, workspace=None):
         self.p, self.pl = p, pl
+        self.ws = workspace
         self.shape = pl.shapes()["dx"]
         self.numel = int(np.prod(self.shape))
         self.buf = torch.full((self.numel + 2 * GUARD,), float("nan"), dtype=torch_dtype(p),
@@ -64,7 +67,7 @@ class GpuRun:
         self.dy_d, self.w_d = dy_d, w_d
 
     def __call__(self, stream=None):
-        cbd.run(self.pl, self.dy_d, self.w_d, self.dx, stream=stream)
+        cbd.run(self.pl, self.dy_d, self.w_d, self.dx, stream=stream, workspace=self.ws)
         return self
 
     def result_f32(self):

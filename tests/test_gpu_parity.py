@@ -142,6 +142,80 @@ def test_c4_full_size():
     assert np.array_equal(bits1, run.result_bits().reshape(bits1.shape))
 
 
+@pytest.mark.parametrize("ksplit", [2, 3, 8])
+def test_c4_ksplit(ksplit):
+    """Split-K on the headline problem: every output against the fp64
+    two-GEMM form, and equal to itself on a second call."""
+    p = by_name("c4")
+    print(f"[ksplit] c4 ksplit={ksplit}", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p, ksplit=ksplit)
+    assert pl.info().ksplit == ksplit
+    ws = torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+    bits = run.result_bits().reshape(p.n, p.hi, p.wi, p.c)
+    assert run.guards_intact()
+    ref = np.empty((p.n, 1, p.wi, p.c), dtype=np.float64)
+    dy2 = dy[:, 0].reshape(-1, p.k).astype(np.float64)
+    for r in range(2):
+        ref[:, 0, r::2, :] = (dy2 @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
+    ok, info = check_bf16(bits, ref)
+    print("[ksplit] c4", info, flush=True)
+    assert ok, info
+    bits1 = bits.copy()
+    run()
+    assert np.array_equal(bits1, run.result_bits().reshape(bits1.shape))
+
+
+@pytest.mark.parametrize("n,ksplit", [(2, 8), (1, 16), (4, 4)])
+def test_c4_shard_ksplit_integer_exact(n, ksplit):
+    """One GPU's batch shard of the headline problem with split-K, on
+    integer-valued operands: bit-exact against the oracle."""
+    p = by_name("c4").with_(n=n)
+    print(f"[ksplit] c4 n={n} ksplit={ksplit}", flush=True)
+    dy, w = operands(p, "int")
+    pl = plan_for(p, ksplit=ksplit)
+    ws = torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
+    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+    got = run.result_f32()
+    assert np.array_equal(got, want.reshape(got.shape))
+    assert run.guards_intact()
+
+
+@pytest.mark.parametrize("seed,count", [(19, 40)])
+def test_fuzz_ksplit_integer_exact(seed, count):
+    rng = random.Random(seed + 7)
+    for i, p in enumerate(fuzz_problems(seed, count, family=cbd.KERNEL_NHWC_BF16)):
+        ksplit = rng.choice([2, 3, 5, 16])
+        pl = plan_for(p, cbd.KERNEL_NHWC_BF16, ksplit=ksplit)
+        print(f"[fuzz-ksplit] i={i} ksplit={ksplit}->{pl.info().ksplit} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(5000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(5000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
+        ws = torch.empty(max(pl.workspace_size(), 1), dtype=torch.uint8, device="cuda")
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+        want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), (p, ksplit)
+        assert run.guards_intact(), (p, ksplit)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3a", "c3b", "c4", "c5-s2", "c2-14-3"])
+def test_per_class_launches_match_single_launch(name):
+    """One launch per residue class gives the same bits as the single launch."""
+    p = by_name(name)
+    print(f"[per-class] {name}", flush=True)
+    dy, w = operands(p)
+    dy_d, w_d = to_device(dy, p), to_device(w, p)
+    one = GpuRun(p, plan_for(p), dy_d, w_d)()
+    pl = plan_for(p, per_class=True)
+    assert pl.info().launches >= pl.info().num_subgemms
+    many = GpuRun(p, pl, dy_d, w_d)()
+    assert np.array_equal(one.result_bits(), many.result_bits())
+    assert many.guards_intact()
+
+
 def test_non_default_stream():
     p = by_name("c3a")
     dy, w = operands(p)

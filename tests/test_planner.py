@@ -248,6 +248,49 @@ def test_exports_and_null_handling():
     assert cbd.run_raw(pl, base, base + (1 << 28), base + 64) == 1           # dx overlaps dy
 
 
+def test_ksplit_plans():
+    """Split-K accounting: S workgroups per tile (clamped to the shortest
+    class's k tiles), a 256x256 f32 workspace block per workgroup, one more
+    launch, cbd_run refusing such a plan before any HIP call."""
+    c4 = [p for p in PROBLEMS if p.name == "c4"][0]
+    base = cbd.plan(problem=cbd.make_problem(c4.n, c4.g, c4.c, c4.k, c4.hi, c4.wi, c4.y, c4.x,
+                                             (c4.sh, c4.sw), (c4.ph, c4.pw), (c4.dh, c4.dw),
+                                             c4.layout, cbd.BF16))
+    b = base.info()
+    assert b.ksplit == 1 and b.workspace_bytes == 0 and base.workspace_size() == 0
+    for s in (2, 3, 8, 64):
+        pl = cbd.plan(c4.n, c4.g, c4.c, c4.k, c4.hi, c4.wi, c4.y, c4.x, (c4.sh, c4.sw),
+                      (c4.ph, c4.pw), (c4.dh, c4.dw), c4.layout, cbd.BF16, ksplit=s)
+        i = pl.info()
+        # c4: K/G = 2048 and one tap per class: 64 k tiles, so 64 splits at most
+        assert i.ksplit == min(s, 64)
+        assert i.grid_main == b.grid_main * i.ksplit
+        assert i.workspace_bytes == i.grid_main * 256 * 256 * 4 == pl.workspace_size()
+        assert i.launches == b.launches + 1
+        assert i.executed_macs == b.executed_macs
+        for sg in pl.subgemms():
+            assert sg.tiles % i.ksplit == 0 and sg.tile_begin % i.ksplit == 0
+        big = 1 << 40
+        assert cbd.run_raw(pl, big, big + (1 << 30), big + (1 << 31)) == 1  # no workspace
+        ws = big + (1 << 33)
+        L = cbd._lib
+        P = ctypes.c_void_p
+        assert L.cbd_run_ws(pl.handle, P(big), P(big + (1 << 30)), P(big + (1 << 31)), P(ws),
+                            ctypes.c_uint64(i.workspace_bytes - 1), P(0)) == 1  # too small
+        assert L.cbd_run_ws(pl.handle, P(big), P(big + (1 << 30)), P(big + (1 << 31)), P(ws + 16),
+                            ctypes.c_uint64(i.workspace_bytes), P(0)) == 2      # misaligned
+        assert L.cbd_run_ws(pl.handle, P(big), P(big + (1 << 30)), P(big + (1 << 31)), P(big),
+                            ctypes.c_uint64(i.workspace_bytes), P(0)) == 1      # overlaps dy
+    # a short class clamps S: 3x3 stride 2 has a one-tap class (K/G = 64: 2 k tiles)
+    pl = cbd.plan(2, 1, 256, 64, 9, 9, 3, 3, 2, 1, 1, "nhwc", "bf16", ksplit=8)
+    assert pl.info().kernel == cbd.KERNEL_NHWC_BF16 and pl.info().ksplit == 2
+    # other kernel families refuse it
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=2)
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=65)
+
+
 def test_run_without_device_returns_hip_error():
     """On a machine with no GPU, cbd_run reports CBD_ERR_HIP instead of
     aborting (run in a child process to keep this one clean)."""
