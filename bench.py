@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--ksplit", type=int, default=0,
                     help="large-tile kernel: split each tile's K loop over this many workgroups "
                          "(f32 workspace + finalising kernel)")
+    ap.add_argument("--static-shape", type=int, default=0, choices=(-1, 0, 1),
+                    help="large-tile kernel: shape-specialised instance when one matches (0), "
+                         "required (1) or never, i.e. the descriptor-driven kernel (-1)")
     ap.add_argument("--per-class", action="store_true",
                     help="one main launch per residue class (ablation of the single launch)")
     ap.add_argument("--cols-per-wg", type=int, default=0,
@@ -204,7 +207,8 @@ def main():
                   (p.dh, p.dw), p.layout, dt, force_kernel=args.force_kernel,
                   no_split=args.no_split, rows_per_wg=args.rows_per_wg,
                   grouped_dot=args.grouped_dot, cols_per_wg=args.cols_per_wg,
-                  ksplit=args.ksplit, per_class=args.per_class)
+                  ksplit=args.ksplit, per_class=args.per_class,
+                  static_shape=args.static_shape)
     info = pl.info()
     sh = pl.shapes()
     dy = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
@@ -273,6 +277,7 @@ def main():
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
                    "rows_per_wg": info.rows_per_wg, "cols_per_wg": info.cols_per_wg,
                    "ksplit": info.ksplit, "launches": info.launches,
+                   "static_shape": info.static_shape,
                    "useful_gflop": round(flops / 1e9, 4),
                    "executed_gmac": round(info.executed_macs / 1e9, 4),
                    "alg_mbytes": round(alg_bytes / 1e6, 3)},

@@ -54,7 +54,8 @@ class PlanOptions(ctypes.Structure):
     _fields_ = [("force_kernel", ctypes.c_int32), ("no_split", ctypes.c_int32),
                 ("rows_per_wg", ctypes.c_int32), ("grouped_dot", ctypes.c_int32),
                 ("cols_per_wg", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("per_class", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("per_class", ctypes.c_int32), ("static_shape", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -67,7 +68,8 @@ class PlanInfo(ctypes.Structure):
                 ("useful_flops", ctypes.c_int64), ("executed_macs", ctypes.c_int64),
                 ("zero_elems", ctypes.c_int64), ("lds_dynamic", ctypes.c_int64),
                 ("rows_per_wg", ctypes.c_int64), ("cols_per_wg", ctypes.c_int64),
-                ("ksplit", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("ksplit", ctypes.c_int64), ("static_shape", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64),
                 ("variant", ctypes.c_int64)]
 
 
@@ -156,11 +158,11 @@ class Plan:
 
     def __init__(self, problem: Problem, force_kernel: int = KERNEL_AUTO, no_split: bool = False,
                  rows_per_wg: int = 0, grouped_dot: bool = False, cols_per_wg: int = 0,
-                 ksplit: int = 0, per_class: bool = False):
+                 ksplit: int = 0, per_class: bool = False, static_shape: int = 0):
         self.problem = problem
         h = ctypes.c_void_p()
         opts = PlanOptions(force_kernel, 1 if no_split else 0, rows_per_wg, 1 if grouped_dot else 0,
-                           cols_per_wg, ksplit, 1 if per_class else 0)
+                           cols_per_wg, ksplit, 1 if per_class else 0, int(static_shape))
         _check(_lib.cbd_plan_ex(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(h)),
                "cbd_plan")
         self._h = h
@@ -217,11 +219,11 @@ class Plan:
 def plan(n=None, g=1, c=None, k=None, hi=None, wi=None, y=None, x=None, stride=1, pad=0, dil=1,
          layout="nchw", dtype="f32", force_kernel=KERNEL_AUTO, problem=None,
          no_split=False, rows_per_wg=0, grouped_dot=False, cols_per_wg=0, ksplit=0,
-         per_class=False) -> Plan:
+         per_class=False, static_shape=0) -> Plan:
     if problem is None:
         problem = make_problem(n, g, c, k, hi, wi, y, x, stride, pad, dil, layout, dtype)
     return Plan(problem, force_kernel, no_split, rows_per_wg, grouped_dot, cols_per_wg, ksplit,
-                per_class)
+                per_class, static_shape)
 
 
 def _torch_dtype(dt):

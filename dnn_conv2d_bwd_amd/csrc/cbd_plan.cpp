@@ -105,8 +105,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int32_t cols_opt = 0;
   int32_t ksplit_opt = 0;
   bool per_class = false;
+  int32_t static_mode = 0;
   if (options) {
-    if (options->reserved[0]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    for (int i = 0; i < 4; i++)
+      if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->static_shape < -1 || options->static_shape > 1)
+      return fail(CBD_ERR_INVALID_ARG, "options.static_shape must be -1, 0 or 1");
+    static_mode = options->static_shape;
     if (options->per_class != 0 && options->per_class != 1)
       return fail(CBD_ERR_INVALID_ARG, "options.per_class must be 0 or 1");
     per_class = options->per_class == 1;
@@ -360,6 +365,23 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     ksplit = std::max<int64_t>(ksplit, 1);
   }
 
+  // Shape-specialised instance (compile-time k tiles per tap and taps per
+  // class): only the one for K/G = 2048 with one tap per class is built.  It
+  // computes the same bits as the descriptor-driven kernel and is used
+  // whenever it matches, unless the caller asks for the latter.
+  bool static_shape = false;
+  {
+    bool ok = kernel == CBD_KERNEL_NHWC_BF16 && ksplit == 1 && Kg == 64 * cbd::kFastBK &&
+              !subs.empty();
+    for (const auto& s : subs) ok = ok && s.taps_h * s.taps_w == 1;
+    if (static_mode == 1 && !ok) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this problem "
+                                       "(built: NHWC bf16, K/G = 2048, one tap per class, no split)");
+    }
+    static_shape = ok && static_mode >= 0;
+  }
+
   // Tiles per class (contiguous ranges of the logical grid, in LPT order).
   int64_t tile = 0;
   int64_t tiles_m = kernel == CBD_KERNEL_GROUPED ? 1 : ceil_div(Cg, bm);
@@ -435,6 +457,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_mfma = grp_mfma ? 1 : 0;
   a.grp_cols = (int32_t)grp_cols;
   a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
+  a.static_shape = static_shape ? 1 : 0;
   a.ws = nullptr;
   pl->grid_finalize = ksplit > 1 ? tile / ksplit * (cbd::kFastBN / 8) : 0;
   for (size_t i = 0; i < subs.size(); i++) {
@@ -513,6 +536,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.rows_per_wg = grp_rows;
   info.cols_per_wg = grp_cols;
   info.ksplit = ksplit;
+  info.static_shape = static_shape ? 1 : 0;
   info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
   info.variant = kernel != CBD_KERNEL_GROUPED ? 0 : grp_mfma ? 3 : grp_rows > 0 ? 2 : grp_lds > 0 ? 1 : 0;
 

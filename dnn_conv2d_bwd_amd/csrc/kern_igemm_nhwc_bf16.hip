@@ -79,8 +79,10 @@ __device__ inline int swz_y(int row) { return (row >> 2) & 3; }  // dY rows: 4 c
 
 // SPLIT: the K loop of each tile is split over a.ksplit workgroups that
 // write f32 partial tiles (a separate instance, so that the plain kernel
-// carries none of its registers).
-template <bool SPLIT>
+// carries none of its registers).  SKPT, STAPS > 0: a shape-specialised
+// instance with k tiles per tap and taps per class fixed at compile time
+// (0: read from the descriptors at run time).
+template <bool SPLIT, int SKPT, int STAPS>
 __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmArgs a) {
   // Stages as distinct objects: the compiler can then see that fragment reads
   // of one stage do not alias the loads in flight into another.
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int rem = local - g * per_group;
   const int m0 = (rem % a.tiles_m) * BM;
   const int n0 = (rem / a.tiles_m) * BN;
-  const int ntaps = s.taps_h * s.taps_w;
+  const int ntaps = STAPS > 0 ? STAPS : s.taps_h * s.taps_w;
 
   // Buffer descriptors of dY and W as plain SGPR quads (the loads below are
   // written in assembly), record count = tensor bytes as in dev::rsrc.
@@ -124,13 +126,16 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // first defined inside a divergent region would live in VGPRs).
   const int YX = __builtin_amdgcn_readfirstlane(a.Y * a.X);
   const uint32_t wrow = __builtin_amdgcn_readfirstlane((uint32_t)(YX * a.Cg) * 2u);  // bytes between k rows of W
-  const int kpt = __builtin_amdgcn_readfirstlane(a.Kg / BK);
+  const int kpt = SKPT > 0 ? SKPT : __builtin_amdgcn_readfirstlane(a.Kg / BK);
   // This workgroup's k tiles: [kb, ke) of the class's ntaps * kpt (tile t =
   // tap t / kpt, k rows 32 (t mod kpt) ...); the planner keeps S <= ntaps*kpt.
-  const int KTall = __builtin_amdgcn_readfirstlane(ntaps * kpt);
+  const int KTall = SKPT > 0 && STAPS > 0 ? SKPT * STAPS : __builtin_amdgcn_readfirstlane(ntaps * kpt);
   const int kb = __builtin_amdgcn_readfirstlane(split * KTall / S);
   const int ke = __builtin_amdgcn_readfirstlane((split + 1) * KTall / S);
-  const int KT = ke - kb;  // k tiles of this workgroup
+  int KT = ke - kb;  // k tiles of this workgroup
+  // Opaque to the optimiser: with a compile-time trip count (the
+  // shape-specialised instance) it restructures the loop and spills.
+  asm volatile("" : "+s"(KT));
   const uint32_t kpt_magic = __builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)kpt + 1u);
 
   // ---- per-workgroup tables (threads 0..255: one position row each)
@@ -195,7 +200,10 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // Tile t = (tap, k tile) with tap = t / kpt, by multiply-high with a
   // rounded-up reciprocal (exact for t < 17 kpt, kpt <= 4096: tiles per
   // class are at most 16 kpt, plus the 4 tiles loaded past the end).
-  auto tap_of = [&](int t) -> int { return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic); };
+  auto tap_of = [&](int t) -> int {
+    if constexpr (SKPT > 0) return t / SKPT;
+    return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic);
+  };
   uint32_t a_soff = 0, b_soff = 0;
   // Move a set of offsets from tile t-1 to tile t: one add per lane offset,
   // except where a new tap starts (uniform branch, once per kpt tiles).
@@ -369,6 +377,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0,
          [&]() { advance_b(kb + kt + NSTAGE); });
   };
+#pragma unroll 1
   for (int kt = 0; kt < KT; kt += NSTAGE) {
     iter(kt, std::integral_constant<int, 0>());
     if (kt + 1 < KT) iter(kt + 1, std::integral_constant<int, 1>());
@@ -510,8 +519,9 @@ int launch_splitk_finalize(const GemmArgs& a, int64_t grid, void* stream) {
 
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  const void* k = a.ksplit > 1 ? (const void*)&igemm_nhwc_bf16_kernel<true>
-                               : (const void*)&igemm_nhwc_bf16_kernel<false>;
+  const void* k = a.ksplit > 1          ? (const void*)&igemm_nhwc_bf16_kernel<true, 0, 0>
+                  : a.static_shape == 1 ? (const void*)&igemm_nhwc_bf16_kernel<false, 64, 1>
+                                        : (const void*)&igemm_nhwc_bf16_kernel<false, 0, 0>;
   return (int)hipLaunchKernel(k, dim3((unsigned)grid), dim3(THREADS), args, 0, (hipStream_t)stream);
 }
 

@@ -122,7 +122,14 @@ typedef struct {
   int32_t per_class;    /* 1: one main launch per residue class instead of one
                            for all (an ablation of the single launch; not
                            with ksplit); 0 or 1 */
-  int32_t reserved[1];  /* must be zero */
+  int32_t static_shape; /* large-tile kernel: shape-specialised instances (k
+                           tiles per tap and taps per class fixed at compile
+                           time; built for K/G = 2048 with one tap per class)
+                           compute the same bits as the descriptor-driven
+                           kernel.  0: used when one matches; 1: required
+                           (UNSUPPORTED if none matches); -1: never (the
+                           descriptor-driven kernel, for comparison) */
+  int32_t reserved[4];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
@@ -198,6 +205,7 @@ typedef struct {
   int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernel: positions
                                per column block of a row (0: other kernels) */
   int64_t ksplit;           /* workgroups per tile of a split-K plan (1: none) */
+  int64_t static_shape;     /* 1: the main launch uses a shape-specialised instance */
   int64_t workspace_bytes;  /* device workspace cbd_run_ws needs (0: none) */
   int64_t variant;          /* kernel within the family; grouped: 0 direct,
                                1 one row per workgroup, 2 pipelined rows on

@@ -216,6 +216,22 @@ def test_per_class_launches_match_single_launch(name):
     assert many.guards_intact()
 
 
+@pytest.mark.parametrize("n", [16, 3])
+def test_static_shape_instance_matches_runtime(n):
+    """The shape-specialised instance of the large-tile kernel gives the same
+    bits as the runtime-descriptor one (c4 shape, full and ragged batch)."""
+    p = by_name("c4").with_(n=n)
+    print(f"[static] c4 n={n}", flush=True)
+    dy, w = operands(p)
+    dy_d, w_d = to_device(dy, p), to_device(w, p)
+    pa, pb = plan_for(p, static_shape=-1), plan_for(p)
+    assert pa.info().static_shape == 0 and pb.info().static_shape == 1
+    a = GpuRun(p, pa, dy_d, w_d)()
+    b = GpuRun(p, pb, dy_d, w_d)()
+    assert np.array_equal(a.result_bits(), b.result_bits())
+    assert b.guards_intact()
+
+
 def test_non_default_stream():
     p = by_name("c3a")
     dy, w = operands(p)

@@ -291,6 +291,23 @@ def test_ksplit_plans():
         cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=65)
 
 
+def test_static_shape_plans():
+    c4 = [p for p in PROBLEMS if p.name == "c4"][0]
+    args = (c4.n, c4.g, c4.c, c4.k, c4.hi, c4.wi, c4.y, c4.x, (c4.sh, c4.sw), (c4.ph, c4.pw),
+            (c4.dh, c4.dw), c4.layout, cbd.BF16)
+    a, b = cbd.plan(*args, static_shape=-1).info(), cbd.plan(*args).info()
+    assert (a.grid_main, a.launches, a.executed_macs) == (b.grid_main, b.launches, b.executed_macs)
+    assert a.static_shape == 0 and b.static_shape == 1
+    assert cbd.plan(*args, static_shape=1).info().static_shape == 1
+    assert cbd.plan(*args, ksplit=2).info().static_shape == 0
+    other = (2, 1, 256, 1024, 1, 64, 1, 2, (1, 2), 0, 1, "nhwc", "bf16")
+    assert cbd.plan(*other).info().static_shape == 0
+    with pytest.raises(cbd.CbdError):   # K/G = 1024: no instance
+        cbd.plan(*other, static_shape=1)
+    with pytest.raises(cbd.CbdError):   # split-K: no instance
+        cbd.plan(*args, static_shape=1, ksplit=2)
+
+
 def test_run_without_device_returns_hip_error():
     """On a machine with no GPU, cbd_run reports CBD_ERR_HIP instead of
     aborting (run in a child process to keep this one clean)."""
