@@ -27,6 +27,7 @@ SOURCES = [
     "kern_grouped_rows.hip",
     "kern_grouped_pipe.hip",
     "kern_grouped_mfma.hip",
+    "kern_grouped_wide.hip",
     "kern_zero_fill.hip",
 ]
 

@@ -81,7 +81,8 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
       switch (info.kernel) {
         case CBD_KERNEL_NHWC_BF16: return cbd::launch_nhwc_bf16(args, grid, stream);
         case CBD_KERNEL_GROUPED:
-          return args.grp_mfma      ? cbd::launch_grouped_mfma(args, grid, stream)
+          return args.grp_wide      ? cbd::launch_grouped_wide(args, grid, stream)
+                 : args.grp_mfma    ? cbd::launch_grouped_mfma(args, grid, stream)
                  : args.grp_rows > 0 ? cbd::launch_grouped_pipe(args, plan->prob.dtype, grid, stream)
                  : args.grp_lds > 0  ? cbd::launch_grouped_rows(args, plan->prob.dtype, grid, stream)
                                      : cbd::launch_grouped(args, plan->prob.dtype, grid, stream);

@@ -30,6 +30,7 @@ int launch_grouped(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_pipe(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_mfma(const GemmArgs& a, int64_t grid, void* stream);
+int launch_grouped_wide(const GemmArgs& a, int64_t grid, void* stream);
 int launch_zero_fill(const ZeroArgs& z, int64_t grid, void* stream);
 const char* hip_error_name(int err);
 

@@ -85,6 +85,13 @@ bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
          max_taps <= cbd::kFastMaxTaps;
 }
 
+// The 16x16x16-MFMA grouped kernel: bf16 NHWC, 16 or 32 channels per group,
+// groups in blocks whose channels make a 256-byte slice, taps one dY row apart.
+bool grouped_wide_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps, int64_t delta_h) {
+  return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Cg == Kg && (Cg == 16 || Cg == 32) &&
+         p.g % (256 / (2 * Cg)) == 0 && delta_h == 1 && max_taps <= cbd::kGroupedMaxTaps;
+}
+
 bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
   return p.layout == CBD_LAYOUT_NHWC && Cg == Kg && (Cg == 1 || Cg == 2 || Cg == 4 || Cg == 8) &&
          p.g <= cbd::kGroupedThreads && cbd::kGroupedThreads % p.g == 0 &&
@@ -234,7 +241,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   if (force == CBD_KERNEL_AUTO) {
     if (fast_ok(p, Cg, Kg, max_taps) && Cg >= 128)
       kernel = CBD_KERNEL_NHWC_BF16;
-    else if (!no_split && grouped_ok(p, Cg, Kg, max_taps))
+    else if (!no_split && (grouped_ok(p, Cg, Kg, max_taps) ||
+                           grouped_wide_ok(p, Cg, Kg, max_taps, ah.delta)))
       kernel = CBD_KERNEL_GROUPED;
     else
       kernel = CBD_KERNEL_GENERIC;
@@ -248,9 +256,11 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "the grouped kernels have no zero-insertion (no_split) mode");
     }
-    if (kernel == CBD_KERNEL_GROUPED && !grouped_ok(p, Cg, Kg, max_taps)) {
+    if (kernel == CBD_KERNEL_GROUPED && !grouped_ok(p, Cg, Kg, max_taps) &&
+        !grouped_wide_ok(p, Cg, Kg, max_taps, ah.delta)) {
       delete pl;
-      return fail(CBD_ERR_UNSUPPORTED, "grouped kernel needs NHWC, C/G == K/G in {1,2,4,8}, G | 256, <= 9 taps per class");
+      return fail(CBD_ERR_UNSUPPORTED, "grouped kernels need NHWC, C/G == K/G in {1,2,4,8} with G | 256, "
+                                       "or bf16 with C/G in {16,32}, taps one dY row apart; <= 9 taps per class");
     }
   }
 
@@ -286,8 +296,50 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int64_t slots = 0;
   int64_t grp_lds = 0;
   int64_t grp_rows = 0, grp_cols = 0;
-  bool grp_mfma = false;
-  if (kernel == CBD_KERNEL_GROUPED) {
+  bool grp_mfma = false, grp_wide = false;
+  if (kernel == CBD_KERNEL_GROUPED && (Cg == 16 || Cg == 32) && !subs.empty()) {
+    // 16x16x16-MFMA kernel: workgroup = (image, R rows, a 256-byte slice of
+    // groups, CB positions); ring slots of CB + span columns (whole KiB)
+    // plus the output buffer of 16-position chunks.  Whole rows unless that
+    // leaves fewer than 3 workgroups per compute unit.
+    grp_wide = true;
+    const int64_t gblocks = p.g / (256 / (2 * Cg));
+    int64_t max_pos_h = 0, max_pos_w = 0;
+    for (const auto& s : subs) {
+      max_pos_h = std::max<int64_t>(max_pos_h, s.pos_h);
+      max_pos_w = std::max<int64_t>(max_pos_w, s.pos_w);
+    }
+    auto lds_wide = [&](int64_t cb) {
+      int64_t r = 0;
+      for (const auto& s : subs) {
+        const int64_t seg = std::min<int64_t>(cb, s.pos_w);
+        const int64_t rowb = (seg + aw.delta * (s.taps_w - 1)) * 256;
+        r = std::max<int64_t>(r, (s.taps_h + 1) * ceil_div(rowb, 1024) * 1024 + 16 * ceil_div(seg, 16) * 256);
+      }
+      return r;
+    };
+    int64_t cb = 16 * ceil_div(max_pos_w, 16);
+    if (cols_opt > 0) {
+      cb = std::min<int64_t>(cb, 16 * ceil_div(cols_opt, 16));
+    } else {
+      for (int64_t k = 2; lds_wide(cb) > cbd::kLdsPerCu / 3 && cb > 16; k++)
+        cb = 16 * ceil_div(max_pos_w, 16 * k);
+    }
+    grp_cols = cb;
+    grp_lds = lds_wide(cb);
+    if (grp_lds > cbd::kLdsPerCu) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "grouped MFMA kernel: a 16-position block's rows exceed LDS");
+    }
+    int64_t units = 0;
+    for (const auto& s : subs) units += p.n * s.pos_h * gblocks * ceil_div(s.pos_w, cb);
+    if (rows_opt > 0) {
+      grp_rows = std::min<int64_t>(rows_opt, max_pos_h);
+    } else {
+      const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / grp_lds);
+      grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(units, resident)));
+    }
+  } else if (kernel == CBD_KERNEL_GROUPED) {
     slots = cbd::kGroupedThreads / p.g;
     const int64_t pixb = p.c * es;
     const bool mfma_ok = !grouped_dot && p.dtype == CBD_BF16 && Cg == 4 && (p.g == 32 || p.g == 64);
@@ -392,7 +444,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     s.id = (int32_t)i;
     s.tile_begin = tile;
     if (kernel == CBD_KERNEL_GROUPED)
-      s.tiles = grp_mfma      ? p.n * ceil_div(s.pos_h, grp_rows) * ceil_div(s.pos_w, grp_cols)
+      s.tiles = grp_wide      ? p.n * ceil_div(s.pos_h, grp_rows) * (p.g / (256 / (2 * Cg))) *
+                                    ceil_div(s.pos_w, grp_cols)
+                : grp_mfma      ? p.n * ceil_div(s.pos_h, grp_rows) * ceil_div(s.pos_w, grp_cols)
                 : grp_rows > 0  ? p.n * ceil_div(s.pos_h, grp_rows)
                 : grp_lds > 0 ? p.n * s.pos_h
                               : ceil_div(s.n, slots * iters);
@@ -455,6 +509,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_lds = (int32_t)grp_lds;
   a.grp_rows = (int32_t)grp_rows;
   a.grp_mfma = grp_mfma ? 1 : 0;
+  a.grp_wide = grp_wide ? 1 : 0;
   a.grp_cols = (int32_t)grp_cols;
   a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
   a.static_shape = static_shape ? 1 : 0;
@@ -538,7 +593,12 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.ksplit = ksplit;
   info.static_shape = static_shape ? 1 : 0;
   info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
-  info.variant = kernel != CBD_KERNEL_GROUPED ? 0 : grp_mfma ? 3 : grp_rows > 0 ? 2 : grp_lds > 0 ? 1 : 0;
+  info.variant = kernel != CBD_KERNEL_GROUPED ? 0
+                 : grp_wide                    ? 4
+                 : grp_mfma                    ? 3
+                 : grp_rows > 0                ? 2
+                 : grp_lds > 0                 ? 1
+                                               : 0;
 
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);

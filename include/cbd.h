@@ -87,7 +87,9 @@ typedef enum {
                                9 taps per class: per-group accumulation, filter
                                in registers; dY rows streamed through an LDS
                                ring when C/G <= 4, a pixel is a multiple of 16
-                               bytes and a class's taps are one dY row apart */
+                               bytes and a class's taps are one dY row apart;
+                               also bf16 with C/G in {16, 32} (16x16x16 MFMA,
+                               taps one dY row apart, 256-byte group slices) */
 } cbd_kernel;
 
 typedef struct {
@@ -108,9 +110,10 @@ typedef struct {
   int32_t grouped_dot;  /* grouped family: 1 keeps the pipelined kernel on
                            dot-product instructions where it would use the
                            4x4x4 MFMA (a comparison switch); 0 or 1 */
-  int32_t cols_per_wg;  /* grouped family, MFMA pipelined kernel: positions of a
-                           row per workgroup, rounded up to a multiple of 4
-                           (0: the planner's choice) */
+  int32_t cols_per_wg;  /* grouped family, MFMA pipelined kernels: positions of
+                           a row per workgroup, rounded up to a multiple of 4
+                           (4x4x4 kernel) or 16 (16x16x16 kernel) (0: the
+                           planner's choice) */
   int32_t ksplit;       /* large-tile (NHWC bf16) kernel: split each tile's K
                            loop over this many workgroups (0 or 1: no split;
                            at most 64; clamped to the k tiles of the
@@ -202,7 +205,7 @@ typedef struct {
                                launch (grouped family: 0 for the direct kernel) */
   int64_t rows_per_wg;      /* grouped family: output rows per workgroup of the
                                pipelined row kernels (0: another kernel) */
-  int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernel: positions
+  int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernels: positions
                                per column block of a row (0: other kernels) */
   int64_t ksplit;           /* workgroups per tile of a split-K plan (1: none) */
   int64_t static_shape;     /* 1: the main launch uses a shape-specialised instance */
@@ -210,8 +213,9 @@ typedef struct {
   int64_t variant;          /* kernel within the family; grouped: 0 direct,
                                1 one row per workgroup, 2 pipelined rows on
                                dot-product instructions, 3 pipelined rows on
-                               4x4x4 MFMA (bf16, C/G = 4, G = 32 or 64);
-                               other families: 0 */
+                               4x4x4 MFMA (bf16, C/G = 4, G = 32 or 64),
+                               4 pipelined rows on 16x16x16 MFMA (bf16, C/G
+                               = 16 or 32); other families: 0 */
 } cbd_plan_info_t;
 
 typedef struct {

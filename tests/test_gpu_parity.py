@@ -436,6 +436,42 @@ def test_grouped_sweep_sampled(name):
     assert run.guards_intact()
 
 
+# The 16x16x16-MFMA grouped kernel: bf16, 16 or 32 channels per group,
+# random geometry, rows and column blocks; integer-exact.
+@pytest.mark.parametrize("seed,count", [(18, 50)])
+def test_fuzz_grouped_wide(seed, count):
+    rng = random.Random(seed)
+    done = 0
+    while done < count:
+        cg = rng.choice([16, 32])
+        g = rng.choice([8, 16, 32]) if cg == 16 else rng.choice([4, 8, 32])
+        p = Problem("fuzz", rng.randint(1, 2), g, cg * g, cg * g, rng.randint(1, 40),
+                    rng.randint(1, 40), rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 3),
+                    rng.randint(1, 3), rng.randint(0, 2), rng.randint(0, 2), rng.randint(1, 2),
+                    rng.randint(1, 2), NHWC, "bf16", "u", "u", 0, 0)
+        if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
+                or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0):
+            continue
+        rows = rng.choice([0, 1, 3, 64])
+        cols = rng.choice([0, 0, 16, 20])
+        try:
+            pl = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols)
+        except cbd.CbdError:
+            continue
+        if pl.info().variant != 4 or pl.info().grid_main == 0:
+            continue
+        print(f"[fuzz-wide] i={done} rows={rows} cols={cols} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(6000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(6000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
+        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+        got = run.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
+        assert run.guards_intact(), (p, rows, cols)
+        done += 1
+
+
 # ------------------------------------------------------------ graph capture ---
 
 @pytest.mark.parametrize("name", ["c3b", "c4", "c5-s2"])
