@@ -85,11 +85,13 @@ bool fast_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
          max_taps <= cbd::kFastMaxTaps;
 }
 
-// The 16x16x16-MFMA grouped kernel: bf16 NHWC, 16 or 32 channels per group,
-// groups in blocks whose channels make a 256-byte slice, taps one dY row apart.
+// The 16x16x16-MFMA grouped kernel: bf16 NHWC, 8, 16 or 32 channels per
+// group, groups in blocks whose channels make a 256-byte slice, taps one dY
+// row apart.
 bool grouped_wide_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps, int64_t delta_h) {
-  return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Cg == Kg && (Cg == 16 || Cg == 32) &&
-         p.g % (256 / (2 * Cg)) == 0 && delta_h == 1 && max_taps <= cbd::kGroupedMaxTaps;
+  return p.layout == CBD_LAYOUT_NHWC && p.dtype == CBD_BF16 && Cg == Kg &&
+         (Cg == 8 || Cg == 16 || Cg == 32) && p.g % (256 / (2 * Cg)) == 0 && delta_h == 1 &&
+         max_taps <= cbd::kGroupedMaxTaps;
 }
 
 bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) {
@@ -297,7 +299,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int64_t grp_lds = 0;
   int64_t grp_rows = 0, grp_cols = 0;
   bool grp_mfma = false, grp_wide = false;
-  if (kernel == CBD_KERNEL_GROUPED && (Cg == 16 || Cg == 32) && !subs.empty()) {
+  if (kernel == CBD_KERNEL_GROUPED && (Cg == 16 || Cg == 32) && rows_opt < 0) {
+    delete pl;
+    return fail(CBD_ERR_UNSUPPORTED, "16 or 32 channels per group run only on the pipelined kernel "
+                                     "(rows_per_wg = -1)");
+  }
+  if (kernel == CBD_KERNEL_GROUPED && !subs.empty() && rows_opt >= 0 &&
+      grouped_wide_ok(p, Cg, Kg, max_taps, ah.delta)) {
     // 16x16x16-MFMA kernel: workgroup = (image, R rows, a 256-byte slice of
     // groups, CB positions); ring slots of CB + span columns (whole KiB)
     // plus the output buffer of 16-position chunks.  Whole rows unless that

@@ -1,5 +1,5 @@
 // kern_grouped_wide.hip -- grouped backward-data, bf16, C/G == K/G in
-// {16, 32}, on the 16x16x16 bf16 MFMA.
+// {8, 16, 32}, on the 16x16x16 bf16 MFMA.
 //
 // Per group the class sum is a small GEMM: dX[c][position] = sum over taps
 // and k of W[tap][k][c] * dY[position + tap][k], with c and k < C/G.  Here
@@ -9,8 +9,10 @@
 // B[4(l/16) .. +3][l % 16], i.e. 8 bytes of the group's channels at
 // position l % 16); D[c][n] lands in lane n + 16 (c/4), register c % 4:
 // four consecutive dX channels of one position.  C/G = 32 takes two
-// channel halves times two k halves.  The lane layout was checked with a
-// one-wave probe.
+// channel halves times two k halves; C/G = 8 runs as C/G = 16 on pairs of
+// adjacent groups (their 16 channels are contiguous in a pixel) with a
+// block-diagonal A: the two groups' 8x8 taps on the diagonal, zeros off it.
+// The lane layout was checked with a one-wave probe.
 //
 // Workgroup = (class, image, R output rows, a block of groups whose
 // channels make a 256-byte slice of each pixel, a block of CB positions):
@@ -44,7 +46,9 @@ __device__ __forceinline__ int chunked_block(int b, int total) {
   return (r << 6) + ((i & 7) << 3) + (i >> 3);
 }
 
-template <int CG, int NT>
+// CG: channels per (virtual) group, 16 or 32; PAIR8: the problem's groups
+// have 8 channels and a virtual group is two of them.
+template <int CG, bool PAIR8, int NT>
 __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, char* ring, int n, int gb,
                                           int th0, int th1, int tb, int seg) {
   constexpr int ES = 2;
@@ -115,7 +119,9 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
   for (int jh = s.taps_h - 1; jh >= 0; jh--) copy_row(th0 + s.beta_h - jh, back(jh));
 
   // A operands: group gl = wave*GPW + j (global gb*GB + gl); lane l holds
-  // W[g*CG + 16 kh + 4 lq + e][ty][tx][16 ch + ln], e = 0..3.
+  // W[g*CG + 16 kh + 4 lq + e][ty][tx][16 ch + ln], e = 0..3 (paired groups
+  // of 8: the entry of real group 2g + ln/8 where k and c fall in the same
+  // group, 0 elsewhere).
   const int YX = a.Y * a.X;
   s16x4 wa[GPW][NT][H][H];
   int jhs[NT], cshift[NT];
@@ -135,9 +141,20 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
         for (int ch = 0; ch < H; ch++) {
           uint32_t e[4];
 #pragma unroll
-          for (int q = 0; q < 4; q++)
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(
-                rw, (uint32_t)(((g * CG + 16 * kh + 4 * lq + q) * YX + ty * a.X + tx) * CG + 16 * ch + ln) * ES, 0, 0);
+          for (int q = 0; q < 4; q++) {
+            if constexpr (PAIR8) {
+              const int k = 4 * lq + q;  // 0..15 within the pair
+              const bool on = (k >> 3) == (ln >> 3);
+              const int rg = 2 * g + (ln >> 3);
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(
+                  rw, on ? (uint32_t)(((rg * 8 + (k & 7)) * YX + ty * a.X + tx) * 8 + (ln & 7)) * ES : dev::kOOB,
+                  0, 0);
+            } else {
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(
+                  rw, (uint32_t)(((g * CG + 16 * kh + 4 * lq + q) * YX + ty * a.X + tx) * CG + 16 * ch + ln) * ES, 0,
+                  0);
+            }
+          }
           const u32x2 v = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
           wa[j][tp][kh][ch] = __builtin_bit_cast(s16x4, v);
         }
@@ -199,10 +216,10 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
   flush_row(th1 - 1);
 }
 
-template <int CG>
+template <int CG, bool PAIR8>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_wide_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
-  constexpr int GB = SB / (CG * 2);
+  constexpr int GB = SB / ((PAIR8 ? 8 : CG) * 2);  // the problem's groups per workgroup
   const int t = chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   // (image, row block, group block, column block), column blocks innermost
@@ -223,22 +240,22 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_wide_kernel(const Gem
   const int seg = tb + CB < s.pos_w ? CB : s.pos_w - tb;
   static_assert(kGroupedMaxTaps == 9, "the switch below covers 1..9 taps");
   switch (s.taps_h * s.taps_w) {
-    case 1: wide_rows<CG, 1>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 2: wide_rows<CG, 2>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 3: wide_rows<CG, 3>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 4: wide_rows<CG, 4>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 5: wide_rows<CG, 5>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 6: wide_rows<CG, 6>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 7: wide_rows<CG, 7>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    case 8: wide_rows<CG, 8>(a, s, ring, n, gb, th0, th1, tb, seg); break;
-    default: wide_rows<CG, 9>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 1: wide_rows<CG, PAIR8, 1>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 2: wide_rows<CG, PAIR8, 2>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 3: wide_rows<CG, PAIR8, 3>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 4: wide_rows<CG, PAIR8, 4>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 5: wide_rows<CG, PAIR8, 5>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 6: wide_rows<CG, PAIR8, 6>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 7: wide_rows<CG, PAIR8, 7>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    case 8: wide_rows<CG, PAIR8, 8>(a, s, ring, n, gb, th0, th1, tb, seg); break;
+    default: wide_rows<CG, PAIR8, 9>(a, s, ring, n, gb, th0, th1, tb, seg); break;
   }
 }
 
-template <int CG>
+template <int CG, bool PAIR8>
 int launch_cg(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&grouped_wide_kernel<CG>, dim3((unsigned)grid),
+  return (int)hipLaunchKernel((const void*)&grouped_wide_kernel<CG, PAIR8>, dim3((unsigned)grid),
                               dim3(kGroupedThreads), args, (size_t)a.grp_lds, (hipStream_t)stream);
 }
 
@@ -246,8 +263,9 @@ int launch_cg(const GemmArgs& a, int64_t grid, void* stream) {
 
 int launch_grouped_wide(const GemmArgs& a, int64_t grid, void* stream) {
   switch (a.Cg) {
-    case 16: return launch_cg<16>(a, grid, stream);
-    case 32: return launch_cg<32>(a, grid, stream);
+    case 8: return launch_cg<16, true>(a, grid, stream);
+    case 16: return launch_cg<16, false>(a, grid, stream);
+    case 32: return launch_cg<32, false>(a, grid, stream);
     default: return (int)hipErrorInvalidValue;
   }
 }

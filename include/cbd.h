@@ -105,8 +105,9 @@ typedef struct {
   int32_t rows_per_wg;  /* grouped family, pipelined row kernel: output rows
                            per workgroup (0: the planner's choice; larger than
                            a class's rows: clamped); -1: never the pipelined
-                           kernel (row or direct kernel instead).  Other
-                           families ignore it. */
+                           kernels (row or direct kernel instead; UNSUPPORTED
+                           for 16 or 32 channels per group).  Other families
+                           ignore it. */
   int32_t grouped_dot;  /* grouped family: 1 keeps the pipelined kernel on
                            dot-product instructions where it would use the
                            4x4x4 MFMA (a comparison switch); 0 or 1 */

@@ -436,15 +436,15 @@ def test_grouped_sweep_sampled(name):
     assert run.guards_intact()
 
 
-# The 16x16x16-MFMA grouped kernel: bf16, 16 or 32 channels per group,
-# random geometry, rows and column blocks; integer-exact.
-@pytest.mark.parametrize("seed,count", [(18, 50)])
+# The 16x16x16-MFMA grouped kernel: bf16, 8 (as pairs), 16 or 32 channels
+# per group, random geometry, rows and column blocks; integer-exact.
+@pytest.mark.parametrize("seed,count", [(18, 60)])
 def test_fuzz_grouped_wide(seed, count):
     rng = random.Random(seed)
     done = 0
     while done < count:
-        cg = rng.choice([16, 32])
-        g = rng.choice([8, 16, 32]) if cg == 16 else rng.choice([4, 8, 32])
+        cg = rng.choice([8, 16, 32])
+        g = {8: [16, 32, 64], 16: [8, 16, 32], 32: [4, 8, 32]}[cg][rng.randint(0, 2)]
         p = Problem("fuzz", rng.randint(1, 2), g, cg * g, cg * g, rng.randint(1, 40),
                     rng.randint(1, 40), rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 3),
                     rng.randint(1, 3), rng.randint(0, 2), rng.randint(0, 2), rng.randint(1, 2),
