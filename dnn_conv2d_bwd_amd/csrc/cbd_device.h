@@ -47,6 +47,18 @@ __device__ inline int logical_tile(int b, int total, int remap) {
   return x * q + (x < r ? x : r) + idx;
 }
 
+// Logical block of hardware workgroup b for the grouped row kernels:
+// workgroups go round-robin to the 8 XCDs, and XCD x gets logical blocks
+// 64r + 8x .. 64r + 8x + 7, so neighbouring row blocks of one image (which
+// share dY rows) meet in one L2.  Blocks past the last multiple of 64 map to
+// themselves.
+__device__ inline int chunked_block(int b, int total) {
+  const int full = total & ~63;
+  if (b >= full) return b;
+  const int r = b >> 6, i = b & 63;
+  return (r << 6) + ((i & 7) << 3) + (i >> 3);
+}
+
 // dY index read by tap j of class position t along one axis.  Residue split:
 // t + beta - delta*j.  Zero-insertion form (no_split): t is the dX index
 // itself and the term exists only where t + pad - j*dil is a non-negative

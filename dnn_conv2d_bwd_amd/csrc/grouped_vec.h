@@ -1,6 +1,6 @@
 // grouped_vec.h -- small helpers shared by the grouped row kernels: one
 // group's channels at one pixel as a vector of 2..16 bytes (LDS read,
-// buffer load, buffer store), and the row -> XCD dealing.
+// buffer load, buffer store).
 #pragma once
 #include "cbd_device.h"
 
@@ -72,15 +72,6 @@ __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const V
     u4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
     __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
   }
-}
-
-// Logical row of hardware workgroup b: workgroups go round-robin to the 8
-// XCDs; XCD x gets logical rows 64r + 8x .. 64r + 8x + 7 in order.
-__device__ inline int chunked_row(int b, int total) {
-  const int full = total & ~63;
-  if (b >= full) return b;
-  const int r = b >> 6, i = b & 63;
-  return (r << 6) + ((i & 7) << 3) + (i >> 3);
 }
 
 }  // namespace grp

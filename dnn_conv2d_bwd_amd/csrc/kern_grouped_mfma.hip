@@ -50,16 +50,6 @@ __device__ __forceinline__ s16x4 as_s16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(s16x4, v);
 }
 
-// Logical block of hardware workgroup b: XCD x gets logical blocks
-// 64r + 8x .. 64r + 8x + 7, so neighbouring row blocks of one image (which
-// share taps_h - 1 dY rows) meet in one L2.
-__device__ inline int chunked_block(int b, int total) {
-  const int full = total & ~63;
-  if (b >= full) return b;
-  const int r = b >> 6, i = b & 63;
-  return (r << 6) + ((i & 7) << 3) + (i >> 3);
-}
-
 template <int G, int NT>
 __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, char* ring, int n,
                                           int th0, int th1, int tb, int seg) {
@@ -215,7 +205,7 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
 template <int G>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_mfma_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
-  const int t = chunked_block(blockIdx.x, a.total_tiles);
+  const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   // (image, row block, column block), column blocks innermost
   const int R = a.grp_rows, CB = a.grp_cols;

@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_pipe_kernel(const Gem
   q.slots = kGroupedThreads / a.G;
 
   // workgroup -> (class, image n, row block)
-  const int t = chunked_row(blockIdx.x, a.total_tiles);
+  const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   const int R = a.grp_rows;
   const int blocks = (s.pos_h + R - 1) / R;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_rows_kernel(const Gem
   const int slot = tid / G;
   const int slots = kGroupedThreads / G;
 
-  const int row = chunked_row(blockIdx.x, a.total_tiles);
+  const int row = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, row)];
   const int local = row - s.tile_begin;
   const int n = local / s.pos_h;

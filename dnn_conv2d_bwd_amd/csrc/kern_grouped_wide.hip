@@ -39,13 +39,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int SB = 256;  // bytes of a pixel's group slice handled by one workgroup
 
-__device__ __forceinline__ int chunked_block(int b, int total) {
-  const int full = total & ~63;
-  if (b >= full) return b;
-  const int r = b >> 6, i = b & 63;
-  return (r << 6) + ((i & 7) << 3) + (i >> 3);
-}
-
 // CG: channels per (virtual) group, 16 or 32; PAIR8: the problem's groups
 // have 8 channels and a virtual group is two of them.
 template <int CG, bool PAIR8, int NT>
@@ -220,7 +213,7 @@ template <int CG, bool PAIR8>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_wide_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   constexpr int GB = SB / ((PAIR8 ? 8 : CG) * 2);  // the problem's groups per workgroup
-  const int t = chunked_block(blockIdx.x, a.total_tiles);
+  const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   // (image, row block, group block, column block), column blocks innermost
   const int R = a.grp_rows, CB = a.grp_cols;

@@ -53,7 +53,7 @@ def to_device(a, p):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dtype(p)).cuda()
 
 
-class GpuRun:
+class DeviceRun:
     """Allocates a sentinel-filled dX with guard bands and runs a plan."""
 
     def __init__(self, p, pl, dy_d, w_d, workspace=None):
@@ -129,7 +129,7 @@ def check_bf16(got_bits, ref64):
     return ok, info
 
 
-def check(p, gpu: GpuRun, ref64):
+def check(p, gpu: DeviceRun, ref64):
     if p.dtype == "f32":
         return check_f32(gpu.result_f32().reshape(ref64.shape), ref64)
     return check_bf16(gpu.result_bits().reshape(ref64.shape), ref64)

@@ -23,7 +23,7 @@ import oracle
 from cbd_inputs import GROUPED_SWEEP, PROBLEMS, small_ints, uniform
 from cbd_inputs.problems import NCHW, NHWC, Problem
 
-from parity import GpuRun, check, check_bf16, check_f32, exact_expected_bits, operands, \
+from parity import DeviceRun, check, check_bf16, check_f32, exact_expected_bits, operands, \
     plan_for, to_device
 
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,7 @@ def test_workload_vs_oracle(name, force):
     dy, w = operands(p)
     ref = oracle.bwd_data(p, dy, w)
     pl = plan_for(p, force)
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     ok, info = check(p, run, ref)
     assert ok, info
     assert run.guards_intact()
@@ -91,7 +91,7 @@ def test_workload_integer_exact(name):
     print(f"[exact] {name}", flush=True)
     dy, w = operands(p, "int")
     pl = plan_for(p)
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     got = run.result_f32()
     if name == "c4":
         # two plain GEMMs (pinned reduction): dX[:,0,r::2,:] = dY[:,0] @ W[:,0,r,:]
@@ -115,7 +115,7 @@ def test_c4_full_size():
     dy, w = operands(p)
     pl = plan_for(p)
     assert pl.info().kernel == cbd.KERNEL_NHWC_BF16
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     bits = run.result_bits().reshape(p.n, p.hi, p.wi, p.c)
     assert run.guards_intact()
     # sampled outputs, one by one, from the oracle: every tile corner plus random points
@@ -152,7 +152,7 @@ def test_c4_ksplit(ksplit):
     pl = plan_for(p, ksplit=ksplit)
     assert pl.info().ksplit == ksplit
     ws = torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
     bits = run.result_bits().reshape(p.n, p.hi, p.wi, p.c)
     assert run.guards_intact()
     ref = np.empty((p.n, 1, p.wi, p.c), dtype=np.float64)
@@ -176,7 +176,7 @@ def test_c4_shard_ksplit_integer_exact(n, ksplit):
     dy, w = operands(p, "int")
     pl = plan_for(p, ksplit=ksplit)
     ws = torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
     want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
     got = run.result_f32()
     assert np.array_equal(got, want.reshape(got.shape))
@@ -194,7 +194,7 @@ def test_fuzz_ksplit_integer_exact(seed, count):
         dy = small_ints(5000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
         w = small_ints(5000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
         ws = torch.empty(max(pl.workspace_size(), 1), dtype=torch.uint8, device="cuda")
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
         want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
         got = run.result_f32()
         assert np.array_equal(got, want.reshape(got.shape)), (p, ksplit)
@@ -208,10 +208,10 @@ def test_per_class_launches_match_single_launch(name):
     print(f"[per-class] {name}", flush=True)
     dy, w = operands(p)
     dy_d, w_d = to_device(dy, p), to_device(w, p)
-    one = GpuRun(p, plan_for(p), dy_d, w_d)()
+    one = DeviceRun(p, plan_for(p), dy_d, w_d)()
     pl = plan_for(p, per_class=True)
     assert pl.info().launches >= pl.info().num_subgemms
-    many = GpuRun(p, pl, dy_d, w_d)()
+    many = DeviceRun(p, pl, dy_d, w_d)()
     assert np.array_equal(one.result_bits(), many.result_bits())
     assert many.guards_intact()
 
@@ -226,8 +226,8 @@ def test_static_shape_instance_matches_runtime(n):
     dy_d, w_d = to_device(dy, p), to_device(w, p)
     pa, pb = plan_for(p, static_shape=-1), plan_for(p)
     assert pa.info().static_shape == 0 and pb.info().static_shape == 1
-    a = GpuRun(p, pa, dy_d, w_d)()
-    b = GpuRun(p, pb, dy_d, w_d)()
+    a = DeviceRun(p, pa, dy_d, w_d)()
+    b = DeviceRun(p, pb, dy_d, w_d)()
     assert np.array_equal(a.result_bits(), b.result_bits())
     assert b.guards_intact()
 
@@ -241,7 +241,7 @@ def test_non_default_stream():
     dy_d, w_d = to_device(dy, p), to_device(w, p)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        run = GpuRun(p, pl, dy_d, w_d)
+        run = DeviceRun(p, pl, dy_d, w_d)
         run(stream=s)
     s.synchronize()
     ok, info = check(p, run, ref)
@@ -309,7 +309,7 @@ def test_fuzz_integer_exact(family, seed, count):
         dy = small_ints(1000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
         w = small_ints(1000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
         pl = plan_for(p, family)
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         ref = oracle.bwd_data(p, dy, w)
         want = exact_expected_bits(p, ref)
         want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
@@ -331,7 +331,7 @@ def test_fuzz_random_values(family, seed, count):
         dy = to_dtype(uniform(2000 * seed + 3 * i + 1, sh["dy"]), p.dtype)
         w = to_dtype(uniform(2000 * seed + 3 * i + 2, sh["w"]), p.dtype)
         pl = plan_for(p, family)
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         ok, info = check(p, run, oracle.bwd_data(p, dy, w))
         assert ok, (p, info)
 
@@ -353,7 +353,7 @@ def test_fuzz_grouped_rows_per_wg(seed, count):
         sh = oracle.shapes(p)
         dy = small_ints(3000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
         w = small_ints(3000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         want = exact_expected_bits(p, oracle.bwd_data(p, dy, w))
         want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
         got = run.result_f32()
@@ -374,7 +374,7 @@ def test_grouped_workload_rows_per_wg(name, rows, dot, cols):
     inf = pl.info()
     assert inf.kernel == cbd.KERNEL_GROUPED
     assert inf.variant == (1 if rows == -1 else 2 if dot else 3)
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     ok, info = check(p, run, oracle.bwd_data(p, dy, w))
     assert ok, info
     assert run.guards_intact()
@@ -407,7 +407,7 @@ def test_fuzz_grouped_mfma(seed, count):
         sh = oracle.shapes(p)
         dy = small_ints(4000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
         w = small_ints(4000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
         got = run.result_f32()
         assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
@@ -423,7 +423,7 @@ def test_grouped_sweep_sampled(name):
     print(f"[sweep] {name} n=4", flush=True)
     dy, w = operands(p)
     pl = plan_for(p)
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     bits = run.result_bits()  # NHWC
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     cnt = 3000
@@ -464,7 +464,7 @@ def test_fuzz_grouped_wide(seed, count):
         sh = oracle.shapes(p)
         dy = small_ints(6000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
         w = small_ints(6000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
         got = run.result_f32()
         assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
@@ -519,7 +519,7 @@ def test_no_split_vs_oracle(name):
     p = by_name(name)
     print(f"[no-split] {name}", flush=True)
     dy, w = operands(p)
-    run = GpuRun(p, plan_no_split(p), to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, plan_no_split(p), to_device(dy, p), to_device(w, p))()
     ok, info = check(p, run, oracle.bwd_data(p, dy, w))
     assert ok, info
     assert run.guards_intact()
@@ -533,7 +533,7 @@ def test_no_split_c4_integer_exact():
     dy, w = operands(p, "int")
     pl = plan_no_split(p)
     assert pl.info().kernel == cbd.KERNEL_NHWC_BF16
-    run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     got = run.result_f32()
     ref = np.empty(got.shape, dtype=np.float64)
     for r in range(2):
@@ -558,7 +558,7 @@ def test_fuzz_no_split_integer_exact(family, seed, count):
             pl = plan_no_split(p, family)
         except cbd.CbdError:
             continue  # e.g. more than 16 taps for the large-tile kernel
-        run = GpuRun(p, pl, to_device(dy, p), to_device(w, p))()
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
         want = exact_expected_bits(p, oracle.bwd_data(p, dy, w))
         want = oracle.bf16_bits_to_f32(want) if p.dtype == "bf16" else want.view(np.float32)
         got = run.result_f32()
