@@ -13,10 +13,13 @@ problem has unreached phases).
 Prints ONE JSON line:
   value        useful TFLOP/s (2*N*C*(K/G)*Ho*Wo*Y*X per step, zero-insertion
                work excluded) over the K timed steps, wall clock between two
-               device synchronisations;
+               device synchronisations; the K calls are captured once in a HIP
+               graph and replayed (cbd_run launches kernels only), or with
+               --no-graph issued one by one;
   roofline     dominant kernel: algorithmic flops (or bytes) per launch divided
                by its mean launch duration from HIP events recorded on the
-               launch stream, against the bf16 dense MFMA peak (or HBM);
+               launch stream (around the replay / K, or around each call),
+               against the bf16 dense MFMA peak (or HBM);
                `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE +
                WRITE_SIZE (profiles/, scaled by a plain copy of known size),
                null when the kernel source changed after the counters were taken;
@@ -160,6 +163,9 @@ def main():
     ap.add_argument("--rows-per-wg", type=int, default=0,
                     help="grouped problems: output rows per workgroup of the pipelined row "
                          "kernel (0 automatic, -1 the one-row kernel)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="time the calls issued one by one on the stream instead of replayed "
+                         "from a captured HIP graph")
     ap.add_argument("--ksplit", type=int, default=0,
                     help="large-tile kernel: split each tile's K loop over this many workgroups "
                          "(f32 workspace + finalising kernel)")
@@ -230,19 +236,52 @@ def main():
         cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: the K calls captured once in a HIP graph and replayed
+    # (the calls launch kernels only, so they capture; no host launch cost
+    # between steps), or with --no-graph issued one by one on the stream,
+    # each between its own event pair.
+    graph = None
+    timing = "stream"
+    if args.graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                cbd.run(pl, dy_d, w_d, dx_d, stream=cap, workspace=ws)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=cap):
+                    for _ in range(args.steps):
+                        cbd.run(pl, dy_d, w_d, dx_d, stream=cap, workspace=ws)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            timing = f"hip graph of {args.steps} calls"
+        except Exception as e:  # capture unsupported here: time on the stream
+            graph = None
+            timing = f"stream (graph capture failed: {type(e).__name__})"
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    if graph is not None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     step_s = wall / args.steps
-    launch_s = float(np.mean(launch_ms)) / 1e3
 
     flops = info.useful_flops
     alg_bytes = algorithmic_bytes(p, info)
@@ -275,6 +314,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 / Box-Muller operands, no dataset)",
         "config": {"workload": describe(p), "problem": p.name,
                    "form": "zero-insertion (no residue split)" if args.no_split else "residue split",
+                   "timing": timing,
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
                    "rows_per_wg": info.rows_per_wg, "cols_per_wg": info.cols_per_wg,
