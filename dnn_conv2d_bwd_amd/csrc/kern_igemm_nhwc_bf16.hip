@@ -183,10 +183,13 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     b_chunk[i] = (uint32_t)(((lane & 3) ^ swz_y(b_row[i])) * 16);
   }
 
-  // Running load offsets of the next tile to load, one set per operand.
-  // Tiles past the end load with an out-of-range scalar offset (zeros into
-  // a stage that is no longer read), which keeps the count of loads in
-  // flight the same on every tile.
+  // Next tile to load, per operand: a vector offset per lane that stays
+  // fixed within a tap, plus a running scalar offset (the k rows of the
+  // tile within its tap), so the per-tile step is one scalar add with no
+  // vector instruction between the MFMAs.  Tiles past the end load through
+  // a buffer descriptor whose record count is 0 (zeros into a stage that is
+  // no longer read), which keeps the count of loads in flight the same on
+  // every tile.
   const uint32_t a_step = (uint32_t)BK * wrow, b_step = (uint32_t)BK * 2u;
   // First tile kb: tap kb / kpt, k tile kb mod kpt within it.
   const int tap0 = __builtin_amdgcn_readfirstlane(kb / kpt);
@@ -194,9 +197,12 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    a_off[i] = a_lane[i] + atab[tap0] + r0 * a_step;
-    b_off[i] = gtab[tap0 * BN + b_row[i]] + b_chunk[i] + r0 * b_step;
+    a_off[i] = a_lane[i] + atab[tap0];
+    b_off[i] = gtab[tap0 * BN + b_row[i]] + b_chunk[i];
   }
+  uint32_t a_soff = __builtin_amdgcn_readfirstlane(r0 * a_step);
+  uint32_t b_soff = __builtin_amdgcn_readfirstlane(r0 * b_step);
+  uint32_t a_rec = a.w_bytes, b_rec = a.dy_bytes;  // record counts of the next tile's loads
   // Tile t = (tap, k tile) with tap = t / kpt, by multiply-high with a
   // rounded-up reciprocal (exact for t < 17 kpt, kpt <= 4096: tiles per
   // class are at most 16 kpt, plus the 4 tiles loaded past the end).
@@ -204,32 +210,31 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     if constexpr (SKPT > 0) return t / SKPT;
     return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic);
   };
-  uint32_t a_soff = 0, b_soff = 0;
-  // Move a set of offsets from tile t-1 to tile t: one add per lane offset,
-  // except where a new tap starts (uniform branch, once per kpt tiles).
-  // Offsets of tiles past the end are never used to read live data.
+  // With one tap per class every tile of [kb, ke) belongs to it.
+  constexpr bool ONE_TAP = STAPS == 1;
+  // Move the offsets of an operand from tile t-1 to tile t (a uniform
+  // branch where a new tap starts, once per kpt tiles).
   auto advance_a = [&](int t) {
-    const int tap = tap_of(t);
-    if (t - tap * kpt == 0 && t < ke) {
-      const uint32_t base = atab[tap];
+    if (!ONE_TAP && t < ke && t - tap_of(t) * kpt == 0) {
+      const uint32_t base = atab[tap_of(t)];
 #pragma unroll
       for (int i = 0; i < 4; i++) a_off[i] = a_lane[i] + base;
+      a_soff = 0;
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; i++) a_off[i] += a_step;
+      a_soff += a_step;
     }
-    a_soff = t < ke ? 0u : dev::kOOB;
+    a_rec = t < ke ? a.w_bytes : 0u;
   };
   auto advance_b = [&](int t) {
-    const int tap = tap_of(t);
-    if (t - tap * kpt == 0 && t < ke) {
+    if (!ONE_TAP && t < ke && t - tap_of(t) * kpt == 0) {
+      const int tap = tap_of(t);
 #pragma unroll
       for (int i = 0; i < 4; i++) b_off[i] = gtab[tap * BN + b_row[i]] + b_chunk[i];
+      b_soff = 0;
     } else {
-#pragma unroll
-      for (int i = 0; i < 4; i++) b_off[i] += b_step;
+      b_soff += b_step;
     }
-    b_soff = t < ke ? 0u : dev::kOOB;
+    b_rec = t < ke ? a.dy_bytes : 0u;
   };
   // Load j of a tile (j < 4: W, else dY): 64 lanes x 16 bytes, global ->
   // LDS without VGPRs (buffer_load ... lds; lane l writes 16 bytes at
@@ -237,40 +242,37 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // own conservative vmcnt waits before fragment reads of other stages: the
   // waits that order these loads against LDS reads are the explicit ones in
   // the main loop and before the epilogue.  The destination stage is a
-  // compile-time constant and M0 a scalar sum.
-  const uint32_t wbase = __builtin_amdgcn_readfirstlane((uint32_t)wave * 4096u);
+  // compile-time constant, so M0 is this wave's base (a scalar register)
+  // plus an immediate.  Nothing else in this kernel uses M0.
   const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_char*)smem;
-  auto issue_one = [&](auto dstc, int j) {
-    constexpr int DS = decltype(dstc)::value;
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        smem_base + wbase + (uint32_t)(j < 4 ? DS * ABYTES + j * 1024 : BBASE + DS * BBYTES + (j - 4) * 1024));
-    const uint32_t voff = j < 4 ? a_off[j] : b_off[j - 4];
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(j < 4 ? a_soff : b_soff);
-    const i32x4 desc = j < 4 ? dw : dyd;
-    // M0 is listed as clobbered; nothing else in this kernel uses M0.
+  const uint32_t mbase = __builtin_amdgcn_readfirstlane(smem_base + (uint32_t)wave * 4096u);
+  auto m0_of = [&](int ds, int j) -> uint32_t {
+    return mbase + (uint32_t)(j < 4 ? ds * ABYTES + j * 1024 : BBASE + ds * BBYTES + (j - 4) * 1024);
+  };
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+  auto issue_one = [&](auto dstc, int j) {
+    constexpr int DS = decltype(dstc)::value;
+    const uint32_t m0v = m0_of(DS, j);
+    const uint32_t voff = j < 4 ? a_off[j] : b_off[j - 4];
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(j < 4 ? a_soff : b_soff);
+    const i32x4 desc = j < 4 ? i32x4{dw[0], dw[1], (int)a_rec, dw[3]} : i32x4{dyd[0], dyd[1], (int)b_rec, dyd[3]};
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_nop 0"
                  :: "s"(m0v), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
-#pragma clang diagnostic pop
   };
   // The same load split in two: M0 is written one MFMA ahead of the load
   // that reads it, which covers the M0 -> LDS-load wait state without an
-  // s_nop.  Nothing else writes M0 in between (nothing else in this kernel
-  // uses M0).
+  // s_nop.
   auto set_m0 = [&](auto dstc, int j) {
     constexpr int DS = decltype(dstc)::value;
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        smem_base + wbase + (uint32_t)(j < 4 ? DS * ABYTES + j * 1024 : BBASE + DS * BBYTES + (j - 4) * 1024));
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+    const uint32_t m0v = m0_of(DS, j);
     asm volatile("s_mov_b32 m0, %0" :: "s"(m0v) : "memory", "m0");
-#pragma clang diagnostic pop
   };
+#pragma clang diagnostic pop
   auto load_m0 = [&](int j) {
     const uint32_t voff = j < 4 ? a_off[j] : b_off[j - 4];
     const uint32_t soff = __builtin_amdgcn_readfirstlane(j < 4 ? a_soff : b_soff);
-    const i32x4 desc = j < 4 ? dw : dyd;
+    const i32x4 desc = j < 4 ? i32x4{dw[0], dw[1], (int)a_rec, dw[3]} : i32x4{dyd[0], dyd[1], (int)b_rec, dyd[3]};
     asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" :: "v"(voff), "s"(desc), "s"(soff) : "memory");
   };
 
