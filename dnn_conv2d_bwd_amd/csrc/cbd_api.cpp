@@ -97,6 +97,7 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
         cbd::GemmArgs c = a;
         c.sub[0] = a.sub[i];
         c.sub[0].tile_begin = 0;
+        c.class_begin[0] = 0;
         c.num_sub = 1;
         c.total_tiles = (int32_t)plan->subs[i].tiles;
         err = launch_main(c, plan->subs[i].tiles);

@@ -42,9 +42,8 @@ __device__ inline uint32_t bf16_pack2(float lo, float hi) {
 // contiguous logical range [x*q + min(x, r), ...), so neighbouring tiles --
 // which share operand panels -- meet in one L2.
 __device__ inline int logical_tile(int b, int total, int remap) {
-  if (!remap) return b;
-  int q = total >> 3, r = total & 7, x = b & 7, idx = b >> 3;
-  return x * q + (x < r ? x : r) + idx;
+  const int q = total >> 3, r = total & 7, x = b & 7, idx = b >> 3;
+  return remap ? x * q + (x < r ? x : r) + idx : b;
 }
 
 // Logical block of hardware workgroup b for the grouped row kernels:
@@ -110,11 +109,29 @@ __device__ inline void zero_item(__amdgpu_buffer_rsrc_t rdx, int layout, int esi
   }
 }
 
-// Class owning logical tile t (tile_begin ascends with the class index).
+// Touch every 64-byte line of the kernel arguments that a GEMM workgroup
+// reads (the header lines, the class table and the first two class
+// descriptors) in one batch at entry.  The first access to each line misses
+// the scalar cache; fetched at their first uses, which depend on one
+// another (tile -> class -> descriptor), the misses would be paid one round
+// trip at a time.
+__device__ inline void prefetch_args(const GemmArgs& a) {
+  const int h0 = a.N, h1 = a.num_sub, h2 = a.class_begin[1], h3 = a.class_begin[15];
+  const int h4 = a.sub[0].phase_h, h5 = a.sub[1].tile_begin;
+  const void* p0 = a.dy;
+  const void* p1 = a.dx;
+  asm volatile("" ::"s"(h0), "s"(h1), "s"(h2), "s"(h3), "s"(h4), "s"(h5), "s"(p0), "s"(p1));
+}
+
+// Class owning logical tile t (class_begin ascends with the class index):
+// the number of classes after the first that begin at or before t.  The
+// first 16 entries are read unconditionally (one batch of scalar loads).
 __device__ inline int find_class(const GemmArgs& a, int t) {
+  const int ns = a.num_sub;
   int r = 0;
-  for (int i = 1; i < a.num_sub; i++)
-    if (a.sub[i].tile_begin <= t) r = i;
+#pragma unroll
+  for (int i = 1; i < 16; i++) r += (i < ns && a.class_begin[i] <= t) ? 1 : 0;
+  for (int i = 16; i < ns; i++) r += a.class_begin[i] <= t ? 1 : 0;
   return r;
 }
 

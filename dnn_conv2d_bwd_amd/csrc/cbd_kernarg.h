@@ -75,8 +75,13 @@ struct GemmArgs {
   const void* w;
   void* dx;
   FusedZero fz;
+  // tile_begin of every class again, contiguous: a kernel finds its class
+  // from one batch of scalar loads instead of one load per class.
+  int32_t class_begin[kMaxSub];
   SubDesc sub[kMaxSub];
 };
+// Kernel arguments travel in the 4 KiB kernel-argument segment.
+static_assert(sizeof(GemmArgs) <= 4096, "GemmArgs exceeds the kernel-argument segment");
 
 
 struct ZeroArgs {

@@ -432,12 +432,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   bool static_shape = false;
   {
     bool ok = kernel == CBD_KERNEL_NHWC_BF16 && ksplit == 1 && Kg == 64 * cbd::kFastBK &&
-              !subs.empty();
+              !no_split && !subs.empty();
     for (const auto& s : subs) ok = ok && s.taps_h * s.taps_w == 1;
     if (static_mode == 1 && !ok) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this problem "
-                                       "(built: NHWC bf16, K/G = 2048, one tap per class, no split)");
+                                       "(built: NHWC bf16, K/G = 2048, one tap per class, residue split, "
+                                       "no K split)");
     }
     static_shape = ok && static_mode >= 0;
   }
@@ -532,6 +533,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     d.cls_h = s.class_h; d.cls_w = s.class_w;
     d.pos_h = (int32_t)s.pos_h; d.pos_w = (int32_t)s.pos_w;
     d.tile_begin = (int32_t)s.tile_begin;
+    a.class_begin[i] = d.tile_begin;
   }
 
   cbd::ZeroArgs& z = pl->zero;

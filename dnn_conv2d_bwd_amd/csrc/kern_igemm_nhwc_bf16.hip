@@ -97,6 +97,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 128-position half
 
+  dev::prefetch_args(a);
   const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   const int npix_img = s.pos_h * s.pos_w;
@@ -138,31 +139,44 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   asm volatile("" : "+s"(KT));
   const uint32_t kpt_magic = __builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)kpt + 1u);
 
-  // ---- per-workgroup tables (threads 0..255: one position row each)
-  if (tid < BN) {
-    const int p = n0 + tid;
-    const bool pv = p < npos;
-    const int pp = pv ? p : 0;
-    const int n = pp / npix_img;
-    const int rr = pp - n * npix_img;
-    const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
-    for (int tap = 0; tap < ntaps; tap++) {
-      const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
-      const int ho = dev::dy_index(a.no_split, th, s.beta_h, a.delta_h, jh, a.pad_h, a.dil_h, a.str_h);
-      const int wo = dev::dy_index(a.no_split, tw, s.beta_w, a.delta_w, jw, a.pad_w, a.dil_w, a.str_w);
-      const bool ok = pv && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
-      gtab[tap * BN + tid] = ok ? (uint32_t)(((n * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg) * 2u : dev::kOOB;
-    }
-    const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
-    otab[tid] = pv ? (uint32_t)(((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg + m0) * 2u : dev::kOOB;
-  }
-  if (tid < ntaps) {
-    const int jh = tid / s.taps_w, jw = tid - (tid / s.taps_w) * s.taps_w;
-    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-    atab[tid] = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
-  }
-  __syncthreads();
+  // With one tap per class (the shape-specialised instance) every tile of
+  // [kb, ke) belongs to tap 0, whose load offsets each lane computes itself:
+  // the first loads then go out before any table is built.
+  constexpr bool ONE_TAP = STAPS == 1;
 
+  // ---- per-workgroup tables (threads 0..255: one position row each): the
+  // dY offsets of every tap (not needed with one tap), the dX offsets, and
+  // the W offset of every tap.
+  auto build_tables = [&]() {
+    if (tid < BN) {
+      const int p = n0 + tid;
+      const bool pv = p < npos;
+      const int pp = pv ? p : 0;
+      const int n = pp / npix_img;
+      const int rr = pp - n * npix_img;
+      const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
+      if constexpr (!ONE_TAP) {
+        for (int tap = 0; tap < ntaps; tap++) {
+          const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
+          const int ho = dev::dy_index(a.no_split, th, s.beta_h, a.delta_h, jh, a.pad_h, a.dil_h, a.str_h);
+          const int wo = dev::dy_index(a.no_split, tw, s.beta_w, a.delta_w, jw, a.pad_w, a.dil_w, a.str_w);
+          const bool ok = pv && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
+          gtab[tap * BN + tid] = ok ? (uint32_t)(((n * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg) * 2u : dev::kOOB;
+        }
+      }
+      const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
+      otab[tid] = pv ? (uint32_t)(((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg + m0) * 2u : dev::kOOB;
+    }
+    if (!ONE_TAP && tid < ntaps) {
+      const int jh = tid / s.taps_w, jw = tid - (tid / s.taps_w) * s.taps_w;
+      const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+      atab[tid] = (uint32_t)(((g * a.Kg) * YX + ty * a.X + tx) * a.Cg) * 2u;
+    }
+  };
+  if constexpr (!ONE_TAP) {
+    build_tables();
+    __syncthreads();
+  }
 
   // ---- load roles.  W: instruction i (0..3) of wave w fills k rows
   // 8w + 2i + (lane >> 5), 16-byte slot lane & 31 holding channel chunk
@@ -195,10 +209,38 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int tap0 = __builtin_amdgcn_readfirstlane(kb / kpt);
   const uint32_t r0 = (uint32_t)(kb - tap0 * kpt);
   uint32_t a_off[4], b_off[4];
+  if constexpr (ONE_TAP) {
+    // Tap 0 of the class (taps y = cls_h, x = cls_w; dY row t + beta).
+    // Position p = (n, th, tw) by multiply-high with m = ceil(2^32 / d):
+    // the estimate is q or q + 1 for every x < 2^32 and one compare fixes it.
+    const uint32_t npix = (uint32_t)npix_img, posw = (uint32_t)s.pos_w;
+    const uint32_t mpix = __builtin_amdgcn_readfirstlane(0xffffffffu / npix + 1u);
+    const uint32_t mw = __builtin_amdgcn_readfirstlane(0xffffffffu / posw + 1u);
+    auto udiv = [](uint32_t x, uint32_t d, uint32_t m) -> uint32_t {
+      const uint32_t q = __umulhi(x, m);
+      return d == 1u ? x : (q * d > x ? q - 1u : q);
+    };
+    const uint32_t abase = (uint32_t)(((g * a.Kg) * YX + s.cls_h * a.X + s.cls_w) * a.Cg) * 2u;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    a_off[i] = a_lane[i] + atab[tap0];
-    b_off[i] = gtab[tap0 * BN + b_row[i]] + b_chunk[i];
+    for (int i = 0; i < 4; i++) {
+      a_off[i] = a_lane[i] + abase;
+      const int p = n0 + b_row[i];
+      const bool pv = p < npos;
+      const uint32_t pp = pv ? (uint32_t)p : 0u;
+      const uint32_t n = udiv(pp, npix, mpix);
+      const uint32_t rr = pp - n * npix;
+      const uint32_t th = udiv(rr, posw, mw);
+      const int ho = (int)th + s.beta_h, wo = (int)(rr - th * posw) + s.beta_w;
+      const bool ok = pv && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
+      b_off[i] = ok ? (uint32_t)((((int)n * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg) * 2u + b_chunk[i]
+                    : dev::kOOB;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      a_off[i] = a_lane[i] + atab[tap0];
+      b_off[i] = gtab[tap0 * BN + b_row[i]] + b_chunk[i];
+    }
   }
   uint32_t a_soff = __builtin_amdgcn_readfirstlane(r0 * a_step);
   uint32_t b_soff = __builtin_amdgcn_readfirstlane(r0 * b_step);
@@ -210,8 +252,6 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     if constexpr (SKPT > 0) return t / SKPT;
     return kpt == 1 ? t : (int)__umulhi((uint32_t)t, kpt_magic);
   };
-  // With one tap per class every tile of [kb, ke) belongs to it.
-  constexpr bool ONE_TAP = STAPS == 1;
   // Move the offsets of an operand from tile t-1 to tile t (a uniform
   // branch where a new tap starts, once per kpt tiles).
   auto advance_a = [&](int t) {
@@ -365,7 +405,10 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   advance_b(kb + 3);
 #pragma unroll
   for (int j = 0; j < DMA_PER_TILE / 2; j++) issue_one(std::integral_constant<int, 3>(), j);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NSTAGE - 2) * DMA_PER_TILE + DMA_PER_TILE / 2));
+  // One tap: the dX offsets are built while the first tiles are in flight
+  // (the wait below also completes their LDS writes).
+  if constexpr (ONE_TAP) build_tables();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE + DMA_PER_TILE / 2));
   __builtin_amdgcn_s_barrier();
   bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
 #pragma unroll
