@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_direct_kernel(const G
   constexpr int VB = CG * ES;  // bytes of one group's channels at one position
   constexpr int MT = kGroupedMaxTaps;
 
+  dev::prefetch_args(a);
   const int tid = threadIdx.x;
   const int G = a.G;
   const int g = tid % G;

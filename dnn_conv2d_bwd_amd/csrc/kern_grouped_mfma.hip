@@ -205,6 +205,7 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
 template <int G>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_mfma_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
+  dev::prefetch_args(a);
   const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   // (image, row block, column block), column blocks innermost

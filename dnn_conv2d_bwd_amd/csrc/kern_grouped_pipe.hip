@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_pipe_kernel(const Gem
   extern __shared__ __attribute__((aligned(16))) char ring[];
   constexpr int ES = DT == 0 ? 4 : 2;
 
+  dev::prefetch_args(a);
   PipeCtx q;
   const int tid = threadIdx.x;
   q.lane = tid & 63;

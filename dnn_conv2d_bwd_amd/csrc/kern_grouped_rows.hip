@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_rows_kernel(const Gem
   constexpr int MT = kGroupedMaxTaps;
   constexpr bool DOT2 = DT == 1 && CG >= 2;
 
+  dev::prefetch_args(a);
   const int tid = threadIdx.x;
   const int G = a.G;
   const int g = tid & (G - 1);

@@ -213,6 +213,7 @@ template <int CG, bool PAIR8>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_wide_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   constexpr int GB = SB / ((PAIR8 ? 8 : CG) * 2);  // the problem's groups per workgroup
+  dev::prefetch_args(a);
   const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
   const SubDesc s = a.sub[dev::find_class(a, t)];
   // (image, row block, group block, column block), column blocks innermost

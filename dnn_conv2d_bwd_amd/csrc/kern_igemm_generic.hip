@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
   __shared__ float lds[LDSF];
 
+  dev::prefetch_args(a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
 
