@@ -24,7 +24,16 @@ Prints ONE JSON line:
                WRITE_SIZE (profiles/, scaled by a plain copy of known size),
                null when the kernel source changed after the counters were taken;
   cpu_baseline the CPU oracle on the host cores over a bounded random sample of
-               the same problem's outputs, scaled to TFLOP/s.
+               the same problem's outputs, scaled to TFLOP/s, with the parity
+               of the GPU's dX at those elements against the oracle (relative
+               L2, max error, bf16 ulps, exact zeros; `pass` applies the fp32 or
+               bf16 tolerance);
+  machine      GPU name and architecture, HIP version, maximum shader clock,
+               host CPU model.
+
+    python bench.py --all      one line per workload problem: warm, graph and
+                               cold (caches flushed) us/call, roofline fractions,
+                               and the same sampled oracle check (about 1 s each).
 """
 from __future__ import annotations
 
@@ -103,8 +112,11 @@ def read_traffic(key, problem):
         return None
 
 
-def cpu_baseline(p, dy, w, info, target_s):
-    """Oracle over a bounded random sample of output elements, scaled."""
+def cpu_baseline(p, dy, w, info, target_s, dx_gpu=None):
+    """Oracle over a bounded random sample of output elements, timed and
+    scaled to the whole problem.  Given the GPU's dX (host array in the
+    layout's memory order), also the parity of the GPU result at the same
+    elements (sample_parity)."""
     import numpy as np
 
     import oracle
@@ -125,14 +137,74 @@ def cpu_baseline(p, dy, w, info, target_s):
     count = int(min(total, max(probe, probe * target_s / max(dt, 1e-6))))
     pts = points(count)
     t0 = time.perf_counter()
-    oracle.bwd_data_at(p, dy64, w64, pts)
+    ref = oracle.bwd_data_at(p, dy64, w64, pts)
     dt = time.perf_counter() - t0
     flops = info.useful_flops * count / total
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{count} random dX elements of {total} ({count / total:.2%}), "
-                      f"fp64 gather per element, {dt:.2f} s; useful flops scaled by the "
-                      f"sampled fraction"}
+    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": oracle.num_threads(), "kind": "oracle", "oracle_s": round(dt, 3),
+           "sample": f"{count} random dX elements of {total} ({count / total:.2%}), "
+                     f"fp64 gather per element, {dt:.2f} s; useful flops scaled by the "
+                     f"sampled fraction"}
+    if dx_gpu is not None:
+        out["parity"] = sample_parity(p, pts, ref, dx_gpu)
+    return out
+
+
+def sample_parity(p, pts, ref64, dx_gpu):
+    """The GPU's dX against the oracle at the sampled elements.
+    fp32: relative L2 <= 1e-5 and max |err| <= 1e-4 max |ref|.  bf16: relative
+    L2 <= 8e-3 and every element within 2 bf16 ulps of the oracle rounded to
+    f32 then bf16, ulps counted at magnitude max(|ref|, 2^-10 rms(ref))
+    (floored) and at |ref| itself (strict, reported only).  Elements whose
+    oracle value is exactly 0 (unreached or edge positions) must be exactly 0."""
+    import numpy as np
+
+    import oracle
+
+    n, c, h, w_ = pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]
+    got = (dx_gpu[n, c, h, w_] if p.layout == 0 else dx_gpu[n, h, w_, c]).astype(np.float64)
+    ref32 = oracle.round_f32(ref64).astype(np.float64)
+    norm = float(np.linalg.norm(ref64))
+    rel_l2 = float(np.linalg.norm(got - ref64) / norm) if norm > 0 else float(np.abs(got).max())
+    max_ref = float(np.abs(ref64).max())
+    max_abs = float(np.abs(got - ref64).max())
+    zeros_ok = bool(np.all(got[ref64 == 0.0] == 0.0))
+    res = {"elements": int(len(ref64)), "rel_l2": rel_l2, "max_abs": max_abs, "max_ref": max_ref,
+           "zeros_ok": zeros_ok}
+    if p.dtype == "f32":
+        ok = rel_l2 <= 1e-5 and max_abs <= 1e-4 * max_ref
+    else:
+        rb = oracle.bf16_bits_to_f32(oracle.round_bf16_bits(ref32.astype(np.float32))).astype(np.float64)
+        rms = float(np.sqrt(np.mean(ref32 ** 2)))
+
+        def ulps(mag):
+            e = np.floor(np.log2(np.maximum(mag, np.finfo(np.float32).tiny)))
+            return np.abs(got - rb) / np.exp2(e - 7)
+        floored = ulps(np.maximum(np.abs(ref32), 2.0 ** -10 * rms))
+        strict = ulps(np.abs(ref32))
+        res.update({"ulp_max": float(floored.max()), "ulp_viol_floored": int((floored > 2).sum()),
+                    "ulp_viol_strict": int((strict > 2).sum())})
+        ok = rel_l2 <= 8e-3 and res["ulp_viol_floored"] == 0
+    res["pass"] = bool(ok and zeros_ok)
+    return res
+
+
+def machine():
+    """GPU name, HIP version, shader clock and host CPU model."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"gpu_name": torch.cuda.get_device_name(0), "gcn_arch": getattr(props, "gcnArchName", ""),
+            "hip_version": torch.version.hip, "sclk_max_mhz": getattr(props, "clock_rate", 0) // 1000,
+            "cpu_model": cpu, "host_cpus": os.cpu_count()}
 
 
 def copy_calibration(nbytes, reps):
@@ -325,9 +397,11 @@ def main():
                    "alg_mbytes": round(alg_bytes / 1e6, 3)},
         "roofline": roof,
         "gpu": torch.cuda.get_device_name(0) or "gfx950",
+        "machine": machine(),
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds,
+                                           dx_gpu=dx_d.float().cpu().numpy())
     print(json.dumps(out), flush=True)
 
 
@@ -384,6 +458,7 @@ def all_problems(args):
 
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    mach = machine()
     for p in PROBLEMS:
         dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
         pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
@@ -391,8 +466,10 @@ def all_problems(args):
         info = pl.info()
         sh = pl.shapes()
         tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
-        dy_d = torch.from_numpy(draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)).to(tdt).cuda()
-        w_d = torch.from_numpy(draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)).to(tdt).cuda()
+        dy_h = draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)
+        w_h = draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)
+        dy_d = torch.from_numpy(dy_h).to(tdt).cuda()
+        w_d = torch.from_numpy(w_h).to(tdt).cuda()
         dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
         for _ in range(10):
             cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
@@ -445,8 +522,12 @@ def all_problems(args):
             unit = "TFLOP/s"
             ach = lambda us: flops / us / 1e6
         med = float(np.median(cold))
-        print(json.dumps({
-            "problem": p.name, "workload": describe(p), "kernel": KERNEL_SYMBOL[kernel_key(info)],
+        line = {
+            "problem": p.name, "workload": describe(p), "dtype": p.dtype,
+            "layout": "NCHW/KCYX" if p.layout == 0 else "NHWC/KYXC",
+            "shape": {"dx": list(sh["dx"]), "dy": list(sh["dy"]), "w": list(sh["w"])},
+            "seed": {"dy": seed_for(p, "dy"), "w": seed_for(p, "w")},
+            "kernel": KERNEL_SYMBOL[kernel_key(info)],
             "launches": info.launches, "grid": info.grid_main,
             "useful_gflop": round(flops / 1e9, 5), "executed_gmac": round(info.executed_macs / 1e9, 5),
             "alg_mbytes": round(nbytes / 1e6, 3),
@@ -458,8 +539,17 @@ def all_problems(args):
             "achieved_warm": round(ach(warm), 2), "achieved_graph": round(ach(us_graph), 2),
             "achieved_cold": round(ach(med), 2), "unit": unit, "peak": peak,
             "frac_warm": round(ach(warm) / peak, 4), "frac_graph": round(ach(us_graph) / peak, 4),
-            "frac_cold": round(ach(med) / peak, 4)}),
-            flush=True)
+            "frac_cold": round(ach(med) / peak, 4)}
+        if args.cpu_seconds > 0:
+            # The oracle on a bounded sample of this problem's dX (about a
+            # second each), and the GPU result's parity at those elements.
+            cb = cpu_baseline(p, dy_h, w_h, info, min(args.cpu_seconds, 1.0),
+                              dx_gpu=dx_d.float().cpu().numpy())
+            line.update({"oracle_s": cb["oracle_s"], "oracle_threads": cb["cores"],
+                         "oracle_tflops": cb["value"], "oracle_sample": cb["sample"],
+                         "parity": cb["parity"]})
+        line.update(mach)
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
