@@ -69,36 +69,42 @@ __device__ inline int dy_index(int no_split, int t, int beta, int delta, int j, 
   return (num >= 0 && num % str == 0) ? num / str : -1;
 }
 
+// x / d for 32-bit x, with mag = ceil(2^32 / d) (0 for d = 1): the
+// multiply-high estimate is the quotient or one more, and one compare fixes it.
+__device__ inline uint32_t fdiv(uint32_t x, uint32_t d, uint32_t mag) {
+  const uint32_t q = __umulhi(x, mag);
+  return d == 1u ? x : (q * d > x ? q - 1u : q);
+}
+
 // Zero-fill work item `item` (regions reg[0..nreg), item_begin ascending):
 // one element (NCHW, or NHWC rows not a multiple of 16 bytes) or one
 // 16-byte chunk of an NHWC pixel row of an unreached dX phase lattice.
+// Item counts stay below 2^32 and dX below 2^31 bytes (the planner's
+// limits), so the arithmetic is 32-bit.
 __device__ inline void zero_item(__amdgpu_buffer_rsrc_t rdx, int layout, int esize, int chunk, int C,
                                  int Hi, int Wi, int Sh, int Sw, const ZeroDesc* reg, int nreg,
-                                 int64_t item) {
+                                 uint32_t item) {
   int r = 0;
   for (int i = 1; i < nreg; i++)
-    if (reg[i].item_begin <= item) r = i;
-  const ZeroDesc d = reg[r];
-  int64_t li = item - d.item_begin;
+    if ((uint32_t)reg[i].item_begin <= item) r = i;
+  const ZeroDesc& d = reg[r];
+  uint32_t li = item - (uint32_t)d.item_begin;
   uint32_t off;
+  uint32_t cidx = 0;
   if (layout == 1) {
-    const int64_t per_pos = (int64_t)C * esize / chunk;
-    const int64_t cidx = li % per_pos;
-    int64_t pos = li / per_pos;
-    const int64_t b = pos % d.pos_w;
-    pos /= d.pos_w;
-    const int64_t a = pos % d.pos_h;
-    const int64_t n = pos / d.pos_h;
-    const int64_t hi = d.phase_h + (int64_t)Sh * a, wi = d.phase_w + (int64_t)Sw * b;
-    off = (uint32_t)((((n * Hi + hi) * Wi + wi) * C) * esize + cidx * chunk);
-  } else {
-    const int64_t b = li % d.pos_w;
-    li /= d.pos_w;
-    const int64_t a = li % d.pos_h;
-    const int64_t nc = li / d.pos_h;
-    const int64_t hi = d.phase_h + (int64_t)Sh * a, wi = d.phase_w + (int64_t)Sw * b;
-    off = (uint32_t)(((nc * Hi + hi) * Wi + wi) * esize);
+    const uint32_t pos = fdiv(li, d.per_pos, d.mag_pp);
+    cidx = li - pos * d.per_pos;
+    li = pos;
   }
+  const uint32_t q = fdiv(li, (uint32_t)d.pos_w, d.mag_w);
+  const uint32_t b = li - q * (uint32_t)d.pos_w;
+  const uint32_t nc = fdiv(q, (uint32_t)d.pos_h, d.mag_h);  // n (NHWC) or n*C + c (NCHW)
+  const uint32_t a = q - nc * (uint32_t)d.pos_h;
+  const uint32_t hi = (uint32_t)d.phase_h + (uint32_t)Sh * a, wi = (uint32_t)d.phase_w + (uint32_t)Sw * b;
+  if (layout == 1)
+    off = (((nc * (uint32_t)Hi + hi) * (uint32_t)Wi + wi) * (uint32_t)C) * (uint32_t)esize + cidx * (uint32_t)chunk;
+  else
+    off = ((nc * (uint32_t)Hi + hi) * (uint32_t)Wi + wi) * (uint32_t)esize;
   if (chunk == 16) {
     typedef uint32_t u4z __attribute__((ext_vector_type(4)));
     __builtin_amdgcn_raw_buffer_store_b128(u4z{0u, 0u, 0u, 0u}, rdx, off, 0, 0);

@@ -24,9 +24,14 @@ struct SubDesc {
 };
 
 // One dX phase lattice (phase_h + Sh*a, phase_w + Sw*b) that no tap reaches.
+// Divisions by pos_w, pos_h and per_pos (16-byte chunks per NHWC pixel row)
+// go through rounded-up reciprocals mag = ceil(2^32 / d) (0 when d = 1):
+// umulhi(x, mag) is x / d or one more for every 32-bit x.
 struct ZeroDesc {
   int32_t phase_h, phase_w;
   int32_t pos_h, pos_w;
+  uint32_t mag_h, mag_w;
+  uint32_t per_pos, mag_pp;
   int64_t item_begin;  // first work item of this region
 };
 

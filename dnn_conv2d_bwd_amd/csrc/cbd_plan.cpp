@@ -38,6 +38,10 @@ int64_t gcd64(int64_t a, int64_t b) {
   return a;
 }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ceil(2^32 / d) for the kernels' multiply-high division (0 for d = 1,
+// which the kernels take as the identity).
+uint32_t magic32(int64_t d) { return d <= 1 ? 0u : (uint32_t)((uint64_t(1) << 32) / (uint64_t)d + ((uint64_t(1) << 32) % (uint64_t)d != 0)); }
 int64_t pos_mod(int64_t a, int64_t m) {
   int64_t r = a % m;
   return r < 0 ? r + m : r;
@@ -550,6 +554,10 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     d.phase_h = zeros[i].phase_h; d.phase_w = zeros[i].phase_w;
     d.pos_h = (int32_t)zeros[i].pos_h; d.pos_w = (int32_t)zeros[i].pos_w;
     d.item_begin = items;
+    d.per_pos = (uint32_t)(p.layout == CBD_LAYOUT_NHWC ? p.c * es / z.chunk : 1);
+    d.mag_h = magic32(d.pos_h);
+    d.mag_w = magic32(d.pos_w);
+    d.mag_pp = magic32(d.per_pos);
     const int64_t npos = p.n * zeros[i].pos_h * zeros[i].pos_w;
     items += p.layout == CBD_LAYOUT_NHWC ? npos * (p.c * es / z.chunk) : npos * p.c;
     zero_elems += npos * p.c;
@@ -562,7 +570,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
 
   // Generic family with few zero regions: fold the zero-fill into the main
   // launch as extra workgroups (one launch instead of two).
-  int64_t grid_zero = ceil_div(items, cbd::kZeroThreads);
+  int64_t grid_zero = ceil_div(items, int64_t(cbd::kZeroThreads) * cbd::kZeroItemsPerThread);
   int64_t grid_main = tile;
   std::memset(&a.fz, 0, sizeof(a.fz));
   if (kernel == CBD_KERNEL_GENERIC && !per_class && items > 0 &&

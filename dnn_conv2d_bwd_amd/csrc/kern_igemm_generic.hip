@@ -77,10 +77,16 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
 
   if ((int)blockIdx.x >= a.total_tiles) {  // zero-fill folded into this launch
     const FusedZero& z = a.fz;
-    const int64_t item = (int64_t)(blockIdx.x - a.total_tiles) * kGenericThreads + tid;
-    if (item < z.total_items)
-      dev::zero_item(dev::rsrc(a.dx, a.dx_bytes), z.layout, z.esize, z.chunk, z.C, z.Hi, z.Wi,
-                     z.Sh, z.Sw, z.reg, z.num_regions, item);
+    const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+    const uint32_t base =
+        (uint32_t)(blockIdx.x - a.total_tiles) * (kGenericThreads * kZeroItemsPerThread) + tid;
+#pragma unroll
+    for (int i = 0; i < kZeroItemsPerThread; i++) {
+      const uint32_t item = base + (uint32_t)(i * kGenericThreads);
+      if ((int64_t)item < z.total_items)
+        dev::zero_item(rdx, z.layout, z.esize, z.chunk, z.C, z.Hi, z.Wi, z.Sh, z.Sw, z.reg,
+                       z.num_regions, item);
+    }
     return;
   }
 

@@ -8,7 +8,9 @@
 // materialised, only the dX lattice is cleared.
 //
 // One work item = one element (NCHW, or NHWC rows whose byte size is not a
-// multiple of 16) or one 16-byte chunk of an NHWC pixel row.
+// multiple of 16) or one 16-byte chunk of an NHWC pixel row; a thread takes
+// kZeroItemsPerThread items, kZeroThreads apart (each store instruction of a
+// wave covers 64 consecutive items).
 #include "cbd_device.h"
 #include "cbd_internal.h"
 
@@ -16,10 +18,15 @@ namespace cbd {
 namespace {
 
 __global__ __launch_bounds__(kZeroThreads) void zero_fill_kernel(const ZeroArgs z) {
-  const int64_t item = (int64_t)blockIdx.x * kZeroThreads + threadIdx.x;
-  if (item >= z.total_items) return;
-  dev::zero_item(dev::rsrc(z.dx, z.dx_bytes), z.layout, z.esize, z.chunk, z.C, z.Hi, z.Wi, z.Sh,
-                 z.Sw, z.reg, z.num_regions, item);
+  const auto rdx = dev::rsrc(z.dx, z.dx_bytes);
+  const uint32_t base = (uint32_t)blockIdx.x * (kZeroThreads * kZeroItemsPerThread) + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kZeroItemsPerThread; i++) {
+    const uint32_t item = base + (uint32_t)(i * kZeroThreads);
+    if ((int64_t)item < z.total_items)
+      dev::zero_item(rdx, z.layout, z.esize, z.chunk, z.C, z.Hi, z.Wi, z.Sh, z.Sw, z.reg,
+                     z.num_regions, item);
+  }
 }
 
 }  // namespace
