@@ -89,16 +89,27 @@ def kernel_key(info):
     return (info.kernel, info.variant)
 
 
+# Headers every kernel source includes: a change in them changes the kernels.
+KERNEL_HEADERS = ("cbd_device.h", "cbd_kernarg.h", "cbd_internal.h")
+
+
+def kernel_digest(key):
+    """sha256 over the kernel's source file followed by the shared headers."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[key],) + KERNEL_HEADERS:
+        h.update(open(os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def read_traffic(key, problem):
     """HBM bytes per launch recorded under profiles/ for this kernel on this
-    problem, if the kernel source still matches the one the counters were
-    taken on."""
-    src = os.path.join(ROOT, "dnn_conv2d_bwd_amd", "csrc", KERNEL_SRC[key])
+    problem, if the kernel source and shared headers still match the ones the
+    counters were taken on."""
     name = KERNEL_SYMBOL[key][:-len("_kernel")]
     path = os.path.join(ROOT, "profiles", f"{name}_{problem}_traffic.txt")
     if not os.path.exists(path):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = kernel_digest(key)
     fields = {}
     for line in open(path):
         if ":" in line:
@@ -202,8 +213,19 @@ def machine():
                 break
     except OSError:
         pass
+    # Highest shader-clock level the driver lists (sysfs), if readable.
+    sclk = None
+    import glob
+    for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            for line in open(f):
+                tok = line.split(":", 1)[-1].strip().split()[0].lower()
+                if tok.endswith("mhz"):
+                    sclk = max(sclk or 0, int(float(tok[:-3])))
+        except (OSError, ValueError, IndexError):
+            pass
     return {"gpu_name": torch.cuda.get_device_name(0), "gcn_arch": getattr(props, "gcnArchName", ""),
-            "hip_version": torch.version.hip, "sclk_max_mhz": getattr(props, "clock_rate", 0) // 1000,
+            "hip_version": torch.version.hip, "sclk_max_mhz": sclk,
             "cpu_model": cpu, "host_cpus": os.cpu_count()}
 
 
