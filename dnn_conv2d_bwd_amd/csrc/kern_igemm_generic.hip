@@ -23,7 +23,7 @@
 // (register double buffer; no workgroup barrier inside the loop), and the
 // four partial tiles are summed in a fixed order through LDS at the end
 // (deterministic).  Tiles are 64 or 32 on each side, chosen by the planner
-// (smaller tiles when the grid would leave CUs idle).  Operands are gathered
+// (32x32 unless 64-wide tiles still give every CU four workgroups).  Operands are gathered
 // element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
 // taps off dY's edge) and converted to f32; bf16 products are exact in f32.
 #include "cbd_device.h"

@@ -85,6 +85,29 @@ def test_workload_vs_oracle(name, force):
     assert np.array_equal(bits1, run.result_bits()), "not deterministic"
 
 
+# Generic family with 64x64 tiles (the planner takes them only for grids of
+# at least 1024 such tiles): a 1x1 stride-1 and a 3x3 stride-2 fp32 problem,
+# and a bf16 NHWC one forced onto the generic family.
+GENERIC64 = [
+    Problem("g64-1x1", 16, 1, 64, 64, 64, 64, 1, 1, 1, 1, 0, 0, 1, 1, NCHW, "f32", "u", "u", 0, 0),
+    Problem("g64-3x3s2", 16, 1, 64, 64, 72, 72, 3, 3, 2, 2, 1, 1, 1, 1, NCHW, "f32", "u", "u", 0, 0),
+    Problem("g64-nhwc", 16, 1, 64, 64, 64, 64, 1, 1, 1, 1, 0, 0, 1, 1, NHWC, "bf16", "n1", "n0.05", 0, 0),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(GENERIC64)))
+def test_generic_64_tiles_vs_oracle(idx):
+    p = GENERIC64[idx]
+    print(f"[parity] {p.name}", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p, cbd.KERNEL_GENERIC)
+    assert (pl.info().tile_m, pl.info().tile_n) == (64, 64)
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
+    ok, info = check(p, run, oracle.bwd_data(p, dy, w))
+    assert ok, info
+    assert run.guards_intact()
+
+
 @pytest.mark.parametrize("name", [p.name for p in PROBLEMS])
 def test_workload_integer_exact(name):
     p = by_name(name)
