@@ -284,7 +284,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(backward-data shards by batch with no collective; see the design notes)",
+              f"(backward-data shards by batch with no collective: each GPU would run this "
+              f"same launch on its own slice of the batch)",
               file=sys.stderr)
         sys.exit(2)
 
