@@ -24,11 +24,15 @@
 //     read one step ahead of the MFMAs that use them;
 //   * a wave issues at most one instruction per four clocks and each VALU
 //     instruction between MFMAs costs MFMA time, so the loop carries only
-//     MFMAs, fragment reads, loads and one add per load offset per tile;
-//     the issue order is pinned with scheduling barriers;
+//     MFMAs, fragment reads, loads and a few scalar instructions per tile
+//     (load offsets step in the scalar offset, past-the-end tiles load
+//     through a zero record count); the issue order is pinned with
+//     scheduling barriers;
 //   * per-tap dY gather offsets (position -> byte offset, or out of range for
 //     taps off dY's edge and ragged tiles) and per-position dX offsets are
-//     built once per workgroup into small LDS tables;
+//     built once per workgroup into small LDS tables; with one tap per class
+//     each lane computes its dY offsets itself and the dX table is built
+//     while the first tiles load;
 //   * epilogue: accumulators -> bf16 (nearest-even, v_cvt_pk_bf16_f32) -> LDS
 //     ([position][c], chunk ^ (row & 31)) -> 16-byte coalesced stores along
 //     each dX pixel row.
