@@ -108,6 +108,58 @@ def test_generic_64_tiles_vs_oracle(idx):
     assert run.guards_intact()
 
 
+# ------------------------------------------------------------ maximum sizes ---
+# dX just under 2^31 bytes, the library's limit for 32-bit buffer offsets,
+# with three of four phases unreached (1x1 filter, stride 2): the GEMM kernels
+# and both zero-fill paths (standalone NHWC 16-byte chunks, folded NCHW
+# elements) run at the largest offsets the planner accepts.  Small-integer
+# operands make every expected value exact; checked at the corners of the
+# tensor, the last elements and random points, plus every unreached element
+# exactly zero and no NaN sentinel left anywhere in dX.
+MAXSIZE = [
+    Problem("max-nhwc-bf16", 15, 1, 256, 256, 512, 512, 1, 1, 2, 2, 0, 0, 1, 1, NHWC, "bf16",
+            "int", "int", 0, 0),
+    Problem("max-nchw-f32", 8, 1, 64, 64, 1000, 1000, 1, 1, 2, 2, 0, 0, 1, 1, NCHW, "f32",
+            "int", "int", 0, 0),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MAXSIZE)))
+def test_max_size_integer_exact(idx):
+    p = MAXSIZE[idx]
+    print(f"[max-size] {p.name}", flush=True)
+    pl = plan_for(p)
+    sh = pl.shapes()
+    es = 4 if p.dtype == "f32" else 2
+    assert 2 ** 31 * 15 // 16 <= int(np.prod(sh["dx"])) * es < 2 ** 31
+    assert pl.info().num_zero_regions == 3
+    dy = small_ints(1, sh["dy"])
+    w = small_ints(2, sh["w"])
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
+    torch.cuda.synchronize()
+    dx = run.dx
+    assert not bool(torch.isnan(dx).any())
+    assert run.guards_intact()
+    odd = [dx[:, :, 1::2, :], dx[:, :, :, 1::2]] if p.layout == NCHW else \
+          [dx[:, 1::2, :, :], dx[:, :, 1::2, :]]
+    for v in odd:
+        assert bool((v == 0).all())
+    rng = np.random.default_rng(77)
+    pts = [(n, c, h, x) for n in (0, p.n - 1) for c in (0, 1, p.c - 1)
+           for h in (0, 1, p.hi - 2, p.hi - 1) for x in (0, 1, p.wi - 2, p.wi - 1)]
+    pts += list(zip(rng.integers(0, p.n, 3000), rng.integers(0, p.c, 3000),
+                    rng.integers(0, p.hi, 3000), rng.integers(0, p.wi, 3000)))
+    pts = np.array(pts, dtype=np.int64)
+    want = exact_expected_bits(p, oracle.bwd_data_at(p, dy, w, pts))
+    i = torch.from_numpy(pts).cuda()
+    got = dx[i[:, 0], i[:, 1], i[:, 2], i[:, 3]] if p.layout == NCHW else \
+        dx[i[:, 0], i[:, 2], i[:, 3], i[:, 1]]
+    got = got.cpu()
+    got_bits = got.view(torch.int32).numpy().view(np.uint32) if p.dtype == "f32" else \
+        got.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_bits, want), int(np.count_nonzero(got_bits != want))
+
+
 @pytest.mark.parametrize("name", [p.name for p in PROBLEMS])
 def test_workload_integer_exact(name):
     p = by_name(name)
