@@ -36,6 +36,9 @@ const char* hip_error_name(int err);
 
 // Tile shapes of each kernel family (the planner sizes grids with them).
 constexpr int kGenericBM = 64, kGenericBN = 64, kGenericBK = 16, kGenericThreads = 256;  // tiles 64 or 32
+// k-tile width of the generic family: 8 for 32x32 tiles (short K loops of
+// small problems: more, shorter gather chains), 16 for larger tiles.
+constexpr int generic_bk(int bm, int bn) { return bm * bn <= 32 * 32 ? 8 : kGenericBK; }
 constexpr int kFastBM = 256, kFastBN = 256, kFastBK = 32, kFastThreads = 256, kFastMaxTaps = 16;
 constexpr int kFastMaxKTiles = 4096;  // k tiles per tap (K/G / 32): bound of the kernel's tap division
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;

@@ -23,7 +23,8 @@
 // (register double buffer; no workgroup barrier inside the loop), and the
 // four partial tiles are summed in a fixed order through LDS at the end
 // (deterministic).  Tiles are 64 or 32 on each side, chosen by the planner
-// (32x32 unless 64-wide tiles still give every CU four workgroups).  Operands are gathered
+// (32x32 unless 64-wide tiles still give every CU four workgroups); k tiles
+// are 8 wide on 32x32 tiles, 16 on larger ones.  Operands are gathered
 // element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
 // taps off dY's edge) and converted to f32; bf16 products are exact in f32.
 #include "cbd_device.h"
@@ -61,7 +62,7 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
 
 template <int DT, int LAYOUT, int BM, int BN>
 __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const GemmArgs a) {
-  constexpr int BK = kGenericBK;            // 16
+  constexpr int BK = generic_bk(BM, BN);    // 8 (32x32 tiles) or 16
   constexpr int NW = kGenericThreads / 64;  // 4 waves, each its own k tiles
   constexpr int MB = BM / 16, NB = BN / 16;
   constexpr int AE = BK * BM / 64, BE = BK * BN / 64;  // gathers per lane per tile
