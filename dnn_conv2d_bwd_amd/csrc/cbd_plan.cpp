@@ -288,6 +288,16 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     } else {
       bn = cbd::kGenericBN;
     }
+    // At most 16 channels per group: 16-row tiles (a 32-row tile would be
+    // half padding), 16 wide too when the grid is small (measured: 16
+    // channels, N = 2, 14x14, 3x3: 16x16 tiles 22 % faster than 32x32; for
+    // 32 channels, 32x16 tiles were slower than 32x32).
+    if (Cg <= 16 && bm == 32 && bn == 32) {
+      bm = 16;
+      int64_t grid1632 = 0;
+      for (const auto& s : subs) grid1632 += p.g * ceil_div(Cg, 16) * ceil_div(s.n, 32);
+      if (grid1632 < 512) bn = 16;
+    }
     bk = cbd::generic_bk((int)bm, (int)bn);
   } else if (kernel == CBD_KERNEL_NHWC_BF16) {
     bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;

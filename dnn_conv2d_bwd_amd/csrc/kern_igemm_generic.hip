@@ -22,9 +22,10 @@
 // with v_mfma_f32_16x16x4_f32 and keeps the next tile's gathers in flight
 // (register double buffer; no workgroup barrier inside the loop), and the
 // four partial tiles are summed in a fixed order through LDS at the end
-// (deterministic).  Tiles are 64 or 32 on each side, chosen by the planner
-// (32x32 unless 64-wide tiles still give every CU four workgroups); k tiles
-// are 8 wide on 32x32 tiles, 16 on larger ones.  Operands are gathered
+// (deterministic).  Tiles are 64, 32 or 16 on each side, chosen by the
+// planner (32x32 unless 64-wide tiles still give every CU four workgroups;
+// 16 rows for at most 16 channels per group); k tiles are 8 wide on tiles of
+// up to 32x32, 16 on larger ones.  Operands are gathered
 // element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
 // taps off dY's edge) and converted to f32; bf16 products are exact in f32.
 #include "cbd_device.h"
@@ -265,6 +266,8 @@ int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
   if (a.tile_m == 32 && a.tile_n == 64) return launch_one<DT, LAYOUT, 32, 64>(a, grid, stream);
   if (a.tile_m == 64 && a.tile_n == 32) return launch_one<DT, LAYOUT, 64, 32>(a, grid, stream);
   if (a.tile_m == 32 && a.tile_n == 32) return launch_one<DT, LAYOUT, 32, 32>(a, grid, stream);
+  if (a.tile_m == 16 && a.tile_n == 32) return launch_one<DT, LAYOUT, 16, 32>(a, grid, stream);
+  if (a.tile_m == 16 && a.tile_n == 16) return launch_one<DT, LAYOUT, 16, 16>(a, grid, stream);
   return (int)hipErrorInvalidValue;
 }
 

@@ -326,15 +326,18 @@ def test_run_without_device_returns_hip_error():
 
 def test_generic_tile_choice():
     """Generic family: 64x64 tiles only when that grid has at least 1024
-    tiles (four per CU), 32x32 otherwise."""
+    tiles (four per CU), 32x32 otherwise, 16 rows for at most 16 channels per
+    group (16 wide too on small grids); k tiles 8 wide up to 32x32."""
     from cbd_inputs.problems import Problem as P_
-    small = [q for q in PROBLEMS if q.name in ("c1", "c2-14-3", "c3a", "c3b")]
+    small = [q for q in PROBLEMS if q.name in ("c2-14-3", "c3a", "c3b")]
     for q in small:
         inf = plan_of(q).info()
-        assert (inf.tile_m, inf.tile_n) == (32, 32), q.name
+        assert (inf.tile_m, inf.tile_n, inf.tile_k) == (32, 32, 8), q.name
+    c1 = plan_of([q for q in PROBLEMS if q.name == "c1"][0]).info()
+    assert (c1.tile_m, c1.tile_n, c1.tile_k) == (16, 16, 8)
     big = P_("g64", 16, 1, 64, 64, 64, 64, 1, 1, 1, 1, 0, 0, 1, 1, NCHW, "f32", "u", "u", 0, 0)
     inf = plan_of(big).info()
-    assert (inf.tile_m, inf.tile_n, inf.grid_main) == (64, 64, 1024)
+    assert (inf.tile_m, inf.tile_n, inf.tile_k, inf.grid_main) == (64, 64, 16, 1024)
     just_below = big.with_(hi=62, wi=64)  # 16*62*64 / 64 = 992 tiles of 64x64
     inf = plan_of(just_below).info()
     assert (inf.tile_m, inf.tile_n) == (32, 32)
