@@ -299,6 +299,18 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       if (grid1632 < 512) bn = 16;
     }
     bk = cbd::generic_bk((int)bm, (int)bn);
+    // Long K on a small grid of 32x32 tiles: eight waves per workgroup share
+    // the K loop (a wave's gather chain halves; measured: 32 channels, 3x3,
+    // N = 32, 14-16 pixels, 36 k tiles on 196-256 workgroups, 6 % faster;
+    // with short K or many workgroups eight waves were slower).
+    if (bm == 32 && bn == 32) {
+      int64_t grid32 = 0, kt = 0;
+      for (const auto& s : subs) {
+        grid32 += p.g * ceil_div(Cg, 32) * ceil_div(s.n, 32);
+        kt = std::max<int64_t>(kt, int64_t(s.taps_h) * s.taps_w * ceil_div(Kg, bk));
+      }
+      if (grid32 < 512 && kt >= 32) threads = 8 * 64;
+    }
   } else if (kernel == CBD_KERNEL_NHWC_BF16) {
     bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;
   } else {
@@ -545,6 +557,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_cols = (int32_t)grp_cols;
   a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
   a.static_shape = static_shape ? 1 : 0;
+  a.gen_waves = kernel == CBD_KERNEL_GENERIC ? (int32_t)(threads / 64) : 0;
   a.ws = nullptr;
   pl->grid_finalize = ksplit > 1 ? tile / ksplit * (cbd::kFastBN / 8) : 0;
   for (size_t i = 0; i < subs.size(); i++) {
@@ -594,8 +607,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   std::memset(&a.fz, 0, sizeof(a.fz));
   if (kernel == CBD_KERNEL_GENERIC && !per_class && items > 0 &&
       (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
-      cbd::kZeroThreads == cbd::kGenericThreads &&
-      (tile + grid_zero) * cbd::kGenericThreads < (int64_t(1) << 32)) {
+      threads == cbd::kZeroThreads &&
+      (tile + grid_zero) * threads < (int64_t(1) << 32)) {
     cbd::FusedZero& f = a.fz;
     f.num_regions = z.num_regions;
     f.layout = z.layout; f.esize = z.esize; f.chunk = z.chunk;

@@ -17,7 +17,8 @@
 //
 // The problems this family serves are small: a workgroup's time is the
 // chain of global-load latencies along K, not MFMA work.  So the K loop is
-// split across the 4 waves of a workgroup (wave w takes k tiles w, w+4, ...),
+// split across the NW waves of a workgroup (4, or 8 for long K loops on small
+// grids; wave w takes k tiles w, w+NW, ...),
 // each wave computes the whole BM x BN tile from its own LDS staging area
 // with v_mfma_f32_16x16x4_f32 and keeps the next tile's gathers in flight
 // (register double buffer; no workgroup barrier inside the loop), and the
@@ -61,14 +62,14 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
   }
 }
 
-template <int DT, int LAYOUT, int BM, int BN>
-__global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const GemmArgs a) {
+template <int DT, int LAYOUT, int BM, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArgs a) {
   constexpr int BK = generic_bk(BM, BN);    // 8 (32x32 tiles) or 16
-  constexpr int NW = kGenericThreads / 64;  // 4 waves, each its own k tiles
+  constexpr int THREADS = NW * 64;          // NW (4 or 8) waves, each its own k tiles
   constexpr int MB = BM / 16, NB = BN / 16;
   constexpr int AE = BK * BM / 64, BE = BK * BN / 64;  // gathers per lane per tile
   constexpr int STG = BK * (BM + BN);                  // staging floats per wave
-  constexpr int RED = 2 * BM * BN;                     // two partial tiles at a time
+  constexpr int RED = (NW / 2) * BM * BN;              // NW/2 partial tiles at a time
   constexpr int LDSF = NW * STG > RED ? NW * STG : RED;
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
   __shared__ float lds[LDSF];
@@ -77,7 +78,8 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
 
-  if ((int)blockIdx.x >= a.total_tiles) {  // zero-fill folded into this launch
+  if ((int)blockIdx.x >= a.total_tiles) {  // zero-fill folded into this launch (four-wave plans)
+    if constexpr (NW != 4) return;
     const FusedZero& z = a.fz;
     const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
     const uint32_t base =
@@ -198,28 +200,33 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
     compute(a1, b1);
   }
 
-  // Cross-wave sum in a fixed order, (w0 + w2) + (w1 + w3), through LDS
-  // (reusing the staging area; two partial tiles at a time).
+  // Cross-wave sum in a fixed order through LDS (reusing the staging area):
+  // a tree that halves the waves holding partial tiles, w += w + NW/2, ...,
+  // down to two, (w0 + w2) + (w1 + w3) for four waves; the last sum is made
+  // by the epilogue.
   auto red_at = [&](int slot, int bm, int bn, int v) -> float& {
     return lds[(slot * BM + bm * 16 + 4 * (lane >> 4) + v) * BN + bn * 16 + (lane & 15)];
   };
-  __syncthreads();
-  if (wave >= 2) {
 #pragma unroll
-    for (int bm = 0; bm < MB; bm++)
+  for (int sr = NW / 2; sr >= 2; sr /= 2) {
+    __syncthreads();
+    if (wave >= sr && wave < 2 * sr) {
 #pragma unroll
-      for (int bn = 0; bn < NB; bn++)
+      for (int bm = 0; bm < MB; bm++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) red_at(wave - 2, bm, bn, v) = acc[bm][bn][v];
-  }
-  __syncthreads();
-  if (wave < 2) {
+        for (int bn = 0; bn < NB; bn++)
 #pragma unroll
-    for (int bm = 0; bm < MB; bm++)
+          for (int v = 0; v < 4; v++) red_at(wave - sr, bm, bn, v) = acc[bm][bn][v];
+    }
+    __syncthreads();
+    if (wave < sr) {
 #pragma unroll
-      for (int bn = 0; bn < NB; bn++)
+      for (int bm = 0; bm < MB; bm++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) acc[bm][bn][v] += red_at(wave, bm, bn, v);
+        for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) acc[bm][bn][v] += red_at(wave, bm, bn, v);
+    }
   }
   __syncthreads();
   if (wave < 2) {
@@ -244,19 +251,19 @@ __global__ __launch_bounds__(kGenericThreads, 2) void igemm_generic_kernel(const
                                 : ((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg;
   const int cstride = LAYOUT == 0 ? a.Hi * a.Wi : 1;
 #pragma unroll
-  for (int i = 0; i < BM * BN / kGenericThreads; i++) {
-    const int m = tid / BN + (kGenericThreads / BN) * i;
+  for (int i = 0; i < BM * BN / THREADS; i++) {
+    const int m = tid / BN + (THREADS / BN) * i;
     const float v = lds[m * BN + tid % BN] + lds[(BM + m) * BN + tid % BN];
     const int c = m0 + m;
     store_elem<DT>(rdx, (pv && c < a.Cg) ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB, v);
   }
 }
 
-template <int DT, int LAYOUT, int BM, int BN>
+template <int DT, int LAYOUT, int BM, int BN, int NW = 4>
 int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN>,
-                              dim3((unsigned)grid), dim3(kGenericThreads), args, 0,
+  return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW>,
+                              dim3((unsigned)grid), dim3(NW * 64), args, 0,
                               (hipStream_t)stream);
 }
 
@@ -265,7 +272,9 @@ int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
   if (a.tile_m == 64 && a.tile_n == 64) return launch_one<DT, LAYOUT, 64, 64>(a, grid, stream);
   if (a.tile_m == 32 && a.tile_n == 64) return launch_one<DT, LAYOUT, 32, 64>(a, grid, stream);
   if (a.tile_m == 64 && a.tile_n == 32) return launch_one<DT, LAYOUT, 64, 32>(a, grid, stream);
-  if (a.tile_m == 32 && a.tile_n == 32) return launch_one<DT, LAYOUT, 32, 32>(a, grid, stream);
+  if (a.tile_m == 32 && a.tile_n == 32)
+    return a.gen_waves == 8 ? launch_one<DT, LAYOUT, 32, 32, 8>(a, grid, stream)
+                            : launch_one<DT, LAYOUT, 32, 32>(a, grid, stream);
   if (a.tile_m == 16 && a.tile_n == 32) return launch_one<DT, LAYOUT, 16, 32>(a, grid, stream);
   if (a.tile_m == 16 && a.tile_n == 16) return launch_one<DT, LAYOUT, 16, 16>(a, grid, stream);
   return (int)hipErrorInvalidValue;
