@@ -44,6 +44,6 @@ constexpr int kFastMaxKTiles = 4096;  // k tiles per tap (K/G / 32): bound of th
 constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
 constexpr int kGroupedRowLds = 64 * 1024;  // one-row kernel: staged dY rows per workgroup
 constexpr int kLdsPerCu = 160 * 1024;       // gfx950 LDS per compute unit (also the per-workgroup limit)
-constexpr int kZeroThreads = 256, kZeroItemsPerThread = 4;
+constexpr int kZeroThreads = 256, kZeroItemsPerThread = 2;
 
 }  // namespace cbd

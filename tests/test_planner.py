@@ -145,7 +145,7 @@ def test_workload_plans():
             tiles += s.tiles
         # the generic family folds the zero-fill workgroups into its launch
         fused = info.num_zero_regions > 0 and info.grid_zero == 0
-        zero_wgs = -(-info.zero_elems // (256 * 4)) if fused and p.layout == NCHW else 0
+        zero_wgs = -(-info.zero_elems // (256 * 2)) if fused and p.layout == NCHW else 0
         assert tiles + zero_wgs == info.grid_main
         assert info.launches == 1 + (info.grid_zero > 0)
         if p.name in expect:
