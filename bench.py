@@ -213,7 +213,7 @@ def machine():
                 break
     except OSError:
         pass
-    # Highest shader-clock level the driver lists (sysfs), if readable.
+    # Highest shader-clock level the amdgpu kernel module lists (sysfs), if readable.
     sclk = None
     import glob
     for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
