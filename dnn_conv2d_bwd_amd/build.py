@@ -41,9 +41,17 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The large-tile kernel takes its tensors and sizes
+# as leading scalar parameters, preloaded into SGPRs at wave launch (code
+# objects keep a fallback that loads them for firmware without preloading).
+EXTRA = {
+    "kern_igemm_nhwc_bf16.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -74,7 +74,7 @@ struct GemmArgs {
   int32_t grp_wide;    // 1: the 16x16x16-MFMA kernel (bf16, C/G = K/G in {16, 32})
   int32_t gen_waves;   // generic family: waves per workgroup (4, or 8 for long K on small grids)
   int32_t ksplit;      // large-tile kernel: workgroups sharing a tile's K loop (<= 1: none)
-  int32_t static_shape;  // large-tile kernel: 1 = the instance for 64 k tiles per tap, 1 tap
+  int32_t static_shape;  // large-tile kernel: 1 = 64 k tiles per tap, 1 tap; 2 = the fixed 2048-channel geometry
   void* ws;            // split-K f32 partial tiles, 256 KiB per workgroup (caller's workspace)
   const void* dy;
   const void* w;

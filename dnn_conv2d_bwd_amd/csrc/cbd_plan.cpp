@@ -460,22 +460,33 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     ksplit = std::max<int64_t>(ksplit, 1);
   }
 
-  // Shape-specialised instance (compile-time k tiles per tap and taps per
-  // class): only the one for K/G = 2048 with one tap per class is built.  It
-  // computes the same bits as the descriptor-driven kernel and is used
-  // whenever it matches, unless the caller asks for the latter.
-  bool static_shape = false;
+  // Shape-specialised instances of the large-tile kernel.  Level 1: k tiles
+  // per tap and taps per class fixed at compile time (K/G = 2048, one tap
+  // per class).  Level 2: the whole geometry fixed (C = K = 2048, G = 1,
+  // Hi = 1, a 1x2 filter at stride 2 along W, no padding or dilation, Wi
+  // even, so class r writes dX pixel 2p + r from dY pixel p; N and Wi stay
+  // free).  Each computes the same bits as the descriptor-driven kernel; the
+  // most specialised one that matches is used unless the caller asks for the
+  // descriptor-driven kernel.
+  int static_shape = 0;
   {
-    bool ok = kernel == CBD_KERNEL_NHWC_BF16 && ksplit == 1 && Kg == 64 * cbd::kFastBK &&
-              !no_split && !subs.empty();
-    for (const auto& s : subs) ok = ok && s.taps_h * s.taps_w == 1;
-    if (static_mode == 1 && !ok) {
+    bool ok1 = kernel == CBD_KERNEL_NHWC_BF16 && ksplit == 1 && Kg == 64 * cbd::kFastBK &&
+               !no_split && !subs.empty();
+    for (const auto& s : subs) ok1 = ok1 && s.taps_h * s.taps_w == 1;
+    // (Level 2 takes a class from its tile index, so not one launch per class.)
+    bool ok2 = ok1 && !per_class && p.g == 1 && Cg == 2048 && p.hi == 1 && p.y == 1 && p.x == 2 &&
+               p.stride_w == 2 && p.pad_h == 0 && p.pad_w == 0 && p.dil_w == 1 && p.wi % 2 == 0 &&
+               subs.size() == 2;
+    for (size_t i = 0; ok2 && i < subs.size(); i++)
+      ok2 = subs[i].phase_w == (int32_t)i && subs[i].class_w == (int32_t)i && subs[i].beta_w == 0 &&
+            subs[i].phase_h == 0 && subs[i].beta_h == 0 && subs[i].pos_h == 1 && subs[i].pos_w == Wo;
+    if (static_mode == 1 && !ok1) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this problem "
                                        "(built: NHWC bf16, K/G = 2048, one tap per class, residue split, "
                                        "no K split)");
     }
-    static_shape = ok && static_mode >= 0;
+    static_shape = static_mode < 0 ? 0 : ok2 ? 2 : ok1 ? 1 : 0;
   }
 
   // Tiles per class (contiguous ranges of the logical grid, in LPT order).
@@ -556,7 +567,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_wide = grp_wide ? 1 : 0;
   a.grp_cols = (int32_t)grp_cols;
   a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
-  a.static_shape = static_shape ? 1 : 0;
+  a.static_shape = static_shape;
   a.gen_waves = kernel == CBD_KERNEL_GENERIC ? (int32_t)(threads / 64) : 0;
   a.ws = nullptr;
   pl->grid_finalize = ksplit > 1 ? tile / ksplit * (cbd::kFastBN / 8) : 0;
@@ -641,7 +652,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.rows_per_wg = grp_rows;
   info.cols_per_wg = grp_cols;
   info.ksplit = ksplit;
-  info.static_shape = static_shape ? 1 : 0;
+  info.static_shape = static_shape;
   info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
   info.variant = kernel != CBD_KERNEL_GROUPED ? 0
                  : grp_wide                    ? 4

@@ -35,7 +35,12 @@
 //     while the first tiles load;
 //   * epilogue: accumulators -> bf16 (nearest-even, v_cvt_pk_bf16_f32) -> LDS
 //     ([position][c], chunk ^ (row & 31)) -> 16-byte coalesced stores along
-//     each dX pixel row.
+//     each dX pixel row, in four column groups so that one group's stores
+//     drain while the next is converted;
+//   * a fully shape-specialised instance for the 2048-channel 1x2 stride-2
+//     problem (any batch and even width) takes the class from its tile
+//     index and computes every offset with shifts and multiplies; the
+//     tensors arrive as preloaded scalar kernel parameters.
 #include <type_traits>
 
 #include "cbd_device.h"
@@ -81,13 +86,43 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) <
 __device__ inline int swz_w(int row) { return 4 * (row & 3); }  // W rows: 32 chunks
 __device__ inline int swz_y(int row) { return (row >> 2) & 3; }  // dY rows: 4 chunks
 
+// Channels of the fully shape-specialised instance (FIX): C = K = 2048, one
+// group, one dX row (Hi = 1) of Wi = 2 Wo pixels, a 1x2 filter at stride 2
+// along W with no padding or dilation -- the problem of the BOO listing in
+// fusilli issue #101 at any batch and width.  Class r (filter tap x = r)
+// then writes dX pixel 2p + r from dY pixel p and the weight slice
+// W[:, 0, r, :]: two plain GEMMs, no descriptor or division anywhere.
+constexpr int FIX_CH = 2048;
+
+// Cache policy of the dX stores: sc0 sc1 (bits 0 and 4 of the buffer_store
+// cache-policy operand), i.e. written through at system scope instead of
+// held dirty in L2.  Every workgroup ends at about the same time, so dirty
+// lines would otherwise all be written back in one burst when the launch
+// completes; written through, they leave while later column groups of the
+// epilogue are still being converted (measured: about 0.9 us less per
+// launch on the 2048-channel problem, with the same bits written).
+#ifndef CBD_NHWC_STORE_AUX
+#define CBD_NHWC_STORE_AUX 17
+#endif
+constexpr int kStoreAux = CBD_NHWC_STORE_AUX;
+
 // SPLIT: the K loop of each tile is split over a.ksplit workgroups that
 // write f32 partial tiles (a separate instance, so that the plain kernel
 // carries none of its registers).  SKPT, STAPS > 0: a shape-specialised
 // instance with k tiles per tap and taps per class fixed at compile time
-// (0: read from the descriptors at run time).
-template <bool SPLIT, int SKPT, int STAPS>
-__global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmArgs a) {
+// (0: read from the descriptors at run time).  FIX: the fully specialised
+// instance above (SKPT = 64, STAPS = 1), which reads nothing but its scalar
+// parameters.
+//
+// The tensors and their byte sizes (buffer record counts) come first as
+// scalar parameters, which the compiler preloads into SGPRs at wave launch:
+// no kernel-argument fetch stands between the launch and the first loads.
+// fix_npos / fix_tiles (positions per class, workgroups) serve FIX only.
+template <bool SPLIT, int SKPT, int STAPS, bool FIX>
+__global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
+    const void* dy_p, const void* w_p, void* dx_p, uint32_t dy_bytes, uint32_t w_bytes,
+    uint32_t dx_bytes, int32_t fix_npos, int32_t fix_tiles, const GemmArgs a) {
+  static_assert(!FIX || (!SPLIT && SKPT == FIX_CH / BK && STAPS == 1), "FIX: one tap, K = 2048, no split");
   // Stages as distinct objects: the compiler can then see that fragment reads
   // of one stage do not alias the loads in flight into another.
   // W parts of the four stages at [0, 64 KiB), dY parts at [64, 128 KiB):
@@ -101,36 +136,54 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 128-position half
 
-  dev::prefetch_args(a);
-  const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
-  const SubDesc s = a.sub[dev::find_class(a, t)];
-  const int npix_img = s.pos_h * s.pos_w;
-  const int npos = a.N * npix_img;
-  const int tiles_n = (npos + BN - 1) / BN;
-  const int per_group = a.tiles_m * tiles_n;
-  // With the K loop split over S workgroups (S = a.ksplit > 1), the S
-  // workgroups of a tile are consecutive: split = t mod S (class ranges
-  // start at multiples of S).
+  // Tile decode: logical tile t -> (class, group, split, m0, n0).
+  SubDesc s = {};
+  int t, npix_img, npos, split, g, m0, n0, fix_r = 0;
   const int S = SPLIT ? a.ksplit : 1;
-  const int split = (t - s.tile_begin) % S;
-  const int local = (t - s.tile_begin) / S;
-  const int g = local / per_group;
-  const int rem = local - g * per_group;
-  const int m0 = (rem % a.tiles_m) * BM;
-  const int n0 = (rem / a.tiles_m) * BN;
+  if constexpr (FIX) {
+    // Two classes of fix_tiles / 2 tiles each, 8 channel tiles per position tile.
+    t = dev::logical_tile(blockIdx.x, fix_tiles, fix_tiles >= 64 ? 1 : 0);
+    fix_r = t >= (fix_tiles >> 1) ? 1 : 0;
+    const int local = t - fix_r * (fix_tiles >> 1);
+    m0 = (local & (FIX_CH / BM - 1)) * BM;
+    n0 = (local / (FIX_CH / BM)) * BN;
+    npos = fix_npos;
+    npix_img = 0;
+    split = 0;
+    g = 0;
+  } else {
+    dev::prefetch_args(a);
+    t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
+    s = a.sub[dev::find_class(a, t)];
+    npix_img = s.pos_h * s.pos_w;
+    npos = a.N * npix_img;
+    const int tiles_n = (npos + BN - 1) / BN;
+    const int per_group = a.tiles_m * tiles_n;
+    // With the K loop split over S workgroups (S = a.ksplit > 1), the S
+    // workgroups of a tile are consecutive: split = t mod S (class ranges
+    // start at multiples of S).
+    split = (t - s.tile_begin) % S;
+    const int local = (t - s.tile_begin) / S;
+    g = local / per_group;
+    const int rem = local - g * per_group;
+    m0 = (rem % a.tiles_m) * BM;
+    n0 = (rem / a.tiles_m) * BN;
+  }
   const int ntaps = STAPS > 0 ? STAPS : s.taps_h * s.taps_w;
+  const int Cg = FIX ? FIX_CH : a.Cg;
 
   // Buffer descriptors of dY and W as plain SGPR quads (the loads below are
   // written in assembly), record count = tensor bytes as in dev::rsrc.
-  const i32x4 dyd = {(int)(uint32_t)(uintptr_t)a.dy, (int)(((uintptr_t)a.dy >> 32) & 0xffff),
-                     (int)a.dy_bytes, 0x00020000};
-  const i32x4 dw = {(int)(uint32_t)(uintptr_t)a.w, (int)(((uintptr_t)a.w >> 32) & 0xffff),
-                    (int)a.w_bytes, 0x00020000};
-  const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+  const i32x4 dyd = {(int)(uint32_t)(uintptr_t)dy_p, (int)(((uintptr_t)dy_p >> 32) & 0xffff),
+                     (int)dy_bytes, 0x00020000};
+  const i32x4 dw = {(int)(uint32_t)(uintptr_t)w_p, (int)(((uintptr_t)w_p >> 32) & 0xffff),
+                    (int)w_bytes, 0x00020000};
+  const auto rdx = dev::rsrc(dx_p, dx_bytes);
   // Uniform loop bounds, fixed before the divergent table build (values
   // first defined inside a divergent region would live in VGPRs).
-  const int YX = __builtin_amdgcn_readfirstlane(a.Y * a.X);
-  const uint32_t wrow = __builtin_amdgcn_readfirstlane((uint32_t)(YX * a.Cg) * 2u);  // bytes between k rows of W
+  const int YX = FIX ? 2 : __builtin_amdgcn_readfirstlane(a.Y * a.X);
+  const uint32_t wrow = FIX ? 2u * FIX_CH * 2u
+                            : __builtin_amdgcn_readfirstlane((uint32_t)(YX * a.Cg) * 2u);  // bytes between k rows of W
   const int kpt = SKPT > 0 ? SKPT : __builtin_amdgcn_readfirstlane(a.Kg / BK);
   // This workgroup's k tiles: [kb, ke) of the class's ntaps * kpt (tile t =
   // tap t / kpt, k rows 32 (t mod kpt) ...); the planner keeps S <= ntaps*kpt.
@@ -152,6 +205,11 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   // dY offsets of every tap (not needed with one tap), the dX offsets, and
   // the W offset of every tap.
   auto build_tables = [&]() {
+    if constexpr (FIX) {
+      const int p = n0 + tid;
+      otab[tid] = p < npos ? (uint32_t)(2 * p + fix_r) * (FIX_CH * 2u) + (uint32_t)m0 * 2u : dev::kOOB;
+      return;
+    }
     if (tid < BN) {
       const int p = n0 + tid;
       const bool pv = p < npos;
@@ -191,7 +249,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   for (int i = 0; i < 4; i++) {
     const int row = 8 * wave + 2 * i + (lane >> 5);
     const int c = m0 + 8 * ((lane & 31) ^ swz_w(row));
-    a_lane[i] = c < a.Cg ? (uint32_t)row * wrow + (uint32_t)c * 2u : dev::kOOB;
+    a_lane[i] = c < Cg ? (uint32_t)row * wrow + (uint32_t)c * 2u : dev::kOOB;
   }
   int b_row[4];
   uint32_t b_chunk[4];
@@ -213,7 +271,15 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   const int tap0 = __builtin_amdgcn_readfirstlane(kb / kpt);
   const uint32_t r0 = (uint32_t)(kb - tap0 * kpt);
   uint32_t a_off[4], b_off[4];
-  if constexpr (ONE_TAP) {
+  if constexpr (FIX) {
+    // dY pixel p, k chunk; W slice r (row k at k * 2 * C, tap r at r * C).
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      a_off[i] = a_lane[i] + (uint32_t)fix_r * (FIX_CH * 2u);
+      const int p = n0 + b_row[i];
+      b_off[i] = p < npos ? (uint32_t)p * (FIX_CH * 2u) + b_chunk[i] : dev::kOOB;
+    }
+  } else if constexpr (ONE_TAP) {
     // Tap 0 of the class (taps y = cls_h, x = cls_w; dY row t + beta).
     // Position p = (n, th, tw) by multiply-high with m = ceil(2^32 / d):
     // the estimate is q or q + 1 for every x < 2^32 and one compare fixes it.
@@ -248,7 +314,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   }
   uint32_t a_soff = __builtin_amdgcn_readfirstlane(r0 * a_step);
   uint32_t b_soff = __builtin_amdgcn_readfirstlane(r0 * b_step);
-  uint32_t a_rec = a.w_bytes, b_rec = a.dy_bytes;  // record counts of the next tile's loads
+  uint32_t a_rec = w_bytes, b_rec = dy_bytes;  // record counts of the next tile's loads
   // Tile t = (tap, k tile) with tap = t / kpt, by multiply-high with a
   // rounded-up reciprocal (exact for t < 17 kpt, kpt <= 4096: tiles per
   // class are at most 16 kpt, plus the 4 tiles loaded past the end).
@@ -267,7 +333,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     } else {
       a_soff += a_step;
     }
-    a_rec = t < ke ? a.w_bytes : 0u;
+    a_rec = t < ke ? w_bytes : 0u;
   };
   auto advance_b = [&](int t) {
     if (!ONE_TAP && t < ke && t - tap_of(t) * kpt == 0) {
@@ -278,7 +344,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
     } else {
       b_soff += b_step;
     }
-    b_rec = t < ke ? a.dy_bytes : 0u;
+    b_rec = t < ke ? dy_bytes : 0u;
   };
   // Load j of a tile (j < 4: W, else dY): 64 lanes x 16 bytes, global ->
   // LDS without VGPRs (buffer_load ... lds; lane l writes 16 bytes at
@@ -380,7 +446,10 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
                   bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0, auto&& advance) {
 #pragma unroll
     for (int q = 0; q < 16; q++) {
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q >> 2], fb[q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+      // Boustrophedon order over the 4x4 blocks: consecutive MFMAs change
+      // one operand at a time (fewer operand bits toggle between them).
+      const int bm = q >> 2, bn = (bm & 1) ? 3 - (q & 3) : (q & 3);
+      acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
       if (q < 12) read_one(rstc, rks, q, ra, rb);
       if ((q & 3) == 2) set_m0(dstc, j0 + (q >> 2));
       if ((q & 3) == 3) load_m0(j0 + (q >> 2));
@@ -478,37 +547,43 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(const GemmA
   }
 
   // ---- epilogue.  C tile [position row][256 channels] bf16 = 128 KiB over
-  // the four stages (64 rows each), 16-byte chunk c/8 of row r stored at
-  // chunk (c/8) ^ (r & 31).
+  // the four stages, 16-byte chunk c/8 of row r stored at chunk
+  // (c/8) ^ (r & 31).  In four column groups bn (positions 32 bn ... and
+  // 128 + 32 bn ..., 64 rows): every wave converts its blocks of group bn,
+  // a barrier, then 16-byte stores along the group's pixel rows; the stores
+  // of one group drain while the next group is converted (distinct rows, so
+  // no further barrier).
   __syncthreads();
+  const int ch = tid & 31;
+  const bool cv = m0 + 8 * ch < Cg;
 #pragma unroll
   for (int bn = 0; bn < 4; bn++) {
-    const int prow = wn * 128 + bn * 32 + (lane & 31);
-    char* rowp = smem + prow * 512;
+    {
+      const int prow = wn * 128 + bn * 32 + (lane & 31);
+      char* rowp = smem + prow * 512;
 #pragma unroll
-    for (int bm = 0; bm < 4; bm++) {
+      for (int bm = 0; bm < 4; bm++) {
 #pragma unroll
-      for (int qq = 0; qq < 4; qq++) {
-        const int c = wm * 128 + bm * 32 + 8 * qq + 4 * (lane >> 5);
-        u32x2 o;
-        o[0] = dev::bf16_pack2(acc[bm][bn][4 * qq + 0], acc[bm][bn][4 * qq + 1]);
-        o[1] = dev::bf16_pack2(acc[bm][bn][4 * qq + 2], acc[bm][bn][4 * qq + 3]);
-        *(u32x2*)(rowp + (((c >> 3) ^ (prow & 31)) << 4) + ((c & 4) << 1)) = o;
+        for (int qq = 0; qq < 4; qq++) {
+          const int c = wm * 128 + bm * 32 + 8 * qq + 4 * (lane >> 5);
+          u32x2 o;
+          o[0] = dev::bf16_pack2(acc[bm][bn][4 * qq + 0], acc[bm][bn][4 * qq + 1]);
+          o[1] = dev::bf16_pack2(acc[bm][bn][4 * qq + 2], acc[bm][bn][4 * qq + 3]);
+          *(u32x2*)(rowp + (((c >> 3) ^ (prow & 31)) << 4) + ((c & 4) << 1)) = o;
+        }
       }
     }
-  }
-  __syncthreads();
-  {
-    const int ch = tid & 31;
-    const bool cv = m0 + 8 * ch < a.Cg;
-#pragma unroll 4
-    for (int it = 0; it < BN / (THREADS / 32); it++) {
-      const int prow = it * (THREADS / 32) + (tid >> 5);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 64 / (THREADS / 32); it++) {
+      const int r = it * (THREADS / 32) + (tid >> 5);  // 0..63
+      const int prow = (r & 32) * 4 + bn * 32 + (r & 31);
       const char* rowp = smem + prow * 512;
       const u32x4 v = *(const u32x4*)(rowp + ((ch ^ (prow & 31)) << 4));
       const uint32_t base = otab[prow];
       __builtin_amdgcn_raw_buffer_store_b128(u4{v[0], v[1], v[2], v[3]}, rdx,
-                                             cv ? base + (uint32_t)ch * 16u : dev::kOOB, 0, 0);
+                                             cv ? base + (uint32_t)ch * 16u : dev::kOOB, 0,
+                                             kStoreAux);
     }
   }
 }
@@ -567,10 +642,17 @@ int launch_splitk_finalize(const GemmArgs& a, int64_t grid, void* stream) {
 }
 
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream) {
-  void* args[] = {const_cast<GemmArgs*>(&a)};
-  const void* k = a.ksplit > 1          ? (const void*)&igemm_nhwc_bf16_kernel<true, 0, 0>
-                  : a.static_shape == 1 ? (const void*)&igemm_nhwc_bf16_kernel<false, 64, 1>
-                                        : (const void*)&igemm_nhwc_bf16_kernel<false, 0, 0>;
+  const void* dy = a.dy;
+  const void* w = a.w;
+  void* dx = a.dx;
+  uint32_t dyb = a.dy_bytes, wb = a.w_bytes, dxb = a.dx_bytes;
+  int32_t npos = a.num_sub > 0 ? a.N * a.sub[0].pos_h * a.sub[0].pos_w : 0;
+  int32_t tiles = a.total_tiles;
+  void* args[] = {&dy, &w, &dx, &dyb, &wb, &dxb, &npos, &tiles, const_cast<GemmArgs*>(&a)};
+  const void* k = a.ksplit > 1          ? (const void*)&igemm_nhwc_bf16_kernel<true, 0, 0, false>
+                  : a.static_shape == 2 ? (const void*)&igemm_nhwc_bf16_kernel<false, 64, 1, true>
+                  : a.static_shape == 1 ? (const void*)&igemm_nhwc_bf16_kernel<false, 64, 1, false>
+                                        : (const void*)&igemm_nhwc_bf16_kernel<false, 0, 0, false>;
   return (int)hipLaunchKernel(k, dim3((unsigned)grid), dim3(THREADS), args, 0, (hipStream_t)stream);
 }
 

@@ -126,13 +126,17 @@ typedef struct {
   int32_t per_class;    /* 1: one main launch per residue class instead of one
                            for all (an ablation of the single launch; not
                            with ksplit); 0 or 1 */
-  int32_t static_shape; /* large-tile kernel: shape-specialised instances (k
-                           tiles per tap and taps per class fixed at compile
-                           time; built for K/G = 2048 with one tap per class)
+  int32_t static_shape; /* large-tile kernel: shape-specialised instances
                            compute the same bits as the descriptor-driven
-                           kernel.  0: used when one matches; 1: required
-                           (UNSUPPORTED if none matches); -1: never (the
-                           descriptor-driven kernel, for comparison) */
+                           kernel.  Level 1: k tiles per tap and taps per
+                           class fixed at compile time (K/G = 2048, one tap
+                           per class).  Level 2: the whole geometry fixed
+                           (G = 1, C = K = 2048, Hi = 1, a 1x2 filter at
+                           stride 2 along W, no padding, even Wi; any N and
+                           Wi; not with per_class).  0: the most specialised
+                           one that matches; 1: required (UNSUPPORTED if none
+                           matches); -1: never (the descriptor-driven kernel,
+                           for comparison) */
   int32_t reserved[4];  /* must be zero */
 } cbd_plan_options;
 
@@ -209,7 +213,8 @@ typedef struct {
   int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernels: positions
                                per column block of a row (0: other kernels) */
   int64_t ksplit;           /* workgroups per tile of a split-K plan (1: none) */
-  int64_t static_shape;     /* 1: the main launch uses a shape-specialised instance */
+  int64_t static_shape;     /* main launch: 0 descriptor-driven kernel, 1 or 2
+                               the shape-specialised instance of that level */
   int64_t workspace_bytes;  /* device workspace cbd_run_ws needs (0: none) */
   int64_t variant;          /* kernel within the family; grouped: 0 direct,
                                1 one row per workgroup, 2 pipelined rows on

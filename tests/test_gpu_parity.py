@@ -291,20 +291,42 @@ def test_per_class_launches_match_single_launch(name):
     assert many.guards_intact()
 
 
-@pytest.mark.parametrize("n", [16, 3])
-def test_static_shape_instance_matches_runtime(n):
-    """The shape-specialised instance of the large-tile kernel gives the same
-    bits as the runtime-descriptor one (c4 shape, full and ragged batch)."""
-    p = by_name("c4").with_(n=n)
-    print(f"[static] c4 n={n}", flush=True)
+# Shape-specialised instances of the large-tile kernel: level 2 (the whole
+# geometry compile-time: the headline problem at any batch and even width)
+# and level 1 (k tiles per tap and taps per class compile-time).
+STATIC_CASES = [
+    ("c4", {}, 2), ("c4", {"n": 3}, 2), ("c4", {"n": 1, "wi": 100}, 2),
+    ("c4", {"c": 1024}, 1), ("c4", {"n": 2, "hi": 3}, 1), ("c4", {"n": 2, "wi": 301}, 1),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(STATIC_CASES)))
+def test_static_shape_instance_matches_runtime(idx):
+    """Each shape-specialised instance gives the same bits as the
+    descriptor-driven kernel (which the oracle checks everywhere else), and
+    matches the oracle at sampled outputs, including ragged batches/widths."""
+    name, kw, level = STATIC_CASES[idx]
+    p = by_name(name).with_(**kw)
+    print(f"[static] {name} {kw} level={level}", flush=True)
     dy, w = operands(p)
     dy_d, w_d = to_device(dy, p), to_device(w, p)
     pa, pb = plan_for(p, static_shape=-1), plan_for(p)
-    assert pa.info().static_shape == 0 and pb.info().static_shape == 1
+    assert pa.info().static_shape == 0 and pb.info().static_shape == level
     a = DeviceRun(p, pa, dy_d, w_d)()
     b = DeviceRun(p, pb, dy_d, w_d)()
-    assert np.array_equal(a.result_bits(), b.result_bits())
+    bits = b.result_bits()
+    assert np.array_equal(a.result_bits(), bits)
     assert b.guards_intact()
+    rng = np.random.default_rng(100 + idx)
+    cnt = 3000
+    pts = np.stack([rng.integers(0, p.n, cnt), rng.integers(0, p.c, cnt),
+                    rng.integers(0, p.hi, cnt), rng.integers(0, p.wi, cnt)], axis=1)
+    pts[:4] = [[p.n - 1, p.c - 1, p.hi - 1, p.wi - 1], [0, 0, 0, 0],
+               [p.n - 1, 0, p.hi - 1, p.wi - 2], [0, p.c - 1, 0, 1]]
+    ref = oracle.bwd_data_at(p, dy, w, pts)
+    got = bits.reshape(p.n, p.hi, p.wi, p.c)[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
+    ok, info = check_bf16(got, ref)
+    assert ok, info
 
 
 def test_non_default_stream():

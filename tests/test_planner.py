@@ -297,9 +297,22 @@ def test_static_shape_plans():
             (c4.dh, c4.dw), c4.layout, cbd.BF16)
     a, b = cbd.plan(*args, static_shape=-1).info(), cbd.plan(*args).info()
     assert (a.grid_main, a.launches, a.executed_macs) == (b.grid_main, b.launches, b.executed_macs)
-    assert a.static_shape == 0 and b.static_shape == 1
-    assert cbd.plan(*args, static_shape=1).info().static_shape == 1
+    # the headline geometry gets the fully specialised instance (level 2)
+    assert a.static_shape == 0 and b.static_shape == 2
+    assert cbd.plan(*args, static_shape=1).info().static_shape == 2
     assert cbd.plan(*args, ksplit=2).info().static_shape == 0
+    assert cbd.plan(*args, per_class=True).info().static_shape == 1
+    # any batch or (even) width keeps level 2; other geometry with K/G = 2048
+    # and one tap per class gets level 1
+    for n, wi in ((3, 512), (1, 64), (16, 1000)):
+        assert cbd.plan(n, 1, 2048, 2048, 1, wi, 1, 2, (1, 2), 0, 1, "nhwc", "bf16").info().static_shape == 2
+    lvl1 = [(16, 1, 1024, 2048, 1, 512, 1, 2, (1, 2), 0, 1),   # C = 1024
+            (4, 1, 2048, 2048, 3, 64, 1, 2, (1, 2), 0, 1),     # Hi = 3
+            (4, 1, 2048, 2048, 1, 63, 1, 2, (1, 2), 0, 1),     # odd width
+            (4, 1, 2048, 2048, 1, 64, 1, 2, (1, 2), (0, 1), 1),  # padding
+            (2, 2, 4096, 4096, 1, 64, 1, 2, (1, 2), 0, 1)]     # two groups
+    for q in lvl1:
+        assert cbd.plan(*q, "nhwc", "bf16").info().static_shape == 1, q
     other = (2, 1, 256, 1024, 1, 64, 1, 2, (1, 2), 0, 1, "nhwc", "bf16")
     assert cbd.plan(*other).info().static_shape == 0
     with pytest.raises(cbd.CbdError):   # K/G = 1024: no instance
