@@ -70,7 +70,9 @@ class PlanInfo(ctypes.Structure):
                 ("rows_per_wg", ctypes.c_int64), ("cols_per_wg", ctypes.c_int64),
                 ("ksplit", ctypes.c_int64), ("static_shape", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64),
-                ("variant", ctypes.c_int64)]
+                ("variant", ctypes.c_int64),
+                ("align_dy", ctypes.c_int32), ("align_w", ctypes.c_int32),
+                ("align_dx", ctypes.c_int32)]
 
 
 class SubGemm(ctypes.Structure):

@@ -61,9 +61,14 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
       return CBD_ERR_INVALID_ARG;
     }
   }
-  if (((uintptr_t)dy | (uintptr_t)w | (uintptr_t)dx) & 15u) {
-    cbd::set_error("tensor pointers must be 16-byte aligned");
-    return CBD_ERR_UNSUPPORTED;
+  {
+    const cbd_plan_info_t& in = plan->info;
+    if (((uintptr_t)dy & (uintptr_t)(in.align_dy - 1)) || ((uintptr_t)w & (uintptr_t)(in.align_w - 1)) ||
+        ((uintptr_t)dx & (uintptr_t)(in.align_dx - 1))) {
+      cbd::set_error("a tensor pointer is not aligned as the plan requires (dy " + std::to_string(in.align_dy) +
+                     ", w " + std::to_string(in.align_w) + ", dx " + std::to_string(in.align_dx) + " bytes)");
+      return CBD_ERR_UNSUPPORTED;
+    }
   }
   const cbd::GemmArgs& tmpl = plan->gemm;
   if (overlap(dx, tmpl.dx_bytes, dy, tmpl.dy_bytes) || overlap(dx, tmpl.dx_bytes, w, tmpl.w_bytes)) {

@@ -20,6 +20,7 @@
 // in MIOpen PR #272; neither page derives it, the derivation above follows
 // from the forward window alone.
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -102,6 +103,58 @@ bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) 
   return p.layout == CBD_LAYOUT_NHWC && Cg == Kg && (Cg == 1 || Cg == 2 || Cg == 4 || Cg == 8) &&
          p.g <= cbd::kGroupedThreads && cbd::kGroupedThreads % p.g == 0 &&
          max_taps <= cbd::kGroupedMaxTaps;
+}
+
+// CBD_LOG set to anything but "" or "0": every plan built is described on
+// stderr (problem, kernel choice, launch shape, sub-GEMMs, zero regions) --
+// which kernel runs a problem, and why it runs at the speed it does, without
+// a debugger.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("CBD_LOG");
+    return v && *v && !(v[0] == '0' && v[1] == 0);
+  }();
+  return on;
+}
+
+const char* kernel_name(int32_t k, int64_t variant) {
+  if (k == CBD_KERNEL_NHWC_BF16) return "nhwc_bf16 (256x256 tiles)";
+  if (k == CBD_KERNEL_GENERIC) return "generic";
+  static const char* const grouped[] = {"grouped/direct", "grouped/rows", "grouped/pipelined-dot",
+                                        "grouped/pipelined-4x4x4-mfma", "grouped/pipelined-16x16x16-mfma"};
+  return variant >= 0 && variant < 5 ? grouped[variant] : "grouped";
+}
+
+void log_plan(const cbd_plan_s& pl) {
+  const cbd_problem& p = pl.prob;
+  const cbd_plan_info_t& i = pl.info;
+  std::fprintf(stderr,
+               "[cbd] plan: N=%lld G=%lld C=%lld K=%lld Hi=%lld Wi=%lld Y=%lld X=%lld stride=(%d,%d) "
+               "pad=(%d,%d) dil=(%d,%d) %s %s -> Ho=%lld Wo=%lld\n",
+               (long long)p.n, (long long)p.g, (long long)p.c, (long long)p.k, (long long)p.hi,
+               (long long)p.wi, (long long)p.y, (long long)p.x, p.stride_h, p.stride_w, p.pad_h, p.pad_w,
+               p.dil_h, p.dil_w, p.layout == CBD_LAYOUT_NHWC ? "NHWC/KYXC" : "NCHW/KCYX",
+               p.dtype == CBD_BF16 ? "bf16" : "f32", (long long)i.ho, (long long)i.wo);
+  std::fprintf(stderr,
+               "[cbd]   kernel %s: tile %dx%dx%d, %d threads, grid %lld (+%lld zero-fill), %d launch(es), "
+               "static level %lld, ksplit %lld, rows/wg %lld, cols/wg %lld, LDS %lld B, workspace %lld B, "
+               "align dy/w/dx %d/%d/%d\n",
+               kernel_name(i.kernel, i.variant), i.tile_m, i.tile_n, i.tile_k, i.threads_main,
+               (long long)i.grid_main, (long long)i.grid_zero, i.launches, (long long)i.static_shape,
+               (long long)i.ksplit, (long long)i.rows_per_wg, (long long)i.cols_per_wg,
+               (long long)i.lds_dynamic, (long long)i.workspace_bytes, i.align_dy, i.align_w, i.align_dx);
+  std::fprintf(stderr, "[cbd]   useful %.6g GFLOP, executed %.6g GMAC, %lld zeroed elements\n",
+               (double)i.useful_flops * 1e-9, (double)i.executed_macs * 1e-9, (long long)i.zero_elems);
+  for (const cbd_subgemm_t& s : pl.subs)
+    std::fprintf(stderr,
+                 "[cbd]   sub-GEMM %d: class (%d,%d) phase (%d,%d) beta (%d,%d) taps %dx%d positions "
+                 "%lldx%lld  M=%lld N=%lld K=%lld  tiles [%lld, %lld)\n",
+                 s.id, s.class_h, s.class_w, s.phase_h, s.phase_w, s.beta_h, s.beta_w, s.taps_h, s.taps_w,
+                 (long long)s.pos_h, (long long)s.pos_w, (long long)s.m, (long long)s.n, (long long)s.k,
+                 (long long)s.tile_begin, (long long)(s.tile_begin + s.tiles));
+  for (const cbd_zero_region_t& z : pl.zeros)
+    std::fprintf(stderr, "[cbd]   zero region: phase (%d,%d), %lldx%lld positions\n", z.phase_h, z.phase_w,
+                 (long long)z.pos_h, (long long)z.pos_w);
 }
 
 }  // namespace
@@ -382,7 +435,16 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / grp_lds);
       grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(units, resident)));
     }
-  } else if (kernel == CBD_KERNEL_GROUPED) {
+  } else if (kernel == CBD_KERNEL_GROUPED && !subs.empty()) {
+    // The row and direct kernels put one group per lane of a 256-lane
+    // workgroup: C/G in {1, 2, 4, 8} and G dividing 256.  (With no
+    // sub-GEMM at all there is no main launch, only the zero-fill.)
+    if (!grouped_ok(p, Cg, Kg, max_taps)) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "grouped problem for the row / direct kernels needs C/G == K/G in "
+                                       "{1,2,4,8} with G dividing 256 (the 16x16x16-MFMA kernel was not "
+                                       "taken: rows_per_wg = -1, or a geometry it does not serve)");
+    }
     slots = cbd::kGroupedThreads / p.g;
     const int64_t pixb = p.c * es;
     const bool mfma_ok = !grouped_dot && p.dtype == CBD_BF16 && Cg == 4 && (p.g == 32 || p.g == 64);
@@ -654,6 +716,15 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.ksplit = ksplit;
   info.static_shape = static_shape;
   info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
+  // Pointer alignment: the generic family gathers and stores single
+  // elements; a zero-fill of NHWC rows writes 16-byte chunks; the other
+  // families move 16-byte vectors.
+  if (kernel == CBD_KERNEL_GENERIC) {
+    info.align_dy = info.align_w = (int32_t)es;
+    info.align_dx = (zero_elems > 0 && z.chunk == 16) ? 16 : (int32_t)es;
+  } else {
+    info.align_dy = info.align_w = info.align_dx = 16;
+  }
   info.variant = kernel != CBD_KERNEL_GROUPED ? 0
                  : grp_wide                    ? 4
                  : grp_mfma                    ? 3
@@ -663,6 +734,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
 
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);
+  if (log_enabled()) log_plan(*pl);
   *out_plan = pl;
   return CBD_OK;
 }

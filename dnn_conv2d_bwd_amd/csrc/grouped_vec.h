@@ -1,6 +1,6 @@
-// grouped_vec.h -- small helpers shared by the grouped row kernels: one
-// group's channels at one pixel as a vector of 2..16 bytes (LDS read,
-// buffer load, buffer store).
+// grouped_vec.h -- small helpers shared by the grouped kernels: one group's
+// channels at one pixel as a vector of 2, 4, 8 or a multiple of 16 bytes
+// (LDS read up to 16 bytes, buffer load, buffer store).
 #pragma once
 #include "cbd_device.h"
 
@@ -51,9 +51,13 @@ __device__ inline Vec<BYTES> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     v.w[0] = x[0];
     v.w[1] = x[1];
   } else {
-    auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    static_assert(BYTES % 16 == 0, "2, 4, 8 or a multiple of 16 bytes");
 #pragma unroll
-    for (int j = 0; j < 4; j++) v.w[j] = x[j];
+    for (int h = 0; h < BYTES / 16; h++) {
+      auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; j++) v.w[4 * h + j] = x[j];
+    }
   }
   return v;
 }
@@ -69,8 +73,12 @@ __device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const V
     u2 x = {v.w[0], v.w[1]};
     __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
   } else {
-    u4 x = {v.w[0], v.w[1], v.w[2], v.w[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+    static_assert(BYTES % 16 == 0, "2, 4, 8 or a multiple of 16 bytes");
+#pragma unroll
+    for (int h = 0; h < BYTES / 16; h++) {
+      u4 x = {v.w[4 * h], v.w[4 * h + 1], v.w[4 * h + 2], v.w[4 * h + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(x, r, off + 16 * h, 0, 0);
+    }
   }
 }
 

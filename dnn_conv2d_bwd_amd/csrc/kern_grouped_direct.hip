@@ -15,58 +15,14 @@
 // group's filter slice for the class's taps (<= 9) in registers as f32.
 #include "cbd_device.h"
 #include "cbd_internal.h"
+#include "grouped_vec.h"
 
 namespace cbd {
 namespace {
 
-// Load / store `BYTES` contiguous bytes (2..32) as 32-bit words.
-template <int BYTES>
-struct Vec {
-  static constexpr int W = BYTES >= 4 ? BYTES / 4 : 1;
-  uint32_t w[W];
-};
-
-template <int BYTES>
-__device__ inline Vec<BYTES> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  Vec<BYTES> v;
-  if constexpr (BYTES == 2) {
-    v.w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  } else if constexpr (BYTES == 4) {
-    v.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  } else if constexpr (BYTES == 8) {
-    auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    v.w[0] = x[0];
-    v.w[1] = x[1];
-  } else {
-#pragma unroll
-    for (int h = 0; h < BYTES / 16; h++) {
-      auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * h, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; j++) v.w[4 * h + j] = x[j];
-    }
-  }
-  return v;
-}
-
-template <int BYTES>
-__device__ inline void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const Vec<BYTES>& v) {
-  if constexpr (BYTES == 2) {
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v.w[0], r, off, 0, 0);
-  } else if constexpr (BYTES == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(v.w[0], r, off, 0, 0);
-  } else if constexpr (BYTES == 8) {
-    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-    u2 x = {v.w[0], v.w[1]};
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
-  } else {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int h = 0; h < BYTES / 16; h++) {
-      u4 x = {v.w[4 * h], v.w[4 * h + 1], v.w[4 * h + 2], v.w[4 * h + 3]};
-      __builtin_amdgcn_raw_buffer_store_b128(x, r, off + 16 * h, 0, 0);
-    }
-  }
-}
+using grp::Vec;
+using grp::load_vec;
+using grp::store_vec;
 
 template <int DT>
 __device__ inline float elem(const uint32_t* w, int i) {

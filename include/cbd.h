@@ -83,13 +83,18 @@ typedef enum {
   CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 32 == 0, K/G <= 131072,
                                C/G % 8 == 0, at most 16 taps per class:
                                256x256x32 tiles, bf16 MFMA, 4-stage LDS */
-  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G in {1,2,4,8}, G | 256, at most
-                               9 taps per class: per-group accumulation, filter
-                               in registers; dY rows streamed through an LDS
-                               ring when C/G <= 4, a pixel is a multiple of 16
-                               bytes and a class's taps are one dY row apart;
-                               also bf16 with C/G in {16, 32} (16x16x16 MFMA,
-                               taps one dY row apart, 256-byte group slices) */
+  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G, at most 9 taps per class.
+                               Either C/G in {1,2,4,8} with G dividing 256:
+                               per-group accumulation, filter in registers, dY
+                               rows streamed through an LDS ring when C/G <= 4,
+                               a pixel is a multiple of 16 bytes and a class's
+                               taps are one dY row apart; or bf16 with C/G in
+                               {8,16,32} and G a multiple of 16, 8 or 4
+                               respectively (groups in 256-byte pixel slices,
+                               any number of slices, G > 256 included), taps
+                               one dY row apart: 16x16x16 MFMA.  The planner
+                               prefers the latter for bf16 C/G = 8 whenever it
+                               applies. */
 } cbd_kernel;
 
 typedef struct {
@@ -148,7 +153,10 @@ typedef struct {
 cbd_status cbd_plan(const cbd_problem* problem, cbd_plan_t** out_plan);
 
 /* As cbd_plan, with options (options may be NULL).  A forced kernel that
- * cannot run the problem gives UNSUPPORTED. */
+ * cannot run the problem gives UNSUPPORTED.
+ * With the environment variable CBD_LOG set (to anything but "" or "0"),
+ * every plan built is described on stderr: the problem, the kernel chosen
+ * and its launch shape, the sub-GEMMs and the zero regions. */
 cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* options,
                        cbd_plan_t** out_plan);
 
@@ -158,8 +166,10 @@ cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* optio
  * hipStream_t (NULL = the default stream).  Asynchronous and stream-ordered:
  * no host synchronisation, no allocation, no copies; safe to call from
  * several threads on distinct streams.  Errors: INVALID_ARG for NULL plan or
- * pointers; UNSUPPORTED for pointers not aligned to 16 bytes; HIP when a
- * launch fails (detail in cbd_last_error()). */
+ * pointers; UNSUPPORTED for a pointer not aligned as the plan requires
+ * (cbd_plan_info: align_dy / align_w / align_dx -- the element size for the
+ * generic family, 16 bytes otherwise); HIP when a launch fails (detail in
+ * cbd_last_error()). */
 cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                    void* stream);
 
@@ -222,6 +232,10 @@ typedef struct {
                                4x4x4 MFMA (bf16, C/G = 4, G = 32 or 64),
                                4 pipelined rows on 16x16x16 MFMA (bf16, C/G
                                = 16 or 32); other families: 0 */
+  int32_t align_dy, align_w, align_dx; /* byte alignment cbd_run requires of
+                               each pointer: the element size for the generic
+                               family (16 for dx when a zero-fill writes
+                               16-byte chunks), 16 for the other families */
 } cbd_plan_info_t;
 
 typedef struct {

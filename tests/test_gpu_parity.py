@@ -12,7 +12,6 @@ every output against its two-GEMM form (fp64 numpy matmul; that reduction
 is pinned against the oracle in test_oracle_pins.py).
 """
 import random
-import zlib
 
 import numpy as np
 import pytest
@@ -512,38 +511,48 @@ def test_fuzz_grouped_mfma(seed, count):
         done += 1
 
 
-# The grouped sweep (32 groups x 4..32 channels, 56..7 pixels, stride 1/2),
-# at batch 4, on 3000 sampled outputs of each shape.
+# The grouped sweep (32 groups x 4..32 channels, 56..7 pixels, stride 1/2)
+# at the batch the benchmark times (N = 32), so the launch configurations it
+# times (rows and columns per workgroup, grid) are the ones checked: every
+# output element against the oracle's loop nest, with the workload's
+# distributions, then again with small-integer operands, bit for bit.
 @pytest.mark.parametrize("name", [p.name for p in GROUPED_SWEEP])
-def test_grouped_sweep_sampled(name):
-    p = [q for q in GROUPED_SWEEP if q.name == name][0].with_(n=4)
-    print(f"[sweep] {name} n=4", flush=True)
-    dy, w = operands(p)
+def test_grouped_sweep_full(name):
+    p = [q for q in GROUPED_SWEEP if q.name == name][0]
+    assert p.n == 32
     pl = plan_for(p)
+    inf = pl.info()
+    print(f"[sweep] {name} n={p.n} variant={inf.variant} rows={inf.rows_per_wg} "
+          f"cols={inf.cols_per_wg} grid={inf.grid_main}", flush=True)
+    dy, w = operands(p)
     run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
-    bits = run.result_bits()  # NHWC
-    rng = np.random.default_rng(zlib.crc32(name.encode()))
-    cnt = 3000
-    pts = np.stack([rng.integers(0, p.n, cnt), rng.integers(0, p.c, cnt),
-                    rng.integers(0, p.hi, cnt), rng.integers(0, p.wi, cnt)], axis=1)
-    ref = oracle.bwd_data_at(p, dy, w, pts)
-    got = bits[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
-    ok, info = check_bf16(got, ref)
+    ok, info = check(p, run, oracle.bwd_data(p, dy, w))
     assert ok, (name, info)
+    assert run.guards_intact()
+    del dy, w
+    dy, w = operands(p, "int")
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
+    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+    got = run.result_f32()
+    assert np.array_equal(got, want.reshape(got.shape)), name
     assert run.guards_intact()
 
 
 # The 16x16x16-MFMA grouped kernel: bf16, 8 (as pairs), 16 or 32 channels
 # per group, random geometry, rows and column blocks; integer-exact.
-@pytest.mark.parametrize("seed,count", [(18, 60)])
+@pytest.mark.parametrize("seed,count", [(18, 60), (28, 40)])
 def test_fuzz_grouped_wide(seed, count):
     rng = random.Random(seed)
     done = 0
     while done < count:
         cg = rng.choice([8, 16, 32])
-        g = {8: [16, 32, 64], 16: [8, 16, 32], 32: [4, 8, 32]}[cg][rng.randint(0, 2)]
-        p = Problem("fuzz", rng.randint(1, 2), g, cg * g, cg * g, rng.randint(1, 40),
-                    rng.randint(1, 40), rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 3),
+        # group counts in slices of 256 bytes, including ones that do not
+        # divide 256 and ones above 256 (the planner picks this kernel for them)
+        g = rng.choice({8: [16, 32, 64, 48, 80, 512], 16: [8, 16, 32, 24, 40, 264],
+                        32: [4, 8, 32, 12, 20, 260]}[cg])
+        hmax = 40 if g <= 64 else 10
+        p = Problem("fuzz", rng.randint(1, 2), g, cg * g, cg * g, rng.randint(1, hmax),
+                    rng.randint(1, hmax), rng.randint(1, 3), rng.randint(1, 3), rng.randint(1, 3),
                     rng.randint(1, 3), rng.randint(0, 2), rng.randint(0, 2), rng.randint(1, 2),
                     rng.randint(1, 2), NHWC, "bf16", "u", "u", 0, 0)
         if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
@@ -661,3 +670,91 @@ def test_fuzz_no_split_integer_exact(family, seed, count):
         got = run.result_f32()
         assert np.array_equal(got, want.reshape(got.shape)), p
         assert run.guards_intact(), p
+
+
+# ------------------------------------------------------------- alignment ---
+
+@pytest.mark.parametrize("name,layout,dtype,elem_off", [
+    ("c1", NCHW, "f32", 1), ("c2-14-3", NCHW, "f32", 3), ("c3b", NCHW, "f32", 1),
+    ("c1", NHWC, "bf16", 1), ("c3a", NHWC, "bf16", 5)])
+def test_generic_unaligned_views(name, layout, dtype, elem_off):
+    """The generic family runs on tensor views that start a few elements into
+    their storage (element-aligned, not 16-byte aligned) and gives the same
+    bits as on aligned tensors, within the oracle's tolerance."""
+    p = by_name(name).with_(layout=layout, dtype=dtype)
+    print(f"[align] {name} layout={layout} {dtype} +{elem_off}", flush=True)
+    dy, w = operands(p)
+    pl = plan_for(p, cbd.KERNEL_GENERIC)
+    inf = pl.info()
+    es = 4 if dtype == "f32" else 2
+    assert inf.align_dy == es and inf.align_w == es
+    sh = pl.shapes()
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+
+    def view(a):
+        flat = torch.zeros(a.size + elem_off, dtype=tdt, device="cuda")
+        flat[elem_off:] = torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(tdt).cuda()
+        return flat[elem_off:].view(a.shape)
+    dy_v, w_v = view(dy), view(w)
+    assert (dy_v.data_ptr() % 16) != 0
+    dx_off = elem_off if inf.align_dx == es else 16 // es
+    buf = torch.full((int(np.prod(sh["dx"])) + dx_off + 64,), float("nan"), dtype=tdt, device="cuda")
+    dx_v = buf[dx_off:dx_off + int(np.prod(sh["dx"]))].view(sh["dx"])
+    cbd.run(pl, dy_v, w_v, dx_v)
+    aligned = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
+    torch.cuda.synchronize()
+    got = dx_v.cpu()
+    want = aligned.dx.cpu()
+    iv = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(got.view(iv), want.view(iv))
+    assert bool(torch.isnan(buf[:dx_off].float()).all()) and bool(torch.isnan(buf[dx_off + got.numel():].float()).all())
+    ok, info = check(p, aligned, oracle.bwd_data(p, dy, w))
+    assert ok, info
+
+
+# ------------------------------------------------------------- concurrency ---
+
+def test_concurrent_runs_on_two_streams():
+    """Two host threads, each with its own stream, call cbd_run at the same
+    time: each its own plan (generic family / grouped family) and both a
+    third plan they share (plans are immutable).  Every result equals the
+    single-threaded result bit for bit."""
+    import threading
+    names = ("c3a", "c5-s2", "c2-16-3")
+    probs = {n: by_name(n) for n in names}
+    plans = {n: plan_for(probs[n]) for n in names}
+    ins = {}
+    ref = {}
+    for n in names:
+        p = probs[n]
+        dy, w = operands(p)
+        ins[n] = (to_device(dy, p), to_device(w, p))
+        ref[n] = DeviceRun(p, plans[n], *ins[n])().result_bits().copy()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    own = ["c3a", "c5-s2"]
+    outs = [{n: DeviceRun(probs[n], plans[n], *ins[n]) for n in (own[t], "c2-16-3")} for t in range(2)]
+    torch.cuda.synchronize()
+    start = threading.Barrier(2)
+    errors = []
+
+    def worker(t):
+        try:
+            start.wait()
+            for _ in range(40):
+                for n, r in outs[t].items():
+                    cbd.run(plans[n], r.dy_d, r.w_d, r.dx, stream=streams[t])
+            streams[t].synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join(timeout=120)
+    assert not errors, errors
+    assert not any(x.is_alive() for x in th)
+    torch.cuda.synchronize()
+    for t in range(2):
+        for n, r in outs[t].items():
+            assert np.array_equal(r.result_bits(), ref[n]), (t, n)
+            assert r.guards_intact()

@@ -244,7 +244,7 @@ def test_exports_and_null_handling():
     # run-time argument checks happen before any HIP call
     base = 1 << 40
     assert cbd.run_raw(pl, 0, base, base + (1 << 30)) == 1                   # NULL dy
-    assert cbd.run_raw(pl, base + 8, base + (1 << 28), base + (1 << 30)) == 2  # misaligned
+    assert cbd.run_raw(pl, base + 2, base + (1 << 28), base + (1 << 30)) == 2  # misaligned (f32: 4 bytes)
     assert cbd.run_raw(pl, base, base + (1 << 28), base + 64) == 1           # dx overlaps dy
 
 
@@ -321,9 +321,14 @@ def test_static_shape_plans():
         cbd.plan(*args, static_shape=1, ksplit=2)
 
 
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="passes made-up device addresses to a real launch: only on a machine "
+                           "with no GPU driver at all, where the launch itself must fail")
 def test_run_without_device_returns_hip_error():
     """On a machine with no GPU, cbd_run reports CBD_ERR_HIP instead of
-    aborting (run in a child process to keep this one clean)."""
+    aborting (run in a child process to keep this one clean).  The addresses
+    are never dereferenced here: with no device the launch fails before any
+    kernel runs; where a GPU driver exists the test is skipped."""
     code = (
         "import dnn_conv2d_bwd_amd as cbd\n"
         "pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, 'nchw', 'f32')\n"
@@ -358,3 +363,59 @@ def test_generic_tile_choice():
     just_below = big.with_(hi=62, wi=64)  # 16*62*64 / 64 = 992 tiles of 64x64
     inf = plan_of(just_below).info()
     assert (inf.tile_m, inf.tile_n) == (32, 32)
+
+
+def test_grouped_beyond_256_groups_no_crash():
+    """Grouped problems the 16x16x16-MFMA kernel accepts with G > 256 (or G
+    not dividing 256): a problem with no sub-GEMM plans as zero-fill only,
+    and asking for the row / direct kernels (rows_per_wg = -1) is refused,
+    never a crash (these once divided by zero in the planner)."""
+    # 1x1 filter, stride 2, pad 1, 1x1 input: the one position is padding, no class has positions
+    for g in (512, 1024):
+        pl = cbd.plan(1, g, 8 * g, 8 * g, 1, 1, 1, 1, 2, 1, 1, "nhwc", "bf16")
+        inf = pl.info()
+        assert inf.num_subgemms == 0 and inf.grid_main == 0 and inf.grid_zero > 0
+    for g, hw in ((512, 8), (1024, 4), (48, 8)):
+        with pytest.raises(cbd.CbdError) as e:
+            cbd.plan(2, g, 8 * g, 8 * g, hw, hw, 3, 3, 1, 1, 1, "nhwc", "bf16", rows_per_wg=-1)
+        assert e.value.status == 2
+        # without the option the 16x16x16-MFMA kernel takes them
+        inf = cbd.plan(2, g, 8 * g, 8 * g, hw, hw, 3, 3, 1, 1, 1, "nhwc", "bf16").info()
+        assert inf.kernel == cbd.KERNEL_GROUPED and inf.variant == 4
+
+
+def test_alignment_requirements():
+    """Generic family: element alignment (16 bytes for dx when a zero-fill
+    writes 16-byte NHWC chunks); other families 16 bytes.  A misaligned
+    pointer is refused before anything is launched."""
+    f32 = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32").info()
+    assert (f32.kernel, f32.align_dy, f32.align_w, f32.align_dx) == (cbd.KERNEL_GENERIC, 4, 4, 4)
+    bf = cbd.plan(2, 1, 12, 12, 9, 9, 3, 3, 1, 1, 1, "nchw", "bf16", force_kernel=cbd.KERNEL_GENERIC).info()
+    assert (bf.align_dy, bf.align_w, bf.align_dx) == (2, 2, 2)
+    # NCHW zero-fill writes elements; NHWC rows of 64 f32 channels in 16-byte chunks
+    z_nchw = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nchw", "f32").info()
+    assert z_nchw.num_zero_regions == 3 and z_nchw.align_dx == 4
+    z_nhwc = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nhwc", "f32",
+                      force_kernel=cbd.KERNEL_GENERIC).info()
+    assert z_nhwc.num_zero_regions == 3 and (z_nhwc.align_dy, z_nhwc.align_dx) == (4, 16)
+    c4 = cbd.plan(16, 1, 2048, 2048, 1, 512, 1, 2, (1, 2), 0, 1, "nhwc", "bf16").info()
+    assert (c4.align_dy, c4.align_w, c4.align_dx) == (16, 16, 16)
+    pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32")
+    big = 1 << 40
+    for off in ((2, 0, 0), (0, 1, 0), (0, 0, 3)):   # refused before any launch
+        assert cbd.run_raw(pl, big + off[0], big + (1 << 28) + off[1], big + (1 << 30) + off[2]) == 2
+    assert "aligned" in cbd._lib.cbd_last_error().decode()
+
+
+def test_cbd_log_plan_dump():
+    """CBD_LOG=1 describes every plan on stderr; unset or 0 prints nothing."""
+    code = ("import dnn_conv2d_bwd_amd as cbd\n"
+            "cbd.plan(32, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, 'nchw', 'f32')\n")
+    for val, expect in (("1", True), ("0", False), ("", False)):
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                           timeout=120, env={**os.environ, "CBD_LOG": val})
+        assert r.returncode == 0, r.stderr
+        assert ("[cbd] plan:" in r.stderr) == expect, (val, r.stderr)
+        if expect:
+            assert "kernel generic" in r.stderr and "sub-GEMM 0:" in r.stderr
+            assert r.stderr.count("zero region:") == 3
