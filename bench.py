@@ -55,11 +55,11 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = {(0, 0): "kern_igemm_generic.hip", (1, 0): "kern_igemm_nhwc_bf16.hip",
               (2, 0): "kern_grouped_direct.hip", (2, 1): "kern_grouped_rows.hip",
               (2, 2): "kern_grouped_pipe.hip", (2, 3): "kern_grouped_mfma.hip",
-              (2, 4): "kern_grouped_wide.hip"}
+              (2, 4): "kern_grouped_wide.hip", (3, 0): "kern_nchw_rows.hip"}
 KERNEL_SYMBOL = {(0, 0): "igemm_generic_kernel", (1, 0): "igemm_nhwc_bf16_kernel",
                  (2, 0): "grouped_direct_kernel", (2, 1): "grouped_rows_kernel",
                  (2, 2): "grouped_pipe_kernel", (2, 3): "grouped_mfma_kernel",
-                 (2, 4): "grouped_wide_kernel"}
+                 (2, 4): "grouped_wide_kernel", (3, 0): "nchw_rows_kernel"}
 # Bound of each workload problem (dense-contraction rows on MFMA, the rest on
 # HBM; the small fp32 rows are launch-latency bound in practice).
 LATENCY_BOUND = ("c1", "c2-14-1", "c2-14-3", "c2-15-1", "c2-15-3", "c2-16-1", "c2-16-3")

@@ -28,8 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libcbd.so")
 
 NCHW, NHWC = 0, 1
 F32, BF16 = 0, 1
-KERNEL_AUTO, KERNEL_GENERIC, KERNEL_NHWC_BF16, KERNEL_GROUPED = -1, 0, 1, 2
-KERNEL_NAMES = {0: "generic", 1: "nhwc_bf16", 2: "grouped"}
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_NHWC_BF16, KERNEL_GROUPED, KERNEL_NCHW_ROWS = -1, 0, 1, 2, 3
+KERNEL_NAMES = {0: "generic", 1: "nhwc_bf16", 2: "grouped", 3: "nchw_rows"}
 
 STATUS = {0: "CBD_OK", 1: "CBD_ERR_INVALID_ARG", 2: "CBD_ERR_UNSUPPORTED", 3: "CBD_ERR_HIP",
           4: "CBD_ERR_NO_MEMORY"}

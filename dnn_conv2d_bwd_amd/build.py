@@ -29,6 +29,7 @@ SOURCES = [
     "kern_grouped_mfma.hip",
     "kern_grouped_wide.hip",
     "kern_zero_fill.hip",
+    "kern_nchw_rows.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -85,6 +85,7 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
     auto launch_main = [&](const cbd::GemmArgs& args, int64_t grid) -> int {
       switch (info.kernel) {
         case CBD_KERNEL_NHWC_BF16: return cbd::launch_nhwc_bf16(args, grid, stream);
+        case CBD_KERNEL_NCHW_ROWS: return cbd::launch_nchw_rows(args, plan->prob.dtype, grid, stream);
         case CBD_KERNEL_GROUPED:
           return args.grp_wide      ? cbd::launch_grouped_wide(args, grid, stream)
                  : args.grp_mfma    ? cbd::launch_grouped_mfma(args, grid, stream)

@@ -31,6 +31,7 @@ int launch_grouped_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream
 int launch_grouped_pipe(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_mfma(const GemmArgs& a, int64_t grid, void* stream);
 int launch_grouped_wide(const GemmArgs& a, int64_t grid, void* stream);
+int launch_nchw_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_zero_fill(const ZeroArgs& z, int64_t grid, void* stream);
 const char* hip_error_name(int err);
 
@@ -45,5 +46,9 @@ constexpr int kGroupedThreads = 256, kGroupedMaxTaps = 9;
 constexpr int kGroupedRowLds = 64 * 1024;  // one-row kernel: staged dY rows per workgroup
 constexpr int kLdsPerCu = 160 * 1024;       // gfx950 LDS per compute unit (also the per-workgroup limit)
 constexpr int kZeroThreads = 256, kZeroItemsPerThread = 2;
+constexpr int kRowsThreads = 256;
+// Row-block family staging capacity per lane: dY loads (k planes per wave
+// x 64-element chunks per plane) and 16-byte W loads.
+constexpr int kRowsMaxChunks = 4, kRowsMaxDyLoads = 64, kRowsMaxWLoads = 16;
 
 }  // namespace cbd

@@ -48,6 +48,30 @@ struct FusedZero {
   ZeroDesc reg[kMaxFusedZero];
 };
 
+// Row-block family (NCHW): workgroup = (image, group, 16-channel block, block
+// of rb dX rows); dY rows, W taps and a dX staging tile live in LDS
+// (float offsets below).  Divisions by runtime extents go through rounded-up
+// reciprocals mag = ceil(2^32 / d) as for the zero-fill.
+struct RowsGeom {
+  int32_t rb;          // dX rows per workgroup
+  int32_t row_blocks;  // ceil(Hi / rb)
+  int32_t c_blocks;    // ceil((C/G) / 16)
+  int32_t nr;          // dY rows staged (bound over every row block)
+  int32_t rw;          // staged dY columns wo_lo ... wo_lo + rw - 1
+  int32_t wo_lo;       // first staged dY column (negative: left padding)
+  int32_t kg4;         // K/G rounded up to a multiple of 16 (whole groups of four k steps)
+  int32_t ks;          // floats per staged k plane (>= nr*rw, = 16 mod 64)
+  int32_t nch;         // 64-element chunks per staged k plane (ceil(nr*rw / 64))
+  int32_t ksw;         // floats per filter row k of the W tile (>= 16*Y*X, = 16 mod 64)
+  int32_t wvec;        // 1: W staged with 16-byte loads (f32, C/G % 16 == 0)
+  int32_t cst;         // floats per dX staging channel plane (>= rb*Wi, multiple of 4)
+  int32_t w_off;       // float offset of the W tile ([kg4][ksw]: channel c, tap at c*Y*X + tap)
+  int32_t st_off;      // float offset of the dX staging tile ([16][cst])
+  int32_t vb;          // bytes per dX store (16, 8, 4 or 2)
+  int32_t lds_bytes;   // dynamic LDS per workgroup
+  uint32_t mag_plane, mag_rw, mag_perk, mag_yx, mag_perc, mag_chunks;
+};
+
 struct GemmArgs {
   // problem (element counts; every tensor is < 2^31 bytes)
   int32_t N, G, C, K, Cg, Kg;
@@ -79,11 +103,12 @@ struct GemmArgs {
   const void* dy;
   const void* w;
   void* dx;
-  FusedZero fz;
+  RowsGeom rg;
   // tile_begin of every class again, contiguous: a kernel finds its class
   // from one batch of scalar loads instead of one load per class.
   int32_t class_begin[kMaxSub];
   SubDesc sub[kMaxSub];
+  FusedZero fz;
 };
 // Kernel arguments travel in the 4 KiB kernel-argument segment.
 static_assert(sizeof(GemmArgs) <= 4096, "GemmArgs exceeds the kernel-argument segment");

@@ -105,6 +105,102 @@ bool grouped_ok(const cbd_problem& p, int64_t Cg, int64_t Kg, int64_t max_taps) 
          max_taps <= cbd::kGroupedMaxTaps;
 }
 
+// Row-block family geometry for rb dX rows per workgroup (see
+// kern_nchw_rows.hip); lds = 0 when the staged tiles cannot fit.
+cbd::RowsGeom rows_geom(const cbd_problem& p, const std::vector<cbd_subgemm_t>& subs, int64_t Cg,
+                        int64_t Kg, int64_t rb, int64_t es) {
+  cbd::RowsGeom r;
+  std::memset(&r, 0, sizeof(r));
+  int64_t wo_lo = INT64_MAX, wo_hi = INT64_MIN;
+  for (const auto& s : subs) {
+    wo_lo = std::min<int64_t>(wo_lo, s.beta_w - (int64_t)s.delta_w * (s.taps_w - 1));
+    wo_hi = std::max<int64_t>(wo_hi, 16 * ceil_div(s.pos_w, 16) + s.beta_w);
+  }
+  // Staged dY rows: the widest span over every residue of a block's first
+  // row modulo the stride (t ranges unclamped, so a superset of any block's).
+  int64_t nr = 1;
+  for (int64_t b = 0; b < p.stride_h; b++) {
+    const int64_t h0 = b * rb;
+    int64_t lo = INT64_MAX, hi = INT64_MIN;
+    for (const auto& s : subs) {
+      const int64_t num_lo = h0 - s.phase_h, num_hi = h0 + rb - 1 - s.phase_h;
+      const int64_t t_lo = num_lo >= 0 ? ceil_div(num_lo, p.stride_h) : -((-num_lo) / p.stride_h);
+      const int64_t t_hi = num_hi >= 0 ? num_hi / p.stride_h : -ceil_div(-num_hi, p.stride_h);
+      if (t_lo > t_hi) continue;
+      lo = std::min<int64_t>(lo, t_lo + s.beta_h - (int64_t)s.delta_h * (s.taps_h - 1));
+      hi = std::max<int64_t>(hi, t_hi + s.beta_h);
+    }
+    if (lo <= hi) nr = std::max<int64_t>(nr, hi - lo + 1);
+  }
+  const int64_t rw = wo_hi - wo_lo;
+  const int64_t kg4 = 16 * ceil_div(Kg, 16);  // k steps of 4 in whole groups of four
+  auto pad16 = [](int64_t v) { return v + ((16 - v % 64) % 64 + 64) % 64; };  // -> 16 (mod 64)
+  const int64_t ks = pad16(nr * rw);
+  const int64_t nch = ceil_div(nr * rw, 64);
+  const int64_t yx = p.y * p.x;
+  const int64_t ksw = pad16(16 * yx);
+  const bool wvec = es == 4 && Cg % 16 == 0 && kg4 * 4 * yx <= int64_t(cbd::kRowsMaxWLoads) * cbd::kRowsThreads;
+  const int64_t cst = pad16(rb * p.wi);
+  const int64_t lds = 4 * (kg4 * ks + kg4 * ksw + 16 * cst);
+  const int64_t rowb = p.wi * es;
+  const int64_t vb = rowb % 16 == 0 ? 16 : rowb % 8 == 0 ? 8 : rowb % 4 == 0 ? 4 : 2;
+  const int64_t chunks = p.wi / (vb / es);
+  // Each wave stages kg4/4 dY planes of nch chunks from registers.
+  if (nch > cbd::kRowsMaxChunks || (kg4 / 4) * cbd::kRowsMaxChunks > cbd::kRowsMaxDyLoads) return r;
+  if (lds > cbd::kLdsPerCu || 16 * rb * chunks >= (int64_t(1) << 31)) return r;
+  r.rb = (int32_t)rb;
+  r.row_blocks = (int32_t)ceil_div(p.hi, rb);
+  r.c_blocks = (int32_t)ceil_div(Cg, 16);
+  r.nr = (int32_t)nr;
+  r.rw = (int32_t)rw;
+  r.wo_lo = (int32_t)wo_lo;
+  r.kg4 = (int32_t)kg4;
+  r.ks = (int32_t)ks;
+  r.nch = (int32_t)nch;
+  r.ksw = (int32_t)ksw;
+  r.wvec = wvec ? 1 : 0;
+  r.cst = (int32_t)cst;
+  r.w_off = (int32_t)(kg4 * ks);
+  r.st_off = (int32_t)(kg4 * ks + kg4 * ksw);
+  r.vb = (int32_t)vb;
+  r.lds_bytes = (int32_t)lds;
+  r.mag_plane = magic32(nr * rw);
+  r.mag_rw = magic32(rw);
+  r.mag_perk = magic32(16 * p.y * p.x);
+  r.mag_yx = magic32(p.y * p.x);
+  r.mag_perc = magic32(rb * chunks);
+  r.mag_chunks = magic32(chunks);
+  return r;
+}
+
+// Rows per workgroup for the row-block family, as B balanced blocks of
+// ceil(Hi / B) rows: the fewest blocks that give 256 workgroups (one per CU);
+// when no B does, the most blocks whose first block still holds four
+// 16-position units (one per wave).  lds = 0 if no block size fits LDS.
+cbd::RowsGeom rows_choose(const cbd_problem& p, const std::vector<cbd_subgemm_t>& subs, int64_t Cg, int64_t Kg,
+                          int64_t es) {
+  cbd::RowsGeom best, fallback;
+  std::memset(&best, 0, sizeof(best));
+  std::memset(&fallback, 0, sizeof(fallback));
+  if (subs.empty()) return best;
+  const int64_t cb = ceil_div(Cg, 16);
+  const int64_t bmax = std::min<int64_t>(p.hi, 4096);
+  for (int64_t nb = 1; nb <= bmax; nb++) {
+    const int64_t rb = ceil_div(p.hi, nb);
+    if (ceil_div(p.hi, rb) != nb) continue;  // the same blocks as a smaller count
+    const cbd::RowsGeom g = rows_geom(p, subs, Cg, Kg, rb, es);
+    if (g.lds_bytes == 0) continue;
+    if (p.n * p.g * cb * nb >= 256) return g;
+    int64_t units = 0;
+    for (const auto& s : subs)
+      for (int64_t h = s.phase_h; h < rb; h += p.stride_h)
+        if ((h - s.phase_h) / p.stride_h < s.pos_h) units += ceil_div(s.pos_w, 16);
+    if (units >= 4) best = g;
+    if (fallback.lds_bytes == 0) fallback = g;
+  }
+  return best.lds_bytes ? best : fallback;
+}
+
 // CBD_LOG set to anything but "" or "0": every plan built is described on
 // stderr (problem, kernel choice, launch shape, sub-GEMMs, zero regions) --
 // which kernel runs a problem, and why it runs at the speed it does, without
@@ -120,6 +216,7 @@ bool log_enabled() {
 const char* kernel_name(int32_t k, int64_t variant) {
   if (k == CBD_KERNEL_NHWC_BF16) return "nhwc_bf16 (256x256 tiles)";
   if (k == CBD_KERNEL_GENERIC) return "generic";
+  if (k == CBD_KERNEL_NCHW_ROWS) return "nchw_rows (row blocks)";
   static const char* const grouped[] = {"grouped/direct", "grouped/rows", "grouped/pipelined-dot",
                                         "grouped/pipelined-4x4x4-mfma", "grouped/pipelined-16x16x16-mfma"};
   return variant >= 0 && variant < 5 ? grouped[variant] : "grouped";
@@ -197,7 +294,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       return fail(CBD_ERR_INVALID_ARG, "options.no_split must be 0 or 1");
     no_split = options->no_split == 1;
     force = options->force_kernel;
-    if (force < CBD_KERNEL_AUTO || force > CBD_KERNEL_GROUPED)
+    if (force < CBD_KERNEL_AUTO || force > CBD_KERNEL_NCHW_ROWS)
       return fail(CBD_ERR_INVALID_ARG, "unknown force_kernel");
   }
   if (p.n < 1 || p.g < 1 || p.c < 1 || p.k < 1 || p.hi < 1 || p.wi < 1 || p.y < 1 || p.x < 1)
@@ -295,8 +392,14 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   std::stable_sort(subs.begin(), subs.end(),
                    [](const cbd_subgemm_t& x, const cbd_subgemm_t& y) { return x.k > y.k; });
 
-  // Kernel family.
+  // Kernel family.  The row-block family is chosen only when forced: on
+  // every NCHW problem measured it ran slower than the implicit GEMM (its
+  // staging, one workgroup per row block and 16 channels, is latency bound).
   int kernel;
+  const bool rows_able = p.layout == CBD_LAYOUT_NCHW && !no_split && !per_class && ksplit_opt < 2;
+  cbd::RowsGeom rgeom;
+  std::memset(&rgeom, 0, sizeof(rgeom));
+  if (rows_able && force == CBD_KERNEL_NCHW_ROWS) rgeom = rows_choose(p, subs, Cg, Kg, es);
   if (force == CBD_KERNEL_AUTO) {
     if (fast_ok(p, Cg, Kg, max_taps) && Cg >= 128)
       kernel = CBD_KERNEL_NHWC_BF16;
@@ -307,6 +410,11 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       kernel = CBD_KERNEL_GENERIC;
   } else {
     kernel = force;
+    if (kernel == CBD_KERNEL_NCHW_ROWS && rgeom.lds_bytes == 0) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "row-block kernel needs NCHW, the residue split without per_class "
+                                       "or ksplit, at least one sub-GEMM, and its staged tiles within LDS");
+    }
     if (kernel == CBD_KERNEL_NHWC_BF16 && !fast_ok(p, Cg, Kg, max_taps)) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "NHWC bf16 kernel needs NHWC, bf16, K/G % 64 == 0, C/G % 8 == 0, <= 16 taps per class");
@@ -366,6 +474,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     }
   } else if (kernel == CBD_KERNEL_NHWC_BF16) {
     bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;
+  } else if (kernel == CBD_KERNEL_NCHW_ROWS) {
+    bm = 16; bn = 16; bk = 4; threads = cbd::kRowsThreads;
   } else {
     threads = cbd::kGroupedThreads;
   }
@@ -560,7 +670,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     cbd_subgemm_t& s = subs[i];
     s.id = (int32_t)i;
     s.tile_begin = tile;
-    if (kernel == CBD_KERNEL_GROUPED)
+    if (kernel == CBD_KERNEL_NCHW_ROWS)
+      s.tiles = 0, s.tile_begin = 0;  // every workgroup serves every class
+    else if (kernel == CBD_KERNEL_GROUPED)
       s.tiles = grp_wide      ? p.n * ceil_div(s.pos_h, grp_rows) * (p.g / (256 / (2 * Cg))) *
                                     ceil_div(s.pos_w, grp_cols)
                 : grp_mfma      ? p.n * ceil_div(s.pos_h, grp_rows) * ceil_div(s.pos_w, grp_cols)
@@ -573,6 +685,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     if (s.k != subs[0].k) equal_k = false;
     exec += p.g * s.m * s.n * s.k;
   }
+  if (kernel == CBD_KERNEL_NCHW_ROWS) tile = p.n * p.g * rgeom.c_blocks * rgeom.row_blocks;
   // A launch must stay below 2^32 work-items.
   if (tile * threads >= (int64_t(1) << 32)) {
     delete pl;
@@ -677,6 +790,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   // launch as extra workgroups (one launch instead of two).
   int64_t grid_zero = ceil_div(items, int64_t(cbd::kZeroThreads) * cbd::kZeroItemsPerThread);
   int64_t grid_main = tile;
+  // The row-block family writes unreached positions itself.
+  if (kernel == CBD_KERNEL_NCHW_ROWS) grid_zero = 0;
+  a.rg = rgeom;
   std::memset(&a.fz, 0, sizeof(a.fz));
   if (kernel == CBD_KERNEL_GENERIC && !per_class && items > 0 &&
       (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
@@ -710,8 +826,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.useful_flops = 2 * p.n * p.c * Kg * Ho * Wo * p.y * p.x;
   info.executed_macs = exec;
   info.zero_elems = zero_elems;
-  info.lds_dynamic = grp_lds;
-  info.rows_per_wg = grp_rows;
+  info.lds_dynamic = kernel == CBD_KERNEL_NCHW_ROWS ? rgeom.lds_bytes : grp_lds;
+  info.rows_per_wg = kernel == CBD_KERNEL_NCHW_ROWS ? rgeom.rb : grp_rows;
   info.cols_per_wg = grp_cols;
   info.ksplit = ksplit;
   info.static_shape = static_shape;
@@ -722,6 +838,12 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   if (kernel == CBD_KERNEL_GENERIC) {
     info.align_dy = info.align_w = (int32_t)es;
     info.align_dx = (zero_elems > 0 && z.chunk == 16) ? 16 : (int32_t)es;
+  } else if (kernel == CBD_KERNEL_NCHW_ROWS) {
+    // element loads of dY (16-byte loads of W when its rows allow);
+    // whole dX rows in the widest store that divides a row
+    info.align_dy = (int32_t)es;
+    info.align_w = rgeom.wvec ? 16 : (int32_t)es;
+    info.align_dx = rgeom.vb;
   } else {
     info.align_dy = info.align_w = info.align_dx = 16;
   }

@@ -83,7 +83,7 @@ typedef enum {
   CBD_KERNEL_NHWC_BF16 = 1, /* NHWC bf16, K/G % 32 == 0, K/G <= 131072,
                                C/G % 8 == 0, at most 16 taps per class:
                                256x256x32 tiles, bf16 MFMA, 4-stage LDS */
-  CBD_KERNEL_GROUPED = 2    /* NHWC, C/G == K/G, at most 9 taps per class.
+  CBD_KERNEL_GROUPED = 2,   /* NHWC, C/G == K/G, at most 9 taps per class.
                                Either C/G in {1,2,4,8} with G dividing 256:
                                per-group accumulation, filter in registers, dY
                                rows streamed through an LDS ring when C/G <= 4,
@@ -95,6 +95,17 @@ typedef enum {
                                one dY row apart: 16x16x16 MFMA.  The planner
                                prefers the latter for bf16 C/G = 8 whenever it
                                applies. */
+  CBD_KERNEL_NCHW_ROWS = 3  /* NCHW / KCYX, f32 or bf16, residue split (no
+                               no_split, per_class or ksplit): a workgroup owns
+                               whole dX rows of 16 channels of one image and
+                               group, stages the dY rows and all W taps it
+                               needs in LDS and computes every class from
+                               there (16x16x4 f32 MFMA); unreached positions
+                               are written in the same rows (no zero-fill
+                               launch).  Needs the staged tiles to fit LDS;
+                               used only when forced (slower than the
+                               generic family on the NCHW problems
+                               measured). */
 } cbd_kernel;
 
 typedef struct {
@@ -219,7 +230,8 @@ typedef struct {
   int64_t lds_dynamic;      /* dynamic LDS bytes per workgroup of the main
                                launch (grouped family: 0 for the direct kernel) */
   int64_t rows_per_wg;      /* grouped family: output rows per workgroup of the
-                               pipelined row kernels (0: another kernel) */
+                               pipelined row kernels; row-block family: dX rows
+                               per workgroup (0: another kernel) */
   int64_t cols_per_wg;      /* grouped family, MFMA pipelined kernels: positions
                                per column block of a row (0: other kernels) */
   int64_t ksplit;           /* workgroups per tile of a split-K plan (1: none) */
@@ -249,7 +261,9 @@ typedef struct {
   int64_t pos_h, pos_w;     /* positions per axis: ceil((Hi - phase) / S) */
   int64_t m, n, k;          /* per-group GEMM: M = C/G, N = N*pos_h*pos_w,
                                K = (K/G)*taps_h*taps_w */
-  int64_t tile_begin, tiles;/* this class's workgroups in the main launch */
+  int64_t tile_begin, tiles;/* this class's workgroups in the main launch (row-
+                               block family: 0, 0 -- every workgroup serves
+                               every class in its rows) */
 } cbd_subgemm_t;
 
 typedef struct {

@@ -144,6 +144,9 @@ int main(void) {
   /* fp32 NCHW 1x1 stride 2 (three zero phases, folded zero-fill) */
   fails += run_case("f32-nchw-1x1-s2", mk(2, 1, 16, 16, 14, 14, 1, 1, 2, 2, 0, 0, CBD_LAYOUT_NCHW, CBD_F32),
                     CBD_KERNEL_GENERIC);
+  /* fp32 NHWC 3x3 stride 2 with 3 groups (generic family) */
+  fails += run_case("f32-nhwc-grouped-generic", mk(2, 3, 24, 18, 11, 9, 3, 3, 2, 2, 1, 1, CBD_LAYOUT_NHWC, CBD_F32),
+                    CBD_KERNEL_GENERIC);
   /* bf16 NHWC 1x2 stride (1,2): the large-tile kernel */
   fails += run_case("bf16-nhwc-1x2", mk(2, 1, 256, 64, 1, 64, 1, 2, 1, 2, 0, 0, CBD_LAYOUT_NHWC, CBD_BF16),
                     CBD_KERNEL_NHWC_BF16);

@@ -55,7 +55,7 @@ int main(int argc, char** argv) {
     p.dtype = (int32_t)(rng() % 50 == 0 ? 9 : uni(0, 1));
     cbd_plan_options o;
     std::memset(&o, 0, sizeof(o));
-    o.force_kernel = (int32_t)uni(-1, 2);
+    o.force_kernel = (int32_t)uni(-1, 3);
     o.no_split = rng() % 8 == 0;
     o.rows_per_wg = (int32_t)pick({0, 0, 0, -1, 1, 3, 64});
     o.grouped_dot = rng() % 6 == 0;
@@ -76,13 +76,20 @@ int main(int argc, char** argv) {
     for (int32_t i = 0; i < in.num_subgemms; i++) {
       cbd_subgemm_t s;
       if (cbd_plan_subgemm(pl, i, &s) != CBD_OK || s.id != i) return fail("subgemm id", p);
-      if (s.m <= 0 || s.n <= 0 || s.k <= 0 || s.tiles <= 0) return fail("empty sub-GEMM", p);
-      if (s.tile_begin != tiles) return fail("tile ranges not contiguous", p);
+      if (s.m <= 0 || s.n <= 0 || s.k <= 0) return fail("empty sub-GEMM", p);
+      if (in.kernel == CBD_KERNEL_NCHW_ROWS) {
+        if (s.tiles != 0 || s.tile_begin != 0) return fail("row-block classes own no tile range", p);
+      } else {
+        if (s.tiles <= 0) return fail("sub-GEMM without tiles", p);
+        if (s.tile_begin != tiles) return fail("tile ranges not contiguous", p);
+      }
       tiles += s.tiles;
       macs += p.g * s.m * s.n * s.k;
     }
     if (macs != in.executed_macs) return fail("executed MACs", p);
     if (in.num_subgemms > 0 && in.grid_main < tiles) return fail("grid below tile count", p);
+    if (in.kernel == CBD_KERNEL_NCHW_ROWS && (in.grid_zero != 0 || in.lds_dynamic <= 0 || in.lds_dynamic > 160 * 1024))
+      return fail("row-block launch shape", p);
     if (in.num_subgemms == 0 && in.grid_main != 0 && in.grid_zero != 0) return fail("grid without sub-GEMM", p);
     for (int32_t i = 0; i < in.num_zero_regions; i++) {
       cbd_zero_region_t z;

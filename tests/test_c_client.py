@@ -27,4 +27,4 @@ def test_c_client_end_to_end():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "CLIENT OK" in r.stdout
-    assert r.stdout.count(" 0 mismatches") == 4
+    assert r.stdout.count(" 0 mismatches") == 5

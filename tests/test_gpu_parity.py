@@ -61,10 +61,12 @@ def spatial(p, a):
 # --------------------------------------------------------------- workload ---
 
 @pytest.mark.parametrize("name", SMALL)
-@pytest.mark.parametrize("force", [cbd.KERNEL_AUTO, cbd.KERNEL_GENERIC])
+@pytest.mark.parametrize("force", [cbd.KERNEL_AUTO, cbd.KERNEL_GENERIC, cbd.KERNEL_NCHW_ROWS])
 def test_workload_vs_oracle(name, force):
     p = by_name(name)
-    print(f"[parity] {name} force={force}", flush=True)
+    if force == cbd.KERNEL_NCHW_ROWS and p.layout != NCHW:
+        pytest.skip("the row-block family serves NCHW problems only")
+    print(f"[parity] {name} force={force} kernel={plan_for(p, force).info().kernel}", flush=True)
     dy, w = operands(p)
     ref = oracle.bwd_data(p, dy, w)
     pl = plan_for(p, force)
@@ -282,8 +284,9 @@ def test_per_class_launches_match_single_launch(name):
     print(f"[per-class] {name}", flush=True)
     dy, w = operands(p)
     dy_d, w_d = to_device(dy, p), to_device(w, p)
-    one = DeviceRun(p, plan_for(p), dy_d, w_d)()
+    # the same family on both sides
     pl = plan_for(p, per_class=True)
+    one = DeviceRun(p, plan_for(p, pl.info().kernel), dy_d, w_d)()
     assert pl.info().launches >= pl.info().num_subgemms
     many = DeviceRun(p, pl, dy_d, w_d)()
     assert np.array_equal(one.result_bits(), many.result_bits())
@@ -373,6 +376,10 @@ def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), 
             kg = cg
             g = rng.choice([1, 2, 4, 8, 16, 32, 64])
             layout = NHWC
+        elif family == cbd.KERNEL_NCHW_ROWS:
+            g = rng.randint(1, 4)
+            cg, kg = rng.randint(1, 40), rng.randint(1, 40)
+            layout = NCHW
         else:
             g = rng.randint(1, 4)
             cg, kg = rng.randint(1, 40), rng.randint(1, 40)
@@ -383,7 +390,7 @@ def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), 
         if (p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0
                 or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0):
             continue
-        if family in (cbd.KERNEL_GROUPED, cbd.KERNEL_NHWC_BF16):
+        if family in (cbd.KERNEL_GROUPED, cbd.KERNEL_NHWC_BF16, cbd.KERNEL_NCHW_ROWS):
             try:
                 if plan_for(p, family).info().kernel != family:
                     continue
@@ -397,6 +404,7 @@ def fuzz_problems(seed, count, *, layouts=(NCHW, NHWC), dtypes=("f32", "bf16"), 
     (cbd.KERNEL_GENERIC, 11, 150),
     (cbd.KERNEL_NHWC_BF16, 12, 60),
     (cbd.KERNEL_GROUPED, 13, 80),
+    (cbd.KERNEL_NCHW_ROWS, 14, 150),
 ])
 def test_fuzz_integer_exact(family, seed, count):
     for i, p in enumerate(fuzz_problems(seed, count, family=family)):
@@ -418,6 +426,7 @@ def test_fuzz_integer_exact(family, seed, count):
     (cbd.KERNEL_GENERIC, 21, 60),
     (cbd.KERNEL_NHWC_BF16, 22, 30),
     (cbd.KERNEL_GROUPED, 23, 40),
+    (cbd.KERNEL_NCHW_ROWS, 24, 60),
 ])
 def test_fuzz_random_values(family, seed, count):
     for i, p in enumerate(fuzz_problems(seed, count, family=family)):

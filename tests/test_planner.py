@@ -131,31 +131,48 @@ def test_workload_plans():
         "c5-s2": (4, 0, cbd.KERNEL_GROUPED), "c5-s1": (1, 0, cbd.KERNEL_GROUPED),
     }
     for p in PROBLEMS:
-        pl = plan_of(p)
-        info = pl.info()
-        ho, wo = oracle.out_hw(p)
-        assert (info.ho, info.wo) == (ho, wo)
-        assert info.useful_flops == 2 * p.n * p.c * (p.k // p.g) * ho * wo * p.y * p.x
-        subs = pl.subgemms()
-        assert [s.id for s in subs] == list(range(len(subs)))
-        assert all(subs[i].k >= subs[i + 1].k for i in range(len(subs) - 1))  # LPT
-        tiles = 0
-        for s in subs:
-            assert s.tile_begin == tiles
-            tiles += s.tiles
-        # the generic family folds the zero-fill workgroups into its launch
-        fused = info.num_zero_regions > 0 and info.grid_zero == 0
-        zero_wgs = -(-info.zero_elems // (256 * 2)) if fused and p.layout == NCHW else 0
-        assert tiles + zero_wgs == info.grid_main
-        assert info.launches == 1 + (info.grid_zero > 0)
+        forces = (cbd.KERNEL_AUTO, cbd.KERNEL_GENERIC) + ((cbd.KERNEL_NCHW_ROWS,) if p.layout == NCHW else ())
+        for force in forces:
+            pl = plan_of(p, force)
+            info = pl.info()
+            ho, wo = oracle.out_hw(p)
+            assert (info.ho, info.wo) == (ho, wo)
+            assert info.useful_flops == 2 * p.n * p.c * (p.k // p.g) * ho * wo * p.y * p.x
+            subs = pl.subgemms()
+            assert [s.id for s in subs] == list(range(len(subs)))
+            assert all(subs[i].k >= subs[i + 1].k for i in range(len(subs) - 1))  # LPT
+            assert info.launches == 1 + (info.grid_zero > 0)
+            if info.kernel == cbd.KERNEL_NCHW_ROWS:
+                # workgroups = images x groups x 16-channel blocks x row blocks;
+                # unreached phases written by the same launch
+                assert all(s.tiles == 0 and s.tile_begin == 0 for s in subs)
+                assert info.grid_main == (p.n * p.g * -(-(p.c // p.g) // 16)
+                                          * -(-p.hi // info.rows_per_wg))
+                assert info.grid_zero == 0 and 0 < info.lds_dynamic <= 160 * 1024
+                continue
+            tiles = 0
+            for s in subs:
+                assert s.tile_begin == tiles
+                tiles += s.tiles
+            # the generic family folds the zero-fill workgroups into its launch
+            fused = info.num_zero_regions > 0 and info.grid_zero == 0
+            zero_wgs = -(-info.zero_elems // (256 * 2)) if fused and p.layout == NCHW else 0
+            assert tiles + zero_wgs == info.grid_main
         if p.name in expect:
+            info = plan_of(p).info()
             assert (info.num_subgemms, info.num_zero_regions, info.kernel) == expect[p.name]
     c4 = plan_of([q for q in PROBLEMS if q.name == "c4"][0])
     assert [(s.m, s.n, s.k) for s in c4.subgemms()] == [(2048, 4096, 2048)] * 2
     assert c4.info().grid_main == 256 and c4.info().executed_macs * 2 == c4.info().useful_flops
-    c3b = plan_of([q for q in PROBLEMS if q.name == "c3b"][0])
-    assert c3b.info().zero_elems == 32 * 64 * 28 * 28 * 3 // 4
-    assert c3b.info().launches == 1 and c3b.info().grid_zero == 0  # zero-fill folded in
+    c3b_p = [q for q in PROBLEMS if q.name == "c3b"][0]
+    for force in (cbd.KERNEL_AUTO, cbd.KERNEL_GENERIC):
+        c3b = plan_of(c3b_p, force)
+        assert c3b.info().zero_elems == 32 * 64 * 28 * 28 * 3 // 4
+        assert c3b.info().launches == 1 and c3b.info().grid_zero == 0  # zeros in the main launch
+    # the row-block family (forced only): one workgroup per CU, balanced row blocks
+    rows = {q.name: plan_of(q, cbd.KERNEL_NCHW_ROWS).info() for q in PROBLEMS if q.layout == NCHW}
+    assert {n: (i.grid_main, i.rows_per_wg) for n, i in rows.items() if n in ("c1", "c2-14-3", "c3a", "c3b")} \
+        == {"c1": (8, 4), "c2-14-3": (256, 4), "c3a": (256, 14), "c3b": (256, 14)}
 
 
 def test_forced_kernels():
@@ -349,19 +366,19 @@ def test_generic_tile_choice():
     from cbd_inputs.problems import Problem as P_
     small = [q for q in PROBLEMS if q.name in ("c2-14-3", "c3a", "c3b")]
     for q in small:
-        inf = plan_of(q).info()
+        inf = plan_of(q, cbd.KERNEL_GENERIC).info()
         assert (inf.tile_m, inf.tile_n, inf.tile_k) == (32, 32, 8), q.name
-    c1 = plan_of([q for q in PROBLEMS if q.name == "c1"][0]).info()
+    c1 = plan_of([q for q in PROBLEMS if q.name == "c1"][0], cbd.KERNEL_GENERIC).info()
     assert (c1.tile_m, c1.tile_n, c1.tile_k) == (16, 16, 8)
     # eight waves per workgroup only for long K (>= 32 k tiles) on small grids
-    waves = {q.name: plan_of(q).info().threads_main // 64 for q in PROBLEMS[:9]}
+    waves = {q.name: plan_of(q, cbd.KERNEL_GENERIC).info().threads_main // 64 for q in PROBLEMS[:9]}
     assert waves == {"c1": 4, "c2-14-1": 4, "c2-14-3": 8, "c2-15-1": 4, "c2-15-3": 8,
                      "c2-16-1": 4, "c2-16-3": 8, "c3a": 4, "c3b": 4}
     big = P_("g64", 16, 1, 64, 64, 64, 64, 1, 1, 1, 1, 0, 0, 1, 1, NCHW, "f32", "u", "u", 0, 0)
-    inf = plan_of(big).info()
+    inf = plan_of(big, cbd.KERNEL_GENERIC).info()
     assert (inf.tile_m, inf.tile_n, inf.tile_k, inf.grid_main) == (64, 64, 16, 1024)
     just_below = big.with_(hi=62, wi=64)  # 16*62*64 / 64 = 992 tiles of 64x64
-    inf = plan_of(just_below).info()
+    inf = plan_of(just_below, cbd.KERNEL_GENERIC).info()
     assert (inf.tile_m, inf.tile_n) == (32, 32)
 
 
@@ -388,19 +405,28 @@ def test_alignment_requirements():
     """Generic family: element alignment (16 bytes for dx when a zero-fill
     writes 16-byte NHWC chunks); other families 16 bytes.  A misaligned
     pointer is refused before anything is launched."""
-    f32 = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32").info()
+    f32 = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC).info()
     assert (f32.kernel, f32.align_dy, f32.align_w, f32.align_dx) == (cbd.KERNEL_GENERIC, 4, 4, 4)
+    # row-block family (forced): element loads of dY, 16-byte loads of W when its
+    # 16-channel blocks are whole (f32), dx stores as wide as a dX row allows
+    for wi, vb in ((14, 8), (15, 4), (16, 16)):
+        r = cbd.plan(2, 1, 16, 16, 14, wi, 3, 3, 1, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_NCHW_ROWS).info()
+        assert (r.kernel, r.align_dy, r.align_w, r.align_dx) == (cbd.KERNEL_NCHW_ROWS, 4, 16, vb)
+    r = cbd.plan(2, 1, 12, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_NCHW_ROWS).info()
+    assert (r.kernel, r.align_dy, r.align_w, r.align_dx) == (cbd.KERNEL_NCHW_ROWS, 4, 4, 8)
+    r = cbd.plan(2, 1, 16, 16, 14, 15, 3, 3, 1, 1, 1, "nchw", "bf16", force_kernel=cbd.KERNEL_NCHW_ROWS).info()
+    assert (r.kernel, r.align_dy, r.align_dx) == (cbd.KERNEL_NCHW_ROWS, 2, 2)
     bf = cbd.plan(2, 1, 12, 12, 9, 9, 3, 3, 1, 1, 1, "nchw", "bf16", force_kernel=cbd.KERNEL_GENERIC).info()
     assert (bf.align_dy, bf.align_w, bf.align_dx) == (2, 2, 2)
     # NCHW zero-fill writes elements; NHWC rows of 64 f32 channels in 16-byte chunks
-    z_nchw = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nchw", "f32").info()
+    z_nchw = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC).info()
     assert z_nchw.num_zero_regions == 3 and z_nchw.align_dx == 4
     z_nhwc = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nhwc", "f32",
                       force_kernel=cbd.KERNEL_GENERIC).info()
     assert z_nhwc.num_zero_regions == 3 and (z_nhwc.align_dy, z_nhwc.align_dx) == (4, 16)
     c4 = cbd.plan(16, 1, 2048, 2048, 1, 512, 1, 2, (1, 2), 0, 1, "nhwc", "bf16").info()
     assert (c4.align_dy, c4.align_w, c4.align_dx) == (16, 16, 16)
-    pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32")
+    pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC)
     big = 1 << 40
     for off in ((2, 0, 0), (0, 1, 0), (0, 0, 3)):   # refused before any launch
         assert cbd.run_raw(pl, big + off[0], big + (1 << 28) + off[1], big + (1 << 30) + off[2]) == 2
