@@ -261,8 +261,9 @@ def main():
                     help="time the calls issued one by one on the stream instead of replayed "
                          "from a captured HIP graph")
     ap.add_argument("--ksplit", type=int, default=0,
-                    help="large-tile kernel: split each tile's K loop over this many workgroups "
-                         "(f32 workspace + finalising kernel)")
+                    help="large-tile or generic kernel: split each tile's K loop over this many "
+                         "workgroups (f32 workspace + finalising kernel); 0 the planner's choice "
+                         "(a workspace is passed whenever the plan asks for one), 1 never")
     ap.add_argument("--static-shape", type=int, default=0, choices=(-1, 0, 1),
                     help="large-tile kernel: shape-specialised instance when one matches (0), "
                          "required (1) or never, i.e. the descriptor-driven kernel (-1)")
@@ -322,6 +323,8 @@ def main():
     dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
     ws = (torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
           if pl.workspace_size() else None)
+    # with a workspace the plan runs its split configuration, if it has one
+    eff_ksplit = info.ksplit if info.ksplit > 1 else (info.auto_ksplit if ws is not None else 1)
     stream = torch.cuda.current_stream()
 
     if args.copy_calibration_mib:
@@ -391,7 +394,7 @@ def main():
     roof["traffic"] = read_traffic(kernel_key(info), p.name) if not (args.batch or args.no_split) else None
     roof["kernel"] = KERNEL_SYMBOL[kernel_key(info)]
     roof["launch_us_mean"] = round(launch_s * 1e6, 3)
-    roof["launches_per_step"] = info.launches
+    roof["launches_per_step"] = info.launches + (eff_ksplit > info.ksplit)
 
     out = {
         "metric": METRIC,
@@ -413,7 +416,7 @@ def main():
                    "kernel": cbd.KERNEL_NAMES[info.kernel], "subgemms": info.num_subgemms,
                    "zero_regions": info.num_zero_regions, "grid": info.grid_main,
                    "rows_per_wg": info.rows_per_wg, "cols_per_wg": info.cols_per_wg,
-                   "ksplit": info.ksplit, "launches": info.launches,
+                   "ksplit": eff_ksplit, "launches": info.launches + (eff_ksplit > info.ksplit),
                    "static_shape": info.static_shape,
                    "useful_gflop": round(flops / 1e9, 4),
                    "executed_gmac": round(info.executed_macs / 1e9, 4),

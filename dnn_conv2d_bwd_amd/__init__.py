@@ -72,7 +72,8 @@ class PlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64),
                 ("variant", ctypes.c_int64),
                 ("align_dy", ctypes.c_int32), ("align_w", ctypes.c_int32),
-                ("align_dx", ctypes.c_int32)]
+                ("align_dx", ctypes.c_int32),
+                ("auto_ksplit", ctypes.c_int64), ("auto_workspace_bytes", ctypes.c_int64)]
 
 
 class SubGemm(ctypes.Structure):
@@ -174,7 +175,9 @@ class Plan:
         return self._h
 
     def workspace_size(self) -> int:
-        """Device workspace bytes cbd_run_ws needs (0: none)."""
+        """Device workspace bytes for the plan's fastest configuration
+        (required for an explicit ksplit >= 2; otherwise enables the
+        planner's split configuration; 0: none)."""
         out = ctypes.c_uint64()
         _check(_lib.cbd_plan_workspace_size(self._h, ctypes.byref(out)), "cbd_plan_workspace_size")
         return int(out.value)
@@ -247,8 +250,10 @@ def _check_tensor(t, shape, dt, name):
 
 def run(p: Plan, dy, w, dx, stream=None, workspace=None) -> None:
     """dx <- conv_bwd_data(dy, w) on `stream` (default: torch's current stream).
-    workspace: a device tensor of at least p.workspace_size() bytes, for
-    split-K plans (cbd_run_ws); None otherwise."""
+    workspace: a device tensor for cbd_run_ws -- required (at least
+    p.workspace_size() bytes) for a plan with an explicit ksplit >= 2;
+    otherwise optional, and with at least p.workspace_size() bytes the plan
+    runs the planner's split-K configuration; None: cbd_run."""
     import torch
 
     sh = p.shapes()

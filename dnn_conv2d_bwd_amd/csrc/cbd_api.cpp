@@ -116,7 +116,10 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
       return CBD_ERR_HIP;
     }
     if (a.ksplit > 1) {
-      const int ferr = cbd::launch_splitk_finalize(a, plan->grid_finalize, stream);
+      const int ferr =
+          info.kernel == CBD_KERNEL_GENERIC
+              ? cbd::launch_generic_finalize(a, plan->prob.layout, plan->prob.dtype, plan->grid_finalize, stream)
+              : cbd::launch_splitk_finalize(a, plan->grid_finalize, stream);
       if (ferr) {
         cbd::set_error(std::string("split-K finalising launch failed: ") + cbd::hip_error_name(ferr));
         return CBD_ERR_HIP;
@@ -145,6 +148,10 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
 
 extern "C" cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                                  void* workspace, uint64_t workspace_bytes, void* stream) {
+  // The planner's split configuration when the workspace holds it.
+  if (plan && plan->split_alt && workspace &&
+      workspace_bytes >= (uint64_t)plan->split_alt->info.workspace_bytes)
+    return run_impl(plan->split_alt, dy, w, dx, workspace, workspace_bytes, stream);
   return run_impl(plan, dy, w, dx, workspace, workspace_bytes, stream);
 }
 
@@ -153,6 +160,7 @@ extern "C" cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* 
     cbd::set_error("NULL plan or output");
     return CBD_ERR_INVALID_ARG;
   }
-  *bytes = (uint64_t)plan->info.workspace_bytes;
+  *bytes = (uint64_t)(plan->info.workspace_bytes > 0 ? plan->info.workspace_bytes
+                                                      : plan->info.auto_workspace_bytes);
   return CBD_OK;
 }

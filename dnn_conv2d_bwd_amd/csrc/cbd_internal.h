@@ -15,6 +15,13 @@ struct cbd_plan_s {
   cbd::ZeroArgs zero;
   int64_t grid_finalize = 0;             // split-K finalising launch (0: none)
   bool per_class = false;                // one main launch per class (ablation)
+  // The planner's split-K configuration of the same problem, run by
+  // cbd_run_ws when the caller's workspace holds it (null: none).
+  cbd_plan_s* split_alt = nullptr;
+  cbd_plan_s() = default;
+  cbd_plan_s(const cbd_plan_s&) = delete;
+  cbd_plan_s& operator=(const cbd_plan_s&) = delete;
+  ~cbd_plan_s() { delete split_alt; }
 };
 
 namespace cbd {
@@ -26,6 +33,7 @@ void set_error(const std::string& msg);
 int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream);
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream);
 int launch_splitk_finalize(const GemmArgs& a, int64_t grid, void* stream);
+int launch_generic_finalize(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream);
 int launch_grouped(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_rows(const GemmArgs& a, int dtype, int64_t grid, void* stream);
 int launch_grouped_pipe(const GemmArgs& a, int dtype, int64_t grid, void* stream);

@@ -254,6 +254,35 @@ void log_plan(const cbd_plan_s& pl) {
                  (long long)z.pos_h, (long long)z.pos_w);
 }
 
+// Shortest K loop of any class, in k tiles of the family (split-K gives
+// each split at least one).
+int64_t min_class_ktiles(const std::vector<cbd_subgemm_t>& subs, int32_t kernel, int64_t Kg, int64_t bk) {
+  if (kernel != CBD_KERNEL_NHWC_BF16 && (kernel != CBD_KERNEL_GENERIC || bk <= 0)) return 0;
+  int64_t m = INT64_MAX;
+  for (const auto& s : subs)
+    m = std::min<int64_t>(m, kernel == CBD_KERNEL_NHWC_BF16 ? s.k / cbd::kFastBK
+                                                              : int64_t(s.taps_h) * s.taps_w * ceil_div(Kg, bk));
+  return subs.empty() ? 0 : m;
+}
+
+// Workgroups per tile of the planner's split-K configuration (1: none).
+// Large-tile kernel only, and only below the measured crossover (64 tiles:
+// a quarter of the CUs); then as many splits as keep the grid within 128
+// workgroups, a power of two, and every split at least one k tile per wave
+// (measured on the headline problem's batch shards: N = 1 best at 8
+// splits, N = 2 at 4, N >= 4 unsplit).  The generic family already spreads
+// K over the waves of a workgroup: splitting it across workgroups measured
+// slower on every problem tried (the finalising launch and the partial
+// tiles cost more than the shorter K loop saves), so it splits only when
+// asked.
+int64_t auto_ksplit(int32_t kernel, int64_t tiles, int64_t kt_min) {
+  if (kernel != CBD_KERNEL_NHWC_BF16 || tiles <= 0 || tiles >= 64) return 1;
+  const int64_t waves = 4;
+  int64_t s = 1;
+  while (tiles * s * 2 <= 128 && kt_min / (s * 2) >= waves) s *= 2;
+  return s;
+}
+
 }  // namespace
 
 extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* options,
@@ -615,20 +644,23 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     }
   }
 
-  // Split-K (large-tile kernel only): S workgroups per tile, each at least
-  // one k tile of every class.
+  // Split-K (large-tile and generic families): S workgroups per tile, each
+  // at least one k tile of every class.
   int64_t ksplit = 1;
   if (ksplit_opt >= 2) {
-    if (kernel != CBD_KERNEL_NHWC_BF16) {
+    if (kernel != CBD_KERNEL_NHWC_BF16 && kernel != CBD_KERNEL_GENERIC) {
       delete pl;
-      return fail(CBD_ERR_UNSUPPORTED, "ksplit needs the NHWC bf16 (large-tile) kernel");
+      return fail(CBD_ERR_UNSUPPORTED, "ksplit needs the NHWC bf16 (large-tile) or the generic kernel");
     }
     if (per_class) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "ksplit and per_class do not combine");
     }
     ksplit = ksplit_opt;
-    for (const auto& s : subs) ksplit = std::min<int64_t>(ksplit, s.k / cbd::kFastBK);
+    for (const auto& s : subs)
+      ksplit = std::min<int64_t>(ksplit, kernel == CBD_KERNEL_NHWC_BF16
+                                             ? s.k / cbd::kFastBK
+                                             : int64_t(s.taps_h) * s.taps_w * ceil_div(Kg, bk));
     ksplit = std::max<int64_t>(ksplit, 1);
   }
 
@@ -745,7 +777,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.static_shape = static_shape;
   a.gen_waves = kernel == CBD_KERNEL_GENERIC ? (int32_t)(threads / 64) : 0;
   a.ws = nullptr;
-  pl->grid_finalize = ksplit > 1 ? tile / ksplit * (cbd::kFastBN / 8) : 0;
+  pl->grid_finalize = ksplit <= 1                    ? 0
+                      : kernel == CBD_KERNEL_GENERIC ? tile / ksplit
+                                                     : tile / ksplit * (cbd::kFastBN / 8);
   for (size_t i = 0; i < subs.size(); i++) {
     cbd::SubDesc& d = a.sub[i];
     const cbd_subgemm_t& s = subs[i];
@@ -831,7 +865,9 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.cols_per_wg = grp_cols;
   info.ksplit = ksplit;
   info.static_shape = static_shape;
-  info.workspace_bytes = ksplit > 1 ? tile * cbd::kFastBM * cbd::kFastBN * 4 : 0;
+  info.workspace_bytes = ksplit > 1 ? tile * bm * bn * 4 : 0;  // one f32 partial per (tile, split)
+  info.auto_ksplit = 1;
+  info.auto_workspace_bytes = 0;
   // Pointer alignment: the generic family gathers and stores single
   // elements; a zero-fill of NHWC rows writes 16-byte chunks; the other
   // families move 16-byte vectors.
@@ -857,6 +893,28 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   pl->subs = std::move(subs);
   pl->zeros = std::move(zeros);
   if (log_enabled()) log_plan(*pl);
+
+  // The planner's own split-K configuration (ksplit option 0), kept beside
+  // the plan and run by cbd_run_ws when the caller's workspace holds it.
+  if (ksplit_opt == 0 && !per_class) {
+    const int64_t auto_s = auto_ksplit(kernel, tile, min_class_ktiles(pl->subs, kernel, Kg, bk));
+    if (auto_s >= 2) {
+      cbd_plan_options o;
+      std::memset(&o, 0, sizeof(o));
+      if (options) o = *options;
+      o.force_kernel = kernel;
+      o.ksplit = (int32_t)auto_s;
+      cbd_plan_t* alt = nullptr;
+      if (cbd_plan_ex(problem, &o, &alt) == CBD_OK && alt->info.ksplit >= 2) {
+        pl->split_alt = alt;
+        pl->info.auto_ksplit = alt->info.ksplit;
+        pl->info.auto_workspace_bytes = alt->info.workspace_bytes;
+      } else {
+        delete alt;
+      }
+      cbd::set_error("");
+    }
+  }
   *out_plan = pl;
   return CBD_OK;
 }

@@ -29,6 +29,12 @@
 // up to 32x32, 16 on larger ones.  Operands are gathered
 // element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
 // taps off dY's edge) and converted to f32; bf16 products are exact in f32.
+//
+// Split-K (a plan with ksplit S >= 2, for grids too small to fill the GPU):
+// the S workgroups of a tile are S consecutive logical tiles; workgroup sp
+// takes k tiles [KT*sp/S, KT*(sp+1)/S) and writes its f32 partial tile to
+// the caller's workspace; a second kernel sums the S partials in split
+// order and writes dX.
 #include "cbd_device.h"
 #include "cbd_internal.h"
 
@@ -100,7 +106,10 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   const int npos = a.N * npix_img;
   const int tiles_n = (npos + BN - 1) / BN;
   const int per_group = a.tiles_m * tiles_n;
-  const int local = t - s.tile_begin;
+  const int S = a.ksplit > 1 ? a.ksplit : 1;
+  const int lt = t - s.tile_begin;
+  const int local = lt / S;
+  const int sp = lt - local * S;  // split index (0 without split-K)
   const int g = local / per_group;
   const int rem = local - g * per_group;
   const int m0 = (rem % a.tiles_m) * BM;
@@ -113,6 +122,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   const int YX = a.Y * a.X;
   const int kpt = (a.Kg + BK - 1) / BK;
   const int KT = s.taps_h * s.taps_w * kpt;
+  const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
 
   // Gather roles.  A: channel m0 + lane % BM, k rows lane / BM + (64/BM)*e.
   // B: position n0 + lane % BN, k rows lane / BN + (64/BN)*e.
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   const int b_ks = LAYOUT == 0 ? a.Ho * a.Wo : 1;
 
   auto gather = [&](int kt, float (&av)[AE], float (&bv)[BE]) {
-    const bool live = kt < KT;
+    const bool live = kt < kend;
     const int ktc = live ? kt : 0;
     const int tap = ktc / kpt;
     const int k0 = (ktc - tap * kpt) * BK;
@@ -191,11 +201,11 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
 
   // Wave-strided K loop, two tiles of gathers in flight.
   float a0[AE], b0[BE], a1[AE], b1[BE];
-  gather(wave, a0, b0);
-  for (int kt = wave; kt < KT; kt += 2 * NW) {
+  gather(kbeg + wave, a0, b0);
+  for (int kt = kbeg + wave; kt < kend; kt += 2 * NW) {
     gather(kt + NW, a1, b1);
     compute(a0, b0);
-    if (kt + NW >= KT) break;
+    if (kt + NW >= kend) break;
     gather(kt + 2 * NW, a0, b0);
     compute(a1, b1);
   }
@@ -239,6 +249,16 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   }
   __syncthreads();
 
+  if (S > 1) {  // split-K: the partial tile, row-major, at logical tile t
+    float* const part = (float*)a.ws + (size_t)t * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < BM * BN / THREADS; i++) {
+      const int e = (tid / BN + (THREADS / BN) * i) * BN + tid % BN;
+      part[e] = lds[e] + lds[BM * BN + e];
+    }
+    return;
+  }
+
   // Epilogue: thread -> position n0 + tid % BN, channels tid / BN + (256/BN)*i.
   const int p = n0 + tid % BN;
   const bool pv = p < npos;
@@ -259,12 +279,73 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   }
 }
 
+// Finalising kernel of a split-K plan: workgroup T sums the S partial tiles
+// of tile T (logical tiles T*S .. T*S+S-1) in split order and writes them to
+// dX as the main kernel's epilogue would.
+template <int DT, int LAYOUT, int BM, int BN>
+__global__ __launch_bounds__(256) void generic_finalize_kernel(const GemmArgs a) {
+  constexpr uint32_t ES = DT == 0 ? 4 : 2;
+  const int tid = threadIdx.x;
+  const int S = a.ksplit;
+  const int t0 = blockIdx.x * S;
+  const SubDesc s = a.sub[dev::find_class(a, t0)];
+  const int npix_img = s.pos_h * s.pos_w;
+  const int npos = a.N * npix_img;
+  const int tiles_n = (npos + BN - 1) / BN;
+  const int per_group = a.tiles_m * tiles_n;
+  const int local = (t0 - s.tile_begin) / S;
+  const int g = local / per_group;
+  const int rem = local - g * per_group;
+  const int m0 = (rem % a.tiles_m) * BM;
+  const int n0 = (rem / a.tiles_m) * BN;
+
+  const int p = n0 + tid % BN;
+  const bool pv = p < npos;
+  const int pp = pv ? p : 0;
+  const int n = pp / npix_img;
+  const int rr = pp - n * npix_img;
+  const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
+  const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
+  const int pbase = LAYOUT == 0 ? (n * a.C + g * a.Cg) * a.Hi * a.Wi + hi * a.Wi + wi
+                                : ((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg;
+  const int cstride = LAYOUT == 0 ? a.Hi * a.Wi : 1;
+  const float* const part = (const float*)a.ws + (size_t)t0 * (BM * BN);
+  const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+#pragma unroll
+  for (int i = 0; i < BM * BN / 256; i++) {
+    const int m = tid / BN + (256 / BN) * i;
+    const int e = m * BN + tid % BN;
+    float v = 0.f;
+    for (int q = 0; q < S; q++) v += part[(size_t)q * (BM * BN) + e];
+    const int c = m0 + m;
+    store_elem<DT>(rdx, (pv && c < a.Cg) ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB, v);
+  }
+}
+
 template <int DT, int LAYOUT, int BM, int BN, int NW = 4>
 int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
   return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW>,
                               dim3((unsigned)grid), dim3(NW * 64), args, 0,
                               (hipStream_t)stream);
+}
+
+template <int DT, int LAYOUT, int BM, int BN>
+int launch_fin(const GemmArgs& a, int64_t grid, void* stream) {
+  void* args[] = {const_cast<GemmArgs*>(&a)};
+  return (int)hipLaunchKernel((const void*)&generic_finalize_kernel<DT, LAYOUT, BM, BN>,
+                              dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+}
+
+template <int DT, int LAYOUT>
+int launch_fin_tiles(const GemmArgs& a, int64_t grid, void* stream) {
+  if (a.tile_m == 64 && a.tile_n == 64) return launch_fin<DT, LAYOUT, 64, 64>(a, grid, stream);
+  if (a.tile_m == 32 && a.tile_n == 64) return launch_fin<DT, LAYOUT, 32, 64>(a, grid, stream);
+  if (a.tile_m == 64 && a.tile_n == 32) return launch_fin<DT, LAYOUT, 64, 32>(a, grid, stream);
+  if (a.tile_m == 32 && a.tile_n == 32) return launch_fin<DT, LAYOUT, 32, 32>(a, grid, stream);
+  if (a.tile_m == 16 && a.tile_n == 32) return launch_fin<DT, LAYOUT, 16, 32>(a, grid, stream);
+  if (a.tile_m == 16 && a.tile_n == 16) return launch_fin<DT, LAYOUT, 16, 16>(a, grid, stream);
+  return (int)hipErrorInvalidValue;
 }
 
 template <int DT, int LAYOUT>
@@ -288,6 +369,14 @@ int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void*
                                      : launch_tiles<0, 1>(a, grid, stream);
   return layout == CBD_LAYOUT_NCHW ? launch_tiles<1, 0>(a, grid, stream)
                                    : launch_tiles<1, 1>(a, grid, stream);
+}
+
+int launch_generic_finalize(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream) {
+  if (dtype == CBD_F32)
+    return layout == CBD_LAYOUT_NCHW ? launch_fin_tiles<0, 0>(a, grid, stream)
+                                     : launch_fin_tiles<0, 1>(a, grid, stream);
+  return layout == CBD_LAYOUT_NCHW ? launch_fin_tiles<1, 0>(a, grid, stream)
+                                   : launch_fin_tiles<1, 1>(a, grid, stream);
 }
 
 }  // namespace cbd

@@ -131,14 +131,22 @@ typedef struct {
                            a row per workgroup, rounded up to a multiple of 4
                            (4x4x4 kernel) or 16 (16x16x16 kernel) (0: the
                            planner's choice) */
-  int32_t ksplit;       /* large-tile (NHWC bf16) kernel: split each tile's K
-                           loop over this many workgroups (0 or 1: no split;
-                           at most 64; clamped to the k tiles of the
-                           shortest class).  Partial tiles go to a caller
-                           workspace as f32 and a second kernel sums them
-                           in split order and writes dX: such a plan runs
-                           only through cbd_run_ws.  For grids too small to
-                           fill the GPU (e.g. one GPU's batch shard). */
+  int32_t ksplit;       /* large-tile (NHWC bf16) and generic kernels: split
+                           each tile's K loop over this many workgroups (at
+                           most 64; clamped to the k tiles of the shortest
+                           class).  Partial tiles go to a caller workspace
+                           as f32 and a second kernel sums them in split
+                           order and writes dX: such a plan runs only
+                           through cbd_run_ws.  For grids too small to fill
+                           the GPU (e.g. one GPU's batch shard).
+                           0: the planner's choice -- for the large-tile
+                           kernel below 64 tiles the plan also holds a
+                           split configuration
+                           (cbd_plan_info: auto_ksplit), which cbd_run_ws
+                           runs when given a workspace of at least
+                           auto_workspace_bytes; cbd_run, or a smaller
+                           workspace, runs the unsplit one.  1: never
+                           split. */
   int32_t per_class;    /* 1: one main launch per residue class instead of one
                            for all (an ablation of the single launch; not
                            with ksplit); 0 or 1 */
@@ -184,20 +192,24 @@ cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_options* optio
 cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                    void* stream);
 
-/* As cbd_run, for plans that need a workspace (cbd_plan_workspace_size > 0,
- * i.e. options.ksplit >= 2; plans that need none accept any workspace,
- * including NULL).  workspace is a DEVICE buffer of at least that many bytes,
- * 256-byte aligned, owned by the caller, not overlapping dy, w or dx; its
- * contents are scratch (no initialisation needed, overwritten).  The plan's
- * calls on one stream may share a workspace; concurrent calls on different
- * streams need one each.  Errors: as cbd_run, plus INVALID_ARG for a missing,
- * small or overlapping workspace and UNSUPPORTED for a misaligned one. */
+/* As cbd_run, with a workspace.  Plans with options.ksplit >= 2 need one
+ * (cbd_plan_info: workspace_bytes); a plan that holds the planner's split
+ * configuration (auto_ksplit > 1) runs it when workspace_bytes is at least
+ * auto_workspace_bytes, and its unsplit configuration otherwise (also for a
+ * NULL workspace); other plans ignore the workspace.  workspace is a DEVICE
+ * buffer, 256-byte aligned, owned by the caller, not overlapping dy, w or
+ * dx; its contents are scratch (no initialisation needed, overwritten).  The
+ * plan's calls on one stream may share a workspace; concurrent calls on
+ * different streams need one each.  Errors: as cbd_run, plus INVALID_ARG for
+ * a missing, small or overlapping workspace where one is used, and
+ * UNSUPPORTED for a misaligned one. */
 cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                       void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace cbd_run_ws needs for this plan (0: none; then
- * cbd_run suffices, and cbd_run on a plan that needs one fails with
- * INVALID_ARG). */
+/* Bytes of device workspace for this plan's fastest configuration: what
+ * cbd_run_ws needs for a plan with options.ksplit >= 2 (cbd_run on such a
+ * plan fails with INVALID_ARG), else what enables the planner's split
+ * configuration (optional); 0: the plan uses none. */
 cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* bytes);
 
 /* Free a plan.  NULL is allowed. */
@@ -248,6 +260,10 @@ typedef struct {
                                each pointer: the element size for the generic
                                family (16 for dx when a zero-fill writes
                                16-byte chunks), 16 for the other families */
+  int64_t auto_ksplit;      /* workgroups per tile of the planner's split
+                               configuration, which cbd_run_ws runs given
+                               auto_workspace_bytes (1: none) */
+  int64_t auto_workspace_bytes; /* workspace that enables it (0: none) */
 } cbd_plan_info_t;
 
 typedef struct {

@@ -277,6 +277,91 @@ def test_fuzz_ksplit_integer_exact(seed, count):
         assert run.guards_intact(), (p, ksplit)
 
 
+# Split-K on the generic family: (problem, requested splits; clamped to the
+# k tiles of the shortest class: c1 18, c2-14-3 36, c3a 8, c3b 8).
+GENERIC_SPLIT = [("c1", 4), ("c1", 64), ("c2-14-3", 2), ("c3a", 3), ("c3b", 2), ("c3b", 8)]
+
+
+@pytest.mark.parametrize("name,ksplit", GENERIC_SPLIT)
+def test_generic_ksplit_vs_oracle(name, ksplit):
+    """Generic family with split-K: random operands within the fp32
+    tolerance, integer operands bit-exact, the same bits on a second call,
+    guard bands intact."""
+    p = by_name(name)
+    pl = plan_for(p, cbd.KERNEL_GENERIC, ksplit=ksplit)
+    info = pl.info()
+    print(f"[ksplit-generic] {name} ksplit={ksplit}->{info.ksplit}", flush=True)
+    assert info.kernel == cbd.KERNEL_GENERIC and 2 <= info.ksplit <= ksplit
+    assert pl.workspace_size() == info.workspace_bytes > 0
+    ws = torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
+    for kind in ("dist", "int"):
+        dy, w = operands(p, kind)
+        ref = oracle.bwd_data(p, dy, w)
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+        if kind == "dist":
+            ok, inf = check(p, run, ref)
+            print(f"[ksplit-generic] {name}", inf, flush=True)
+            assert ok, inf
+        else:
+            assert np.array_equal(run.result_bits().reshape(ref.shape), exact_expected_bits(p, ref))
+        assert run.guards_intact()
+        bits1 = run.result_bits().copy()
+        run()
+        assert np.array_equal(bits1, run.result_bits())
+
+
+@pytest.mark.parametrize("seed,count", [(23, 60)])
+def test_fuzz_generic_ksplit_integer_exact(seed, count):
+    """Random problems (both layouts, both dtypes, groups, strides,
+    dilations, padding) on the generic family with split-K: bit-exact."""
+    rng = random.Random(seed + 11)
+    for i, p in enumerate(fuzz_problems(seed, count)):
+        ksplit = rng.choice([2, 3, 5, 16])
+        pl = plan_for(p, cbd.KERNEL_GENERIC, ksplit=ksplit)
+        print(f"[fuzz-ksplit-generic] i={i} ksplit={ksplit}->{pl.info().ksplit} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(7000 * seed + 3 * i + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(7000 * seed + 3 * i + 2, sh["w"]).astype(np.float32)
+        ws = torch.empty(max(pl.workspace_size(), 1), dtype=torch.uint8, device="cuda")
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+        ref = oracle.bwd_data(p, dy, w)
+        assert np.array_equal(run.result_bits().reshape(ref.shape), exact_expected_bits(p, ref)), (p, ksplit)
+        assert run.guards_intact(), (p, ksplit)
+
+
+@pytest.mark.parametrize("name,n", [("c4", 1), ("c4", 2)])
+def test_auto_split_runs_with_workspace(name, n):
+    """The planner's split configuration: cbd_run (and cbd_run_ws with too
+    small a workspace) runs the unsplit plan, cbd_run_ws with
+    auto_workspace_bytes runs the split one (the same bits as an explicit
+    ksplit plan); all within the tolerance of the oracle."""
+    p = by_name(name) if n is None else by_name(name).with_(n=n)
+    pl = plan_for(p)
+    info = pl.info()
+    print(f"[auto-split] {name} n={p.n} auto_ksplit={info.auto_ksplit}", flush=True)
+    assert info.ksplit == 1 and info.workspace_bytes == 0
+    assert info.auto_ksplit > 1 and pl.workspace_size() == info.auto_workspace_bytes > 0
+    dy, w = operands(p)
+    dyd, wd = to_device(dy, p), to_device(w, p)
+    ws = torch.empty(info.auto_workspace_bytes, dtype=torch.uint8, device="cuda")
+    small_ws = torch.empty(info.auto_workspace_bytes - 256, dtype=torch.uint8, device="cuda")
+    plain = DeviceRun(p, pl, dyd, wd)().result_bits().copy()
+    small = DeviceRun(p, pl, dyd, wd, workspace=small_ws)().result_bits().copy()
+    split_run = DeviceRun(p, pl, dyd, wd, workspace=ws)()
+    split = split_run.result_bits().copy()
+    assert split_run.guards_intact()
+    explicit = DeviceRun(p, plan_for(p, info.kernel, ksplit=info.auto_ksplit), dyd, wd, workspace=ws)()
+    assert np.array_equal(plain, small)
+    assert np.array_equal(split, explicit.result_bits())
+    ref = oracle.bwd_data(p, dy, w)
+    for bits in (plain, split):
+        if p.dtype == "f32":
+            ok, inf = check_f32(bits.view(np.float32).reshape(ref.shape), ref)
+        else:
+            ok, inf = check_bf16(bits.reshape(ref.shape), ref)
+        assert ok, inf
+
+
 @pytest.mark.parametrize("name", ["c1", "c3a", "c3b", "c4", "c5-s2", "c2-14-3"])
 def test_per_class_launches_match_single_launch(name):
     """One launch per residue class gives the same bits as the single launch."""

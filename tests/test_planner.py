@@ -301,9 +301,12 @@ def test_ksplit_plans():
     # a short class clamps S: 3x3 stride 2 has a one-tap class (K/G = 64: 2 k tiles)
     pl = cbd.plan(2, 1, 256, 64, 9, 9, 3, 3, 2, 1, 1, "nhwc", "bf16", ksplit=8)
     assert pl.info().kernel == cbd.KERNEL_NHWC_BF16 and pl.info().ksplit == 2
-    # other kernel families refuse it
+    # the grouped and row-block families refuse it
     with pytest.raises(cbd.CbdError):
-        cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=2)
+        cbd.plan(2, 32, 128, 128, 12, 12, 3, 3, 2, 1, 1, "nhwc", "bf16", ksplit=2)
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=2,
+                 force_kernel=cbd.KERNEL_NCHW_ROWS)
     with pytest.raises(cbd.CbdError):
         cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", ksplit=65)
 
@@ -445,3 +448,52 @@ def test_cbd_log_plan_dump():
         if expect:
             assert "kernel generic" in r.stderr and "sub-GEMM 0:" in r.stderr
             assert r.stderr.count("zero region:") == 3
+
+
+def test_split_k_plans():
+    """Split-K: explicit splits on the large-tile and generic families
+    (clamped to the shortest class's k tiles, one f32 partial tile per
+    (tile, split) in the workspace, a finalising launch), and the planner's
+    own split configuration (large-tile kernel, below 64 tiles)."""
+    by = {q.name: q for q in PROBLEMS}
+
+    def mk(p, **kw):
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        return cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                        (p.dh, p.dw), p.layout, dt, **kw)
+
+    # explicit splits on the generic family, clamped: c3b has one 1x1 class,
+    # 64/8 = 8 k tiles; c3a's shortest class has one tap, 8 k tiles; c1 has
+    # 9 taps x 16/8
+    for name, req, want in (("c3b", 64, 8), ("c3a", 5, 5), ("c1", 64, 18), ("c2-14-3", 3, 3)):
+        pl = mk(by[name], force_kernel=cbd.KERNEL_GENERIC, ksplit=req)
+        i = pl.info()
+        assert (i.kernel, i.ksplit) == (cbd.KERNEL_GENERIC, want), name
+        gemm_tiles = sum(s.tiles for s in pl.subgemms())
+        assert gemm_tiles % want == 0
+        assert i.workspace_bytes == gemm_tiles * i.tile_m * i.tile_n * 4
+        assert pl.workspace_size() == i.workspace_bytes
+        assert i.launches == 2 + (i.grid_zero > 0)
+        assert (i.auto_ksplit, i.auto_workspace_bytes) == (1, 0)
+    # the planner's split configuration: below 64 tiles, splits up to 128
+    # workgroups (a power of two, each split at least 4 k tiles)
+    c4 = by["c4"]
+    for n, s in ((1, 8), (2, 4), (4, 1), (8, 1), (16, 1)):
+        i = mk(c4.with_(n=n)).info()
+        assert (i.ksplit, i.auto_ksplit) == (1, s), n
+        assert (i.auto_workspace_bytes > 0) == (s > 1)
+        assert i.auto_workspace_bytes == (i.grid_main * s * 256 * 256 * 4 if s > 1 else 0)
+    # the generic family splits only when asked (c1: 25 tiles, still unsplit)
+    for name in by:
+        i = mk(by[name]).info()
+        assert (i.auto_ksplit, i.auto_workspace_bytes) == (1, 0), name
+    c4_1 = c4.with_(n=1)
+    assert mk(c4_1).workspace_size() == mk(c4_1).info().auto_workspace_bytes > 0
+    # ksplit 1: never split; per_class: no split configuration
+    for kw in ({"ksplit": 1}, {"per_class": True}):
+        i = mk(c4_1, **kw).info()
+        assert (i.ksplit, i.auto_ksplit, i.auto_workspace_bytes, i.workspace_bytes) == (1, 1, 0, 0)
+    # families without split-K refuse an explicit split
+    with pytest.raises(cbd.CbdError) as e:
+        mk(by["c5-s2"], ksplit=2)
+    assert e.value.status == 2
