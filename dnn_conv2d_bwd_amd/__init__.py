@@ -35,7 +35,7 @@ STATUS = {0: "CBD_OK", 1: "CBD_ERR_INVALID_ARG", 2: "CBD_ERR_UNSUPPORTED", 3: "C
           4: "CBD_ERR_NO_MEMORY"}
 
 # Every symbol include/cbd.h declares.
-EXPORTS = ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_plan_workspace_size",
+EXPORTS = ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_run_noalloc", "cbd_plan_workspace_size",
            "cbd_plan_destroy", "cbd_status_string", "cbd_last_error", "cbd_plan_info",
            "cbd_plan_subgemm", "cbd_plan_zero_region")
 
@@ -102,6 +102,7 @@ def _load():
     L.cbd_plan_ex.argtypes = [P(Problem), P(PlanOptions), P(ctypes.c_void_p)]
     L.cbd_run.argtypes = [ctypes.c_void_p] * 5
     L.cbd_run_ws.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_uint64, ctypes.c_void_p]
+    L.cbd_run_noalloc.argtypes = [ctypes.c_void_p] * 5
     L.cbd_plan_workspace_size.argtypes = [ctypes.c_void_p, P(ctypes.c_uint64)]
     L.cbd_plan_destroy.argtypes = [ctypes.c_void_p]
     L.cbd_plan_destroy.restype = None
@@ -111,7 +112,7 @@ def _load():
     L.cbd_plan_info.argtypes = [ctypes.c_void_p, P(PlanInfo)]
     L.cbd_plan_subgemm.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(SubGemm)]
     L.cbd_plan_zero_region.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ZeroRegion)]
-    for f in ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_plan_workspace_size",
+    for f in ("cbd_plan", "cbd_plan_ex", "cbd_run", "cbd_run_ws", "cbd_run_noalloc", "cbd_plan_workspace_size",
               "cbd_plan_info", "cbd_plan_subgemm",
               "cbd_plan_zero_region"):
         getattr(L, f).restype = ctypes.c_int
@@ -275,6 +276,26 @@ def run(p: Plan, dy, w, dx, stream=None, workspace=None) -> None:
                                ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_uint64(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(handle)), "cbd_run_ws")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # CBD_NOALLOC_SCRATCH_BYTES
+
+
+def run_noalloc(p: Plan, dy, w, dx, stream=None) -> None:
+    """dx <- conv_bwd_data(dy, w) through cbd_run_noalloc: the library's own
+    static device workspace instead of a caller's (no allocation)."""
+    import torch
+
+    sh = p.shapes()
+    dt = p.problem.dtype
+    _check_tensor(dy, sh["dy"], dt, "dy")
+    _check_tensor(w, sh["w"], dt, "w")
+    _check_tensor(dx, sh["dx"], dt, "dx")
+    if stream is None:
+        stream = torch.cuda.current_stream(dx.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    _check(_lib.cbd_run_noalloc(p.handle, ctypes.c_void_p(dy.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                                ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(handle)), "cbd_run_noalloc")
 
 
 def run_raw(p: Plan, dy_ptr: int, w_ptr: int, dx_ptr: int, stream_handle: int = 0) -> int:

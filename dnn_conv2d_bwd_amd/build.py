@@ -21,6 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build", "cbd")
 SOURCES = [
     "cbd_plan.cpp",
     "cbd_api.cpp",
+    "cbd_noalloc.hip",
     "kern_igemm_generic.hip",
     "kern_igemm_nhwc_bf16.hip",
     "kern_grouped_direct.hip",

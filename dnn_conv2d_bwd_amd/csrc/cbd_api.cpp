@@ -141,6 +141,17 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
 
 }  // namespace
 
+namespace cbd {
+cbd_status run_with_workspace(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                              void* workspace, uint64_t workspace_bytes, void* stream) {
+  // The planner's split configuration when the workspace holds it.
+  if (plan && plan->split_alt && workspace &&
+      workspace_bytes >= (uint64_t)plan->split_alt->info.workspace_bytes)
+    return run_impl(plan->split_alt, dy, w, dx, workspace, workspace_bytes, stream);
+  return run_impl(plan, dy, w, dx, workspace, workspace_bytes, stream);
+}
+}  // namespace cbd
+
 extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                               void* stream) {
   return run_impl(plan, dy, w, dx, nullptr, 0, stream);
@@ -148,11 +159,7 @@ extern "C" cbd_status cbd_run(const cbd_plan_t* plan, const void* dy, const void
 
 extern "C" cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
                                  void* workspace, uint64_t workspace_bytes, void* stream) {
-  // The planner's split configuration when the workspace holds it.
-  if (plan && plan->split_alt && workspace &&
-      workspace_bytes >= (uint64_t)plan->split_alt->info.workspace_bytes)
-    return run_impl(plan->split_alt, dy, w, dx, workspace, workspace_bytes, stream);
-  return run_impl(plan, dy, w, dx, workspace, workspace_bytes, stream);
+  return cbd::run_with_workspace(plan, dy, w, dx, workspace, workspace_bytes, stream);
 }
 
 extern "C" cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* bytes) {

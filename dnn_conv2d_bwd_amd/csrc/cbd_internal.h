@@ -29,6 +29,11 @@ namespace cbd {
 // Thread-local error detail for CBD_ERR_HIP and planner rejections.
 void set_error(const std::string& msg);
 
+// cbd_run_ws: the plan's split configuration when the workspace holds it,
+// else the plan itself.
+cbd_status run_with_workspace(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                              void* workspace, uint64_t workspace_bytes, void* stream);
+
 // Launchers (defined next to their kernels).  Each returns 0 or a hipError_t.
 int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream);
 int launch_nhwc_bf16(const GemmArgs& a, int64_t grid, void* stream);

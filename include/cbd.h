@@ -212,6 +212,29 @@ cbd_status cbd_run_ws(const cbd_plan_t* plan, const void* dy, const void* w, voi
  * configuration (optional); 0: the plan uses none. */
 cbd_status cbd_plan_workspace_size(const cbd_plan_t* plan, uint64_t* bytes);
 
+/* Bytes of the workspace that cbd_run_noalloc holds on each GPU. */
+#define CBD_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* As cbd_run_ws, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the workspace is a device array of CBD_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) inside the library, one copy per GPU, held until the process
+ * ends; its device address is looked up on the first call on each device,
+ * which must be the current device of the calling thread and the device of
+ * stream.  A plan with options.ksplit >= 2 runs with it as its workspace; a
+ * plan holding the planner's split configuration runs that configuration
+ * when its workspace fits (the large-tile kernel's batch shards: at most 32
+ * MiB); other plans run as with cbd_run.  No call allocates or frees memory.
+ * The array keeps the last call's contents and nothing in it needs to start
+ * at zero (split-K partial tiles are written before they are read).  Calls
+ * that overlap in time on one GPU (different streams, or threads) share the
+ * array and race: serialise them, or use cbd_run_ws with a workspace each.
+ * Errors: as cbd_run_ws, plus UNSUPPORTED for a plan whose workspace
+ * exceeds CBD_NOALLOC_SCRATCH_BYTES (nothing is launched) and HIP if the
+ * array's address cannot be looked up. */
+cbd_status cbd_run_noalloc(const cbd_plan_t* plan, const void* dy, const void* w, void* dx,
+                           void* stream);
+
 /* Free a plan.  NULL is allowed. */
 void cbd_plan_destroy(cbd_plan_t* plan);
 
