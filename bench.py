@@ -123,46 +123,30 @@ def read_traffic(key, problem):
         return None
 
 
-def cpu_baseline(p, dy, w, info, target_s, dx_gpu=None):
-    """Oracle over a bounded random sample of output elements, timed and
-    scaled to the whole problem.  Given the GPU's dX (host array in the
-    layout's memory order), also the parity of the GPU result at the same
-    elements (sample_parity)."""
-    import numpy as np
-
+def cpu_baseline(p, dy, w, info, dx_gpu=None):
+    """The oracle's loop nest (bwd_data: fp64, OpenMP over the host threads)
+    on the whole problem, one call, wall-clocked; nothing is scaled.  Given
+    the GPU's dX (host array in the layout's memory order), also the parity
+    of the whole GPU result against that oracle result (parity_of)."""
     import oracle
 
-    dy64 = np.ascontiguousarray(dy, dtype=np.float64)
-    w64 = np.ascontiguousarray(w, dtype=np.float64)
-    rng = np.random.default_rng(7)
     total = p.n * p.c * p.hi * p.wi
-
-    def points(count):
-        return np.stack([rng.integers(0, p.n, count), rng.integers(0, p.c, count),
-                         rng.integers(0, p.hi, count), rng.integers(0, p.wi, count)], axis=1)
-    probe = min(total, 20000)
-    pts = points(probe)
     t0 = time.perf_counter()
-    oracle.bwd_data_at(p, dy64, w64, pts)
+    ref = oracle.bwd_data(p, dy, w)
     dt = time.perf_counter() - t0
-    count = int(min(total, max(probe, probe * target_s / max(dt, 1e-6))))
-    pts = points(count)
-    t0 = time.perf_counter()
-    ref = oracle.bwd_data_at(p, dy64, w64, pts)
-    dt = time.perf_counter() - t0
-    flops = info.useful_flops * count / total
-    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-           "cores": oracle.num_threads(), "kind": "oracle", "oracle_s": round(dt, 3),
-           "sample": f"{count} random dX elements of {total} ({count / total:.2%}), "
-                     f"fp64 gather per element, {dt:.2f} s; useful flops scaled by the "
-                     f"sampled fraction"}
+    threads = oracle.num_threads()
+    out = {"value": round(info.useful_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": threads, "oracle_threads": threads, "kind": "oracle", "oracle_s": round(dt, 3),
+           "sample": f"the whole problem: one call of the oracle's fp64 loop nest (bwd_data) "
+                     f"over all {total} dX elements on {threads} OpenMP threads, {dt:.2f} s; "
+                     f"nothing scaled"}
     if dx_gpu is not None:
-        out["parity"] = sample_parity(p, pts, ref, dx_gpu)
+        out["parity"] = parity_of(p, dx_gpu.ravel(), ref.ravel())
     return out
 
 
-def sample_parity(p, pts, ref64, dx_gpu):
-    """The GPU's dX against the oracle at the sampled elements.
+def parity_of(p, got, ref64):
+    """The GPU's dX (flat, any float dtype) against the oracle (flat fp64).
     fp32: relative L2 <= 1e-5 and max |err| <= 1e-4 max |ref|.  bf16: relative
     L2 <= 8e-3 and every element within 2 bf16 ulps of the oracle rounded to
     f32 then bf16, ulps counted at magnitude max(|ref|, 2^-10 rms(ref))
@@ -172,8 +156,7 @@ def sample_parity(p, pts, ref64, dx_gpu):
 
     import oracle
 
-    n, c, h, w_ = pts[:, 0], pts[:, 1], pts[:, 2], pts[:, 3]
-    got = (dx_gpu[n, c, h, w_] if p.layout == 0 else dx_gpu[n, h, w_, c]).astype(np.float64)
+    got = got.astype(np.float64)
     ref32 = oracle.round_f32(ref64).astype(np.float64)
     norm = float(np.linalg.norm(ref64))
     rel_l2 = float(np.linalg.norm(got - ref64) / norm) if norm > 0 else float(np.abs(got).max())
@@ -198,6 +181,75 @@ def sample_parity(p, pts, ref64, dx_gpu):
         ok = rel_l2 <= 8e-3 and res["ulp_viol_floored"] == 0
     res["pass"] = bool(ok and zeros_ok)
     return res
+
+
+def graph_us(cbd, torch, pl, dy_d, w_d, dx_d, ws=None, calls=50, reps=4):
+    """GPU µs per call: `calls` calls captured in a HIP graph, replayed `reps`
+    times under one event pair (no host launch cost)."""
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        cbd.run(pl, dy_d, w_d, dx_d, stream=cap, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(calls):
+                cbd.run(pl, dy_d, w_d, dx_d, stream=cap, workspace=ws)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) * 1e3 / (calls * reps)
+
+
+def roof_of(p, info, us):
+    """(bound, achieved, peak, unit) of a problem's own roofline at `us` per call."""
+    if p.name in HBM_BOUND:
+        return "hbm", algorithmic_bytes(p, info) / us / 1e3, PEAK_HBM_GBS, "GB/s"
+    peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_F32_TFLOPS
+    return "mfma", info.useful_flops / us / 1e6, peak, "TFLOP/s"
+
+
+SECONDARY = ("c3a", "c3b", "c5-s2", "c5-s1")
+
+
+def secondary_rows():
+    """Graph-mode µs per call and roofline fraction of the other rows whose
+    kernels carry a roofline claim (no oracle)."""
+    import torch
+
+    import dnn_conv2d_bwd_amd as cbd
+    from cbd_inputs import draw, problem_by_name, seed_for
+
+    rows = {}
+    for name in SECONDARY:
+        p = problem_by_name(name)
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                      (p.dh, p.dw), p.layout, dt)
+        info = pl.info()
+        sh = pl.shapes()
+        tdt = torch.float32 if p.dtype == "f32" else torch.bfloat16
+        dy_d = torch.from_numpy(draw(p.dist_dy, seed_for(p, "dy"), sh["dy"], p.dtype)).to(tdt).cuda()
+        w_d = torch.from_numpy(draw(p.dist_w, seed_for(p, "w"), sh["w"], p.dtype)).to(tdt).cuda()
+        dx_d = torch.empty(sh["dx"], dtype=tdt, device="cuda")
+        ws = (torch.empty(pl.workspace_size(), dtype=torch.uint8, device="cuda")
+              if pl.workspace_size() else None)
+        for _ in range(10):
+            cbd.run(pl, dy_d, w_d, dx_d, workspace=ws)
+        us = graph_us(cbd, torch, pl, dy_d, w_d, dx_d, ws)
+        bound, ach, peak, unit = roof_of(p, info, us)
+        rows[name] = {"workload": describe(p), "kernel": KERNEL_SYMBOL[kernel_key(info)],
+                      "us_graph": round(us, 3), "bound": bound, "achieved": round(ach, 2),
+                      "peak": peak, "unit": unit, "frac": round(ach / peak, 4)}
+        del dy_d, w_d, dx_d, ws
+    return rows
 
 
 def machine():
@@ -246,8 +298,12 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--problem", default="c4")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="0 skips the CPU baseline; any other value runs the oracle once on the "
+                         "whole problem (a few seconds for the headline problem)")
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false",
+                    help="leave out the graph-mode µs and roofline fractions of the other "
+                         "roofline rows (c3a, c3b, c5-s2, c5-s1)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain copy of this size (rocprofv3 counter scaling)")
     ap.add_argument("--force-kernel", type=int, default=-1)
@@ -425,9 +481,10 @@ def main():
         "gpu": torch.cuda.get_device_name(0) or "gfx950",
         "machine": machine(),
     }
+    if args.secondary:
+        out["secondary"] = secondary_rows()
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(p, dy, w, info, args.cpu_seconds,
-                                           dx_gpu=dx_d.float().cpu().numpy())
+        out["cpu_baseline"] = cpu_baseline(p, dy, w, info, dx_gpu=dx_d.float().cpu().numpy())
     print(json.dumps(out), flush=True)
 
 
@@ -567,10 +624,8 @@ def all_problems(args):
             "frac_warm": round(ach(warm) / peak, 4), "frac_graph": round(ach(us_graph) / peak, 4),
             "frac_cold": round(ach(med) / peak, 4)}
         if args.cpu_seconds > 0:
-            # The oracle on a bounded sample of this problem's dX (about a
-            # second each), and the GPU result's parity at those elements.
-            cb = cpu_baseline(p, dy_h, w_h, info, min(args.cpu_seconds, 1.0),
-                              dx_gpu=dx_d.float().cpu().numpy())
+            # The oracle on the whole problem, and the GPU result's parity.
+            cb = cpu_baseline(p, dy_h, w_h, info, dx_gpu=dx_d.float().cpu().numpy())
             line.update({"oracle_s": cb["oracle_s"], "oracle_threads": cb["cores"],
                          "oracle_tflops": cb["value"], "oracle_sample": cb["sample"],
                          "parity": cb["parity"]})

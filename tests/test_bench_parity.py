@@ -1,7 +1,8 @@
-"""The benchmark's sampled parity check (bench.sample_parity), on the CPU:
+"""The benchmark's whole-tensor parity check (bench.parity_of), on the CPU:
 the oracle's own result, rounded to the output dtype, passes; a result off by
 more than the stated tolerance, or nonzero where the oracle is exactly zero,
-fails."""
+fails.  And the CPU baseline (bench.cpu_baseline) times one oracle call on the
+whole problem and reports its thread count."""
 import numpy as np
 
 import bench
@@ -17,44 +18,45 @@ def _case(layout, dtype, stride):
     w = draw(p.dist_w, seed_for(p, "w"), sh["w"], dtype)
     ref = oracle.reference(p, dy, w)
     out = ref["ref_f32"] if dtype == "f32" else oracle.bf16_bits_to_f32(ref["ref_bf16_bits"]).reshape(sh["dx"])
-    rng = np.random.default_rng(3)
-    pts = np.stack([rng.integers(0, p.n, 400), rng.integers(0, p.c, 400),
-                    rng.integers(0, p.hi, 400), rng.integers(0, p.wi, 400)], axis=1)
-    return p, pts, oracle.bwd_data_at(p, dy, w, pts), np.array(out, dtype=np.float32)
-
-
-def _at(p, a, pt):
-    n, c, h, w = pt
-    return (n, c, h, w) if p.layout == NCHW else (n, h, w, c)
+    return p, dy, w, ref["dx64"].ravel(), np.array(out, dtype=np.float32).ravel()
 
 
 def test_exact_result_passes():
     for layout in (NCHW, NHWC):
         for dtype in ("f32", "bf16"):
-            p, pts, ref, out = _case(layout, dtype, 2)
-            r = bench.sample_parity(p, pts, ref, out)
-            assert r["pass"] and r["zeros_ok"], (layout, dtype, r)
+            p, _, _, ref, out = _case(layout, dtype, 2)
+            r = bench.parity_of(p, out, ref)
+            assert r["pass"] and r["zeros_ok"] and r["elements"] == ref.size, (layout, dtype, r)
             if dtype == "bf16":
                 assert r["ulp_max"] <= 0.5 + 1e-9 and r["ulp_viol_floored"] == 0
 
 
 def test_bf16_off_by_four_ulps_fails():
-    p, pts, ref, out = _case(NHWC, "bf16", 1)
+    p, _, _, ref, out = _case(NHWC, "bf16", 1)
     i = int(np.argmax(np.abs(ref)))
-    idx = _at(p, out, pts[i])
-    v = np.float32(out[idx])
-    bits = np.array([v], dtype=np.float32).view(np.uint32)
+    bits = np.array([out[i]], dtype=np.float32).view(np.uint32)
     bits += np.uint32(4 << 16)  # four bf16 ulps further from zero
-    out[idx] = bits.view(np.float32)[0]
-    r = bench.sample_parity(p, pts, ref, out)
+    out[i] = bits.view(np.float32)[0]
+    r = bench.parity_of(p, out, ref)
     assert not r["pass"] and r["ulp_viol_floored"] >= 1
 
 
 def test_nonzero_at_unreached_position_fails():
     # 1x1 filter, stride 2: odd rows and columns of dX are never reached.
-    p, pts, ref, out = _case(NCHW, "f32", 2)
-    zero = [i for i in range(len(ref)) if ref[i] == 0.0]
-    assert zero
-    out[_at(p, out, pts[zero[0]])] = 1e-30
-    r = bench.sample_parity(p, pts, ref, out)
+    p, _, _, ref, out = _case(NCHW, "f32", 2)
+    zero = np.flatnonzero(ref == 0.0)
+    assert zero.size
+    out[zero[0]] = 1e-30
+    r = bench.parity_of(p, out, ref)
     assert not r["zeros_ok"] and not r["pass"]
+
+
+def test_cpu_baseline_whole_problem():
+    p, dy, w, ref, out = _case(NHWC, "bf16", 2)
+
+    class Info:
+        useful_flops = 2 * p.n * p.c * p.k * 5 * 5  # any positive count
+    r = bench.cpu_baseline(p, dy, w, Info, dx_gpu=out.reshape(oracle.shapes(p)["dx"]))
+    assert r["kind"] == "oracle" and r["cores"] == r["oracle_threads"] == oracle.num_threads() >= 1
+    assert r["value"] > 0 and r["oracle_s"] >= 0 and "whole problem" in r["sample"]
+    assert r["parity"]["pass"] and r["parity"]["elements"] == ref.size
