@@ -50,12 +50,14 @@ __device__ inline uint32_t opaque(uint32_t x) {
   return x;
 }
 
+// One element at byte offset voff + soff (soff wave-uniform: the scalar
+// offset of the buffer instruction), converted to f32.
 template <int DT>
-__device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+__device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   if constexpr (DT == 0) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
   } else {
-    return dev::bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
+    return dev::bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
   }
 }
 
@@ -68,12 +70,22 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
   }
 }
 
-template <int DT, int LAYOUT, int BM, int BN, int NW>
+// NS: the zero-insertion form (no residue split: each tap's dY index needs a
+// divisibility test); otherwise a tap's dY index is the position plus a
+// wave-uniform shift.
+template <int DT, int LAYOUT, int BM, int BN, int NW, bool NS>
 __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArgs a) {
   constexpr int BK = generic_bk(BM, BN);    // 8 (32x32 tiles) or 16
   constexpr int THREADS = NW * 64;          // NW (4 or 8) waves, each its own k tiles
   constexpr int MB = BM / 16, NB = BN / 16;
   constexpr int AE = BK * BM / 64, BE = BK * BN / 64;  // gathers per lane per tile
+  // k tiles in flight per wave: eight on the small-grid shapes (eight-wave
+  // workgroups, 16x16 tiles), where one wave's chain of memory round trips
+  // sets the time; two elsewhere, where the extra registers would cost
+  // occupancy (measured: c1 4.97 -> 4.29 us and the 3x3 32-channel
+  // problems 8.05 -> 7.73 us with eight; the stride-2 64-channel problems
+  // 17.1 -> 18.0 and 7.5 -> 8.5 us).
+  constexpr int DEPTH = (AE + BE <= 8 && (NW == 8 || BM * BN <= 256)) ? 8 : 2;
   constexpr int STG = BK * (BM + BN);                  // staging floats per wave
   constexpr int RED = (NW / 2) * BM * BN;              // NW/2 partial tiles at a time
   constexpr int LDSF = NW * STG > RED ? NW * STG : RED;
@@ -115,55 +127,92 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   const int m0 = (rem % a.tiles_m) * BM;
   const int n0 = (rem / a.tiles_m) * BN;
 
+  const int YX = a.Y * a.X;
   const auto rdy = dev::rsrc(a.dy, a.dy_bytes);
-  const auto rw = dev::rsrc(a.w, a.w_bytes);
+  // W of this group only: k rows past K/G fall outside it and read 0.
+  const uint32_t wg_bytes = (uint32_t)(a.Kg * a.Cg * YX) * ES;
+  const auto rw = dev::rsrc((const char*)a.w + (size_t)__builtin_amdgcn_readfirstlane(g) * wg_bytes, wg_bytes);
   const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
 
-  const int YX = a.Y * a.X;
   const int kpt = (a.Kg + BK - 1) / BK;
   const int KT = s.taps_h * s.taps_w * kpt;
   const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
 
-  // Gather roles.  A: channel m0 + lane % BM, k rows lane / BM + (64/BM)*e.
-  // B: position n0 + lane % BN, k rows lane / BN + (64/BN)*e.
+  // Gather roles.  A: channel m0 + lane % BM, k rows lane / BM + AR*e.
+  // B: position n0 + lane % BN, k rows lane / BN + BR*e.  Each lane's part
+  // of an address is fixed (A) or fixed per tap (B); the k tile's part is
+  // wave-uniform and goes to the load's scalar offset.
+  constexpr int AR = 64 / BM, BR = 64 / BN;
   const int ac = m0 + lane % BM;
-  const bool ac_ok = ac < a.Cg;
   const int ak = lane / BM, bk = lane / BN;
+  const int a_ks = a.Cg * YX;  // W elements between k rows (both layouts)
+  const uint32_t a_lane =
+      ac < a.Cg ? (uint32_t)(LAYOUT == 0 ? (ak * a.Cg + ac) * YX : ak * a_ks + ac) * ES : dev::kOOB;
   const int bp = n0 + lane % BN;
   const bool bp_ok = bp < npos;
   const int bpp = bp_ok ? bp : 0;
   const int pn = bpp / npix_img;
   const int prr = bpp - pn * npix_img;
   const int pth = prr / s.pos_w, ptw = prr - (prr / s.pos_w) * s.pos_w;
-  // element strides along k
-  const int a_ks = LAYOUT == 0 ? a.Cg * YX : YX * a.Cg;
-  const int b_ks = LAYOUT == 0 ? a.Ho * a.Wo : 1;
+  const int b_ks = LAYOUT == 0 ? a.Ho * a.Wo : 1;  // dY elements between k rows
+  // dY element of (k row bk, dY pixel (pth, ptw) of image pn); a tap adds a
+  // wave-uniform pixel shift (times K for NHWC).
+  const int bpos = LAYOUT == 0 ? ((pn * a.K + g * a.Kg + bk) * a.Ho + pth) * a.Wo + ptw
+                               : ((pn * a.Ho + pth) * a.Wo + ptw) * a.K + g * a.Kg + bk;
 
-  auto gather = [&](int kt, float (&av)[AE], float (&bv)[BE]) {
-    const bool live = kt < kend;
-    const int ktc = live ? kt : 0;
-    const int tap = ktc / kpt;
-    const int k0 = (ktc - tap * kpt) * BK;
-    const int jh = tap / s.taps_w, jw = tap - (tap / s.taps_w) * s.taps_w;
-    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-    const int ho = dev::dy_index(a.no_split, pth, s.beta_h, a.delta_h, jh, a.pad_h, a.dil_h, a.str_h);
-    const int wo = dev::dy_index(a.no_split, ptw, s.beta_w, a.delta_w, jw, a.pad_w, a.dil_w, a.str_w);
-    const bool bok = live && bp_ok && ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
-    const int abase = LAYOUT == 0 ? ((g * a.Kg) * a.Cg + ac) * YX + ty * a.X + tx
-                                  : ((g * a.Kg) * YX + ty * a.X + tx) * a.Cg + ac;
-    const int bbase = LAYOUT == 0 ? ((pn * a.K + g * a.Kg) * a.Ho + ho) * a.Wo + wo
-                                  : ((pn * a.Ho + ho) * a.Wo + wo) * a.K + g * a.Kg;
-#pragma unroll
-    for (int e = 0; e < AE; e++) {
-      const int k = k0 + ak + (64 / BM) * e;
-      const bool ok = live && ac_ok && k < a.Kg;
-      av[e] = load_elem<DT>(rw, opaque(ok ? (uint32_t)(abase + k * a_ks) * ES : dev::kOOB));
+  // k tile -> (k tile within its tap, tap row, tap column); advanced
+  // without division (the walk is wave-uniform).
+  struct Walk {
+    int kk, jh, jw;
+  };
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  auto walk_at = [&](int kt) {
+    const int tap = kt / kpt;
+    return Walk{uni(kt - tap * kpt), uni(tap / s.taps_w), uni(tap - (tap / s.taps_w) * s.taps_w)};
+  };
+  auto advance = [&](Walk& w, int n) {
+    int kk = uni(w.kk) + n, jh = uni(w.jh), jw = uni(w.jw);
+    while (kk >= kpt) {
+      kk -= kpt;
+      if (++jw == s.taps_w) {
+        jw = 0;
+        ++jh;
+      }
     }
+    w = Walk{kk, jh, jw};
+  };
+
+  auto gather = [&](const Walk& w, bool live, float (&av)[AE], float (&bv)[BE]) {
+    const int k0 = w.kk * BK;
+    const int tapoff = (s.cls_h + a.tstep_h * w.jh) * a.X + s.cls_w + a.tstep_w * w.jw;
+    // (wave-uniform by construction; readfirstlane lets the compiler see it)
+    const uint32_t a_s = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(LAYOUT == 0 ? k0 * a_ks + tapoff : (k0 * YX + tapoff) * a.Cg) * ES);
+    int dh, dw;  // dY pixel shift of this tap
+    bool bok;
+    if constexpr (NS) {
+      const int ho = dev::dy_index(1, pth, s.beta_h, a.delta_h, w.jh, a.pad_h, a.dil_h, a.str_h);
+      const int wo = dev::dy_index(1, ptw, s.beta_w, a.delta_w, w.jw, a.pad_w, a.dil_w, a.str_w);
+      dh = ho - pth;
+      dw = wo - ptw;
+      bok = ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
+    } else {
+      dh = uni(s.beta_h - a.delta_h * w.jh);
+      dw = uni(s.beta_w - a.delta_w * w.jw);
+      bok = pth >= -dh && pth < a.Ho - dh && ptw >= -dw && ptw < a.Wo - dw;
+    }
+    bok = bok && live && bp_ok;
+    const int shift = LAYOUT == 0 ? dh * a.Wo + dw : (dh * a.Wo + dw) * a.K;
+    const uint32_t b_lane = bok ? (uint32_t)(bpos + shift) * ES : dev::kOOB;
+    const uint32_t al = live ? a_lane : dev::kOOB;
+    const int krem = a.Kg - k0;  // k rows of this tile inside K/G
+#pragma unroll
+    for (int e = 0; e < AE; e++)
+      av[e] = load_elem<DT>(rw, opaque(al), a_s + (uint32_t)(e * AR * a_ks) * ES);
 #pragma unroll
     for (int e = 0; e < BE; e++) {
-      const int k = k0 + bk + (64 / BN) * e;
-      const bool ok = bok && k < a.Kg;
-      bv[e] = load_elem<DT>(rdy, opaque(ok ? (uint32_t)(bbase + k * b_ks) * ES : dev::kOOB));
+      const uint32_t off = bk + BR * e < krem ? b_lane : dev::kOOB;
+      bv[e] = load_elem<DT>(rdy, opaque(off), __builtin_amdgcn_readfirstlane((uint32_t)((k0 + BR * e) * b_ks) * ES));
     }
   };
 
@@ -199,15 +248,32 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
     }
   };
 
-  // Wave-strided K loop, two tiles of gathers in flight.
-  float a0[AE], b0[BE], a1[AE], b1[BE];
-  gather(kbeg + wave, a0, b0);
-  for (int kt = kbeg + wave; kt < kend; kt += 2 * NW) {
-    gather(kt + NW, a1, b1);
-    compute(a0, b0);
-    if (kt + NW >= kend) break;
-    gather(kt + 2 * NW, a0, b0);
-    compute(a1, b1);
+  // Wave-strided K loop with up to DEPTH k tiles of gathers in flight (a
+  // ring of registers; a slot is refilled right after its tile is used).
+  // Tiles past this workgroup's k range are skipped, not gathered.
+  float av[DEPTH][AE], bv[DEPTH][BE];
+  Walk wn = walk_at(kbeg + wave);  // next tile to gather
+  int kn = kbeg + wave;
+#pragma unroll
+  for (int d = 0; d < DEPTH; d++) {
+    if (kn < kend) {
+      gather(wn, true, av[d], bv[d]);
+      advance(wn, NW);
+    }
+    kn += NW;
+  }
+  for (int kt = kbeg + wave; kt < kend; kt += DEPTH * NW) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) {
+      if (kt + d * NW < kend) {
+        compute(av[d], bv[d]);
+        if (kn < kend) {
+          gather(wn, true, av[d], bv[d]);
+          advance(wn, NW);
+        }
+        kn += NW;
+      }
+    }
   }
 
   // Cross-wave sum in a fixed order through LDS (reusing the staging area):
@@ -325,7 +391,9 @@ __global__ __launch_bounds__(256) void generic_finalize_kernel(const GemmArgs a)
 template <int DT, int LAYOUT, int BM, int BN, int NW = 4>
 int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW>,
+  const void* k = a.no_split ? (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, true>
+                             : (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false>;
+  return (int)hipLaunchKernel(k,
                               dim3((unsigned)grid), dim3(NW * 64), args, 0,
                               (hipStream_t)stream);
 }
