@@ -90,7 +90,7 @@ def kernel_key(info):
 
 
 # Headers every kernel source includes: a change in them changes the kernels.
-KERNEL_HEADERS = ("cbd_device.h", "cbd_kernarg.h", "cbd_internal.h")
+KERNEL_HEADERS = ("cbd_device.h", "cbd_kernarg.h", "cbd_internal.h", "generic_shapes.h")
 
 
 def kernel_digest(key):
@@ -595,6 +595,15 @@ def all_problems(args):
         g1.record(stream)
         torch.cuda.synchronize()
         us_graph = g0.elapsed_time(g1) * 1e3 / 200
+        # the descriptor-driven kernel of the same plan (static_shape=-1), for
+        # the shape-specialised instances' comparison
+        us_dyn = None
+        if info.static_shape:
+            pd = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                          (p.dh, p.dw), p.layout, dt, static_shape=-1)
+            for _ in range(10):
+                cbd.run(pd, dy_d, w_d, dx_d, stream=stream)
+            us_dyn = graph_us(cbd, torch, pd, dy_d, w_d, dx_d)
         flops, nbytes = info.useful_flops, algorithmic_bytes(p, info)
         if p.name in HBM_BOUND:
             bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
@@ -614,6 +623,8 @@ def all_problems(args):
             "launches": info.launches, "grid": info.grid_main,
             "useful_gflop": round(flops / 1e9, 5), "executed_gmac": round(info.executed_macs / 1e9, 5),
             "alg_mbytes": round(nbytes / 1e6, 3),
+            "static_shape": info.static_shape,
+            "us_graph_descriptor_driven": round(us_dyn, 2) if us_dyn is not None else None,
             "us_warm": round(warm, 2), "us_graph": round(us_graph, 2),
             "us_cold_median": round(med, 2),
             "us_cold_p10": round(float(np.percentile(cold, 10)), 2),

@@ -98,7 +98,9 @@ struct GemmArgs {
   int32_t grp_wide;    // 1: the 16x16x16-MFMA kernel (bf16, C/G = K/G in {16, 32})
   int32_t gen_waves;   // generic family: waves per workgroup (4, or 8 for long K on small grids)
   int32_t ksplit;      // large-tile kernel: workgroups sharing a tile's K loop (<= 1: none)
-  int32_t static_shape;  // large-tile kernel: 1 = 64 k tiles per tap, 1 tap; 2 = the fixed 2048-channel geometry
+  int32_t static_shape;  // large-tile kernel: 1 = 64 k tiles per tap, 1 tap; 2 = the fixed 2048-channel
+                         // geometry; generic family: 2 = the instance generic_shapes.h lists as static_id
+  int32_t static_id;
   void* ws;            // split-K f32 partial tiles, 256 KiB per workgroup (caller's workspace)
   const void* dy;
   const void* w;
@@ -113,6 +115,18 @@ struct GemmArgs {
 // Kernel arguments travel in the 4 KiB kernel-argument segment.
 static_assert(sizeof(GemmArgs) <= 4096, "GemmArgs exceeds the kernel-argument segment");
 
+
+// The whole geometry of one generic-family plan, fixed at compile time in a
+// shape-specialised instance.  The planner runs the instance only when every
+// field equals the one of the plan it built.
+constexpr int kShapeMaxSub = 4;
+struct ShapeKey {
+  int32_t layout, dtype, bm, bn, nw;
+  int32_t N, G, C, K, Cg, Kg, Hi, Wi, Ho, Wo, Y, X, Sh, Sw;
+  int32_t tstep_h, tstep_w, delta_h, delta_w;
+  int32_t tiles_m, total_tiles, xcd_remap, num_sub;
+  SubDesc sub[kShapeMaxSub];
+};
 
 struct ZeroArgs {
   int32_t N, C, Hi, Wi, Sh, Sw;

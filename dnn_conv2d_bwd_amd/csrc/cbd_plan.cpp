@@ -27,6 +27,7 @@
 #include <string>
 
 #include "cbd_internal.h"
+#include "generic_shapes.h"
 
 namespace {
 
@@ -252,6 +253,28 @@ void log_plan(const cbd_plan_s& pl) {
   for (const cbd_zero_region_t& z : pl.zeros)
     std::fprintf(stderr, "[cbd]   zero region: phase (%d,%d), %lldx%lld positions\n", z.phase_h, z.phase_w,
                  (long long)z.pos_h, (long long)z.pos_w);
+}
+
+// Every field of a compiled generic-family shape equals the plan's.
+bool generic_shape_matches(const cbd::ShapeKey& k, const cbd::GemmArgs& a, const cbd_problem& p, int64_t threads) {
+  if (k.layout != p.layout || k.dtype != p.dtype || k.bm != a.tile_m || k.bn != a.tile_n ||
+      k.nw * 64 != threads)
+    return false;
+  if (k.N != a.N || k.G != a.G || k.C != a.C || k.K != a.K || k.Cg != a.Cg || k.Kg != a.Kg || k.Hi != a.Hi ||
+      k.Wi != a.Wi || k.Ho != a.Ho || k.Wo != a.Wo || k.Y != a.Y || k.X != a.X || k.Sh != a.Sh || k.Sw != a.Sw)
+    return false;
+  if (k.tstep_h != a.tstep_h || k.tstep_w != a.tstep_w || k.delta_h != a.delta_h || k.delta_w != a.delta_w ||
+      k.tiles_m != a.tiles_m || k.total_tiles != a.total_tiles || k.xcd_remap != a.xcd_remap ||
+      k.num_sub != a.num_sub || a.num_sub > cbd::kShapeMaxSub)
+    return false;
+  for (int q = 0; q < a.num_sub; q++) {
+    const cbd::SubDesc &x = k.sub[q], &y = a.sub[q];
+    if (x.phase_h != y.phase_h || x.phase_w != y.phase_w || x.beta_h != y.beta_h || x.beta_w != y.beta_w ||
+        x.taps_h != y.taps_h || x.taps_w != y.taps_w || x.cls_h != y.cls_h || x.cls_w != y.cls_w ||
+        x.pos_h != y.pos_h || x.pos_w != y.pos_w || x.tile_begin != y.tile_begin)
+      return false;
+  }
+  return true;
 }
 
 // Shortest K loop of any class, in k tiles of the family (split-K gives
@@ -684,11 +707,11 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     for (size_t i = 0; ok2 && i < subs.size(); i++)
       ok2 = subs[i].phase_w == (int32_t)i && subs[i].class_w == (int32_t)i && subs[i].beta_w == 0 &&
             subs[i].phase_h == 0 && subs[i].beta_h == 0 && subs[i].pos_h == 1 && subs[i].pos_w == Wo;
-    if (static_mode == 1 && !ok1) {
+    if (static_mode == 1 && kernel != CBD_KERNEL_GENERIC && !ok1) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this problem "
                                        "(built: NHWC bf16, K/G = 2048, one tap per class, residue split, "
-                                       "no K split)");
+                                       "no K split; and the generic family's listed workload shapes)");
     }
     static_shape = static_mode < 0 ? 0 : ok2 ? 2 : ok1 ? 1 : 0;
   }
@@ -790,6 +813,24 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     d.pos_h = (int32_t)s.pos_h; d.pos_w = (int32_t)s.pos_w;
     d.tile_begin = (int32_t)s.tile_begin;
     a.class_begin[i] = d.tile_begin;
+  }
+  // Generic family: the shape-specialised instance whose compiled geometry
+  // is exactly this plan's, if one was built.
+  a.static_id = 0;
+  if (kernel == CBD_KERNEL_GENERIC && static_mode >= 0 && ksplit == 1 && !no_split && !per_class) {
+    for (int i = 0; i < cbd::kGenericShapes; i++) {
+      if (generic_shape_matches(cbd::kGenericShapeKeys[i], a, p, threads)) {
+        static_shape = 2;
+        a.static_shape = 2;
+        a.static_id = i;
+        break;
+      }
+    }
+  }
+  if (static_mode == 1 && kernel == CBD_KERNEL_GENERIC && static_shape == 0) {
+    delete pl;
+    return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance of the generic family for this plan "
+                                     "(built for the listed workload shapes only)");
   }
 
   cbd::ZeroArgs& z = pl->zero;

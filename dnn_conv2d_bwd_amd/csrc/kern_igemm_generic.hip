@@ -37,6 +37,7 @@
 // order and writes dX.
 #include "cbd_device.h"
 #include "cbd_internal.h"
+#include "generic_shapes.h"
 
 namespace cbd {
 namespace {
@@ -70,11 +71,58 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
   }
 }
 
+// Geometry of a launch: read from the kernel arguments (DynGeo, the
+// descriptor-driven instances) or fixed at compile time (StatGeo<T>, the
+// shape-specialised instances: T::k is one plan's whole geometry, so every
+// index computation folds to constants and no argument is read before the
+// first gather but the three tensor pointers, which arrive preloaded).
+struct DynGeo {
+  static constexpr bool kStatic = false;
+#define CBD_DYN(f) \
+  __device__ static int f(const GemmArgs& a) { return a.f; }
+  CBD_DYN(N) CBD_DYN(C) CBD_DYN(K) CBD_DYN(Cg) CBD_DYN(Kg) CBD_DYN(Hi) CBD_DYN(Wi) CBD_DYN(Ho)
+  CBD_DYN(Wo) CBD_DYN(Y) CBD_DYN(X) CBD_DYN(Sh) CBD_DYN(Sw) CBD_DYN(tstep_h) CBD_DYN(tstep_w)
+  CBD_DYN(delta_h) CBD_DYN(delta_w) CBD_DYN(tiles_m) CBD_DYN(total_tiles) CBD_DYN(xcd_remap)
+  CBD_DYN(ksplit)
+#undef CBD_DYN
+  __device__ static uint32_t dy_bytes(const GemmArgs& a) { return a.dy_bytes; }
+  __device__ static uint32_t dx_bytes(const GemmArgs& a) { return a.dx_bytes; }
+  __device__ static SubDesc sub(const GemmArgs& a, int t) { return a.sub[dev::find_class(a, t)]; }
+};
+
+template <class T>
+struct StatGeo {
+  static constexpr bool kStatic = true;
+#define CBD_STAT(f) \
+  __device__ static constexpr int f(const GemmArgs&) { return T::k.f; }
+  CBD_STAT(N) CBD_STAT(C) CBD_STAT(K) CBD_STAT(Cg) CBD_STAT(Kg) CBD_STAT(Hi) CBD_STAT(Wi) CBD_STAT(Ho)
+  CBD_STAT(Wo) CBD_STAT(Y) CBD_STAT(X) CBD_STAT(Sh) CBD_STAT(Sw) CBD_STAT(tstep_h) CBD_STAT(tstep_w)
+  CBD_STAT(delta_h) CBD_STAT(delta_w) CBD_STAT(tiles_m) CBD_STAT(total_tiles) CBD_STAT(xcd_remap)
+#undef CBD_STAT
+  __device__ static constexpr int ksplit(const GemmArgs&) { return 0; }
+  static constexpr uint32_t kEs = T::k.dtype == CBD_F32 ? 4 : 2;
+  __device__ static constexpr uint32_t dy_bytes(const GemmArgs&) {
+    return (uint32_t)(T::k.N * T::k.K * T::k.Ho * T::k.Wo) * kEs;
+  }
+  __device__ static constexpr uint32_t dx_bytes(const GemmArgs&) {
+    return (uint32_t)(T::k.N * T::k.C * T::k.Hi * T::k.Wi) * kEs;
+  }
+  // The class of logical tile t: classes own ascending tile ranges.
+  __device__ static SubDesc sub(const GemmArgs&, int t) {
+    SubDesc r = T::k.sub[0];
+#pragma unroll
+    for (int q = 1; q < T::k.num_sub; q++)
+      if (t >= T::k.sub[q].tile_begin) r = T::k.sub[q];
+    return r;
+  }
+};
+
 // NS: the zero-insertion form (no residue split: each tap's dY index needs a
 // divisibility test); otherwise a tap's dY index is the position plus a
 // wave-uniform shift.
-template <int DT, int LAYOUT, int BM, int BN, int NW, bool NS>
-__global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArgs a) {
+template <int DT, int LAYOUT, int BM, int BN, int NW, bool NS, class Geo>
+__global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* dy_p, const void* w_p, void* dx_p,
+                                                                   const GemmArgs a) {
   constexpr int BK = generic_bk(BM, BN);    // 8 (32x32 tiles) or 16
   constexpr int THREADS = NW * 64;          // NW (4 or 8) waves, each its own k tiles
   constexpr int MB = BM / 16, NB = BN / 16;
@@ -92,16 +140,22 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
   __shared__ float lds[LDSF];
 
-  dev::prefetch_args(a);
+  if constexpr (!Geo::kStatic) dev::prefetch_args(a);
+  const int N = Geo::N(a), C = Geo::C(a), K = Geo::K(a), Cg = Geo::Cg(a), Kg = Geo::Kg(a);
+  const int Hi = Geo::Hi(a), Wi = Geo::Wi(a), Ho = Geo::Ho(a), Wo = Geo::Wo(a);
+  const int Yf = Geo::Y(a), Xf = Geo::X(a), Sh = Geo::Sh(a), Sw = Geo::Sw(a);
+  const int tstep_h = Geo::tstep_h(a), tstep_w = Geo::tstep_w(a);
+  const int delta_h = Geo::delta_h(a), delta_w = Geo::delta_w(a);
+  const int tiles_m = Geo::tiles_m(a), total_tiles = Geo::total_tiles(a);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
 
-  if ((int)blockIdx.x >= a.total_tiles) {  // zero-fill folded into this launch (four-wave plans)
+  if ((int)blockIdx.x >= total_tiles) {  // zero-fill folded into this launch (four-wave plans)
     if constexpr (NW != 4) return;
     const FusedZero& z = a.fz;
-    const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+    const auto rdx = dev::rsrc(dx_p, Geo::dx_bytes(a));
     const uint32_t base =
-        (uint32_t)(blockIdx.x - a.total_tiles) * (kGenericThreads * kZeroItemsPerThread) + tid;
+        (uint32_t)(blockIdx.x - total_tiles) * (kGenericThreads * kZeroItemsPerThread) + tid;
 #pragma unroll
     for (int i = 0; i < kZeroItemsPerThread; i++) {
       const uint32_t item = base + (uint32_t)(i * kGenericThreads);
@@ -112,29 +166,29 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
     return;
   }
 
-  const int t = dev::logical_tile(blockIdx.x, a.total_tiles, a.xcd_remap);
-  const SubDesc s = a.sub[dev::find_class(a, t)];
+  const int t = dev::logical_tile(blockIdx.x, total_tiles, Geo::xcd_remap(a));
+  const SubDesc s = Geo::sub(a, t);
   const int npix_img = s.pos_h * s.pos_w;
-  const int npos = a.N * npix_img;
+  const int npos = N * npix_img;
   const int tiles_n = (npos + BN - 1) / BN;
-  const int per_group = a.tiles_m * tiles_n;
-  const int S = a.ksplit > 1 ? a.ksplit : 1;
+  const int per_group = tiles_m * tiles_n;
+  const int S = Geo::ksplit(a) > 1 ? Geo::ksplit(a) : 1;
   const int lt = t - s.tile_begin;
   const int local = lt / S;
   const int sp = lt - local * S;  // split index (0 without split-K)
   const int g = local / per_group;
   const int rem = local - g * per_group;
-  const int m0 = (rem % a.tiles_m) * BM;
-  const int n0 = (rem / a.tiles_m) * BN;
+  const int m0 = (rem % tiles_m) * BM;
+  const int n0 = (rem / tiles_m) * BN;
 
-  const int YX = a.Y * a.X;
-  const auto rdy = dev::rsrc(a.dy, a.dy_bytes);
+  const int YX = Yf * Xf;
+  const auto rdy = dev::rsrc(dy_p, Geo::dy_bytes(a));
   // W of this group only: k rows past K/G fall outside it and read 0.
-  const uint32_t wg_bytes = (uint32_t)(a.Kg * a.Cg * YX) * ES;
-  const auto rw = dev::rsrc((const char*)a.w + (size_t)__builtin_amdgcn_readfirstlane(g) * wg_bytes, wg_bytes);
-  const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+  const uint32_t wg_bytes = (uint32_t)(Kg * Cg * YX) * ES;
+  const auto rw = dev::rsrc((const char*)w_p + (size_t)__builtin_amdgcn_readfirstlane(g) * wg_bytes, wg_bytes);
+  const auto rdx = dev::rsrc(dx_p, Geo::dx_bytes(a));
 
-  const int kpt = (a.Kg + BK - 1) / BK;
+  const int kpt = (Kg + BK - 1) / BK;
   const int KT = s.taps_h * s.taps_w * kpt;
   const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
 
@@ -145,20 +199,20 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   constexpr int AR = 64 / BM, BR = 64 / BN;
   const int ac = m0 + lane % BM;
   const int ak = lane / BM, bk = lane / BN;
-  const int a_ks = a.Cg * YX;  // W elements between k rows (both layouts)
+  const int a_ks = Cg * YX;  // W elements between k rows (both layouts)
   const uint32_t a_lane =
-      ac < a.Cg ? (uint32_t)(LAYOUT == 0 ? (ak * a.Cg + ac) * YX : ak * a_ks + ac) * ES : dev::kOOB;
+      ac < Cg ? (uint32_t)(LAYOUT == 0 ? (ak * Cg + ac) * YX : ak * a_ks + ac) * ES : dev::kOOB;
   const int bp = n0 + lane % BN;
   const bool bp_ok = bp < npos;
   const int bpp = bp_ok ? bp : 0;
   const int pn = bpp / npix_img;
   const int prr = bpp - pn * npix_img;
   const int pth = prr / s.pos_w, ptw = prr - (prr / s.pos_w) * s.pos_w;
-  const int b_ks = LAYOUT == 0 ? a.Ho * a.Wo : 1;  // dY elements between k rows
+  const int b_ks = LAYOUT == 0 ? Ho * Wo : 1;  // dY elements between k rows
   // dY element of (k row bk, dY pixel (pth, ptw) of image pn); a tap adds a
   // wave-uniform pixel shift (times K for NHWC).
-  const int bpos = LAYOUT == 0 ? ((pn * a.K + g * a.Kg + bk) * a.Ho + pth) * a.Wo + ptw
-                               : ((pn * a.Ho + pth) * a.Wo + ptw) * a.K + g * a.Kg + bk;
+  const int bpos = LAYOUT == 0 ? ((pn * K + g * Kg + bk) * Ho + pth) * Wo + ptw
+                               : ((pn * Ho + pth) * Wo + ptw) * K + g * Kg + bk;
 
   // k tile -> (k tile within its tap, tap row, tap column); advanced
   // without division (the walk is wave-uniform).
@@ -184,28 +238,28 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
 
   auto gather = [&](const Walk& w, bool live, float (&av)[AE], float (&bv)[BE]) {
     const int k0 = w.kk * BK;
-    const int tapoff = (s.cls_h + a.tstep_h * w.jh) * a.X + s.cls_w + a.tstep_w * w.jw;
+    const int tapoff = (s.cls_h + tstep_h * w.jh) * Xf + s.cls_w + tstep_w * w.jw;
     // (wave-uniform by construction; readfirstlane lets the compiler see it)
     const uint32_t a_s = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(LAYOUT == 0 ? k0 * a_ks + tapoff : (k0 * YX + tapoff) * a.Cg) * ES);
+        (uint32_t)(LAYOUT == 0 ? k0 * a_ks + tapoff : (k0 * YX + tapoff) * Cg) * ES);
     int dh, dw;  // dY pixel shift of this tap
     bool bok;
     if constexpr (NS) {
-      const int ho = dev::dy_index(1, pth, s.beta_h, a.delta_h, w.jh, a.pad_h, a.dil_h, a.str_h);
-      const int wo = dev::dy_index(1, ptw, s.beta_w, a.delta_w, w.jw, a.pad_w, a.dil_w, a.str_w);
+      const int ho = dev::dy_index(1, pth, s.beta_h, delta_h, w.jh, a.pad_h, a.dil_h, a.str_h);
+      const int wo = dev::dy_index(1, ptw, s.beta_w, delta_w, w.jw, a.pad_w, a.dil_w, a.str_w);
       dh = ho - pth;
       dw = wo - ptw;
-      bok = ho >= 0 && ho < a.Ho && wo >= 0 && wo < a.Wo;
+      bok = ho >= 0 && ho < Ho && wo >= 0 && wo < Wo;
     } else {
-      dh = uni(s.beta_h - a.delta_h * w.jh);
-      dw = uni(s.beta_w - a.delta_w * w.jw);
-      bok = pth >= -dh && pth < a.Ho - dh && ptw >= -dw && ptw < a.Wo - dw;
+      dh = uni(s.beta_h - delta_h * w.jh);
+      dw = uni(s.beta_w - delta_w * w.jw);
+      bok = pth >= -dh && pth < Ho - dh && ptw >= -dw && ptw < Wo - dw;
     }
     bok = bok && live && bp_ok;
-    const int shift = LAYOUT == 0 ? dh * a.Wo + dw : (dh * a.Wo + dw) * a.K;
+    const int shift = LAYOUT == 0 ? dh * Wo + dw : (dh * Wo + dw) * K;
     const uint32_t b_lane = bok ? (uint32_t)(bpos + shift) * ES : dev::kOOB;
     const uint32_t al = live ? a_lane : dev::kOOB;
-    const int krem = a.Kg - k0;  // k rows of this tile inside K/G
+    const int krem = Kg - k0;  // k rows of this tile inside K/G
 #pragma unroll
     for (int e = 0; e < AE; e++)
       av[e] = load_elem<DT>(rw, opaque(al), a_s + (uint32_t)(e * AR * a_ks) * ES);
@@ -332,16 +386,16 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const GemmArg
   const int n = pp / npix_img;
   const int rr = pp - n * npix_img;
   const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
-  const int hi = s.phase_h + a.Sh * th, wi = s.phase_w + a.Sw * tw;
-  const int pbase = LAYOUT == 0 ? (n * a.C + g * a.Cg) * a.Hi * a.Wi + hi * a.Wi + wi
-                                : ((n * a.Hi + hi) * a.Wi + wi) * a.C + g * a.Cg;
-  const int cstride = LAYOUT == 0 ? a.Hi * a.Wi : 1;
+  const int hi = s.phase_h + Sh * th, wi = s.phase_w + Sw * tw;
+  const int pbase = LAYOUT == 0 ? (n * C + g * Cg) * Hi * Wi + hi * Wi + wi
+                                : ((n * Hi + hi) * Wi + wi) * C + g * Cg;
+  const int cstride = LAYOUT == 0 ? Hi * Wi : 1;
 #pragma unroll
   for (int i = 0; i < BM * BN / THREADS; i++) {
     const int m = tid / BN + (THREADS / BN) * i;
     const float v = lds[m * BN + tid % BN] + lds[(BM + m) * BN + tid % BN];
     const int c = m0 + m;
-    store_elem<DT>(rdx, (pv && c < a.Cg) ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB, v);
+    store_elem<DT>(rdx, (pv && c < Cg) ? (uint32_t)(pbase + c * cstride) * ES : dev::kOOB, v);
   }
 }
 
@@ -390,9 +444,12 @@ __global__ __launch_bounds__(256) void generic_finalize_kernel(const GemmArgs a)
 
 template <int DT, int LAYOUT, int BM, int BN, int NW = 4>
 int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
-  void* args[] = {const_cast<GemmArgs*>(&a)};
-  const void* k = a.no_split ? (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, true>
-                             : (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false>;
+  const void* dy = a.dy;
+  const void* w = a.w;
+  void* dx = a.dx;
+  void* args[] = {&dy, &w, &dx, const_cast<GemmArgs*>(&a)};
+  const void* k = a.no_split ? (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, true, DynGeo>
+                             : (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeo>;
   return (int)hipLaunchKernel(k,
                               dim3((unsigned)grid), dim3(NW * 64), args, 0,
                               (hipStream_t)stream);
@@ -416,6 +473,31 @@ int launch_fin_tiles(const GemmArgs& a, int64_t grid, void* stream) {
   return (int)hipErrorInvalidValue;
 }
 
+// A shape-specialised instance (StatGeo<T>): its tile shape and dtype/layout
+// come from T's geometry.
+template <class T>
+int launch_stat(const GemmArgs& a, int64_t grid, void* stream) {
+  constexpr int DT = T::k.dtype == CBD_F32 ? 0 : 1;
+  const void* dy = a.dy;
+  const void* w = a.w;
+  void* dx = a.dx;
+  void* args[] = {&dy, &w, &dx, const_cast<GemmArgs*>(&a)};
+  const void* k =
+      (const void*)&igemm_generic_kernel<DT, T::k.layout, T::k.bm, T::k.bn, T::k.nw, false, StatGeo<T>>;
+  return (int)hipLaunchKernel(k, dim3((unsigned)grid), dim3(T::k.nw * 64), args, 0, (hipStream_t)stream);
+}
+
+int launch_static(const GemmArgs& a, int64_t grid, void* stream) {
+  switch (a.static_id) {
+#define CBD_CASE(i, T, name) \
+  case i:                    \
+    return launch_stat<T>(a, grid, stream);
+    CBD_GENERIC_SHAPE_LIST(CBD_CASE)
+#undef CBD_CASE
+  }
+  return (int)hipErrorInvalidValue;
+}
+
 template <int DT, int LAYOUT>
 int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
   if (a.tile_m == 64 && a.tile_n == 64) return launch_one<DT, LAYOUT, 64, 64>(a, grid, stream);
@@ -432,6 +514,7 @@ int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
 }  // namespace
 
 int launch_generic(const GemmArgs& a, int layout, int dtype, int64_t grid, void* stream) {
+  if (a.static_shape == 2) return launch_static(a, grid, stream);
   if (dtype == CBD_F32)
     return layout == CBD_LAYOUT_NCHW ? launch_tiles<0, 0>(a, grid, stream)
                                      : launch_tiles<0, 1>(a, grid, stream);

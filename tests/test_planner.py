@@ -341,6 +341,36 @@ def test_static_shape_plans():
         cbd.plan(*args, static_shape=1, ksplit=2)
 
 
+GENERIC_STATIC = ("c1", "c2-14-1", "c2-14-3", "c2-15-1", "c2-15-3", "c2-16-1", "c2-16-3", "c3a", "c3b")
+
+
+def test_generic_static_shapes():
+    """Every workload problem on the generic family finds its
+    shape-specialised instance (the compiled table is current), with the
+    same launch as the descriptor-driven plan; other shapes, split-K,
+    per-class, no-split and static_shape=-1 plans do not, and requiring one
+    where none exists is refused."""
+    by = {q.name: q for q in PROBLEMS}
+    for name in GENERIC_STATIC:
+        p = by[name]
+        a, b = plan_of(p).info(), plan_of(p, cbd.KERNEL_GENERIC).info()
+        assert (a.kernel, a.static_shape, b.static_shape) == (cbd.KERNEL_GENERIC, 2, 2), name
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        args = (p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw), (p.dh, p.dw), p.layout, dt)
+        d = cbd.plan(*args, static_shape=-1).info()
+        assert d.static_shape == 0
+        assert (d.grid_main, d.grid_zero, d.launches, d.tile_m, d.tile_n, d.threads_main) == \
+            (a.grid_main, a.grid_zero, a.launches, a.tile_m, a.tile_n, a.threads_main)
+        assert cbd.plan(*args, static_shape=1).info().static_shape == 2
+        for kw in ({"ksplit": 2}, {"per_class": True}, {"no_split": True}):
+            assert cbd.plan(*args, **kw).info().static_shape == 0, (name, kw)
+    # a batch the table does not hold: the descriptor-driven kernel
+    c3a = by["c3a"]
+    assert plan_of(c3a.with_(n=31)).info().static_shape == 0
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(31, 1, 64, 64, 28, 28, 3, 3, 2, 1, 1, "nchw", "f32", static_shape=1)
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"),
                     reason="passes made-up device addresses to a real launch: only on a machine "
                            "with no GPU driver at all, where the launch itself must fail")
