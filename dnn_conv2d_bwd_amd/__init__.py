@@ -73,7 +73,8 @@ class PlanInfo(ctypes.Structure):
                 ("variant", ctypes.c_int64),
                 ("align_dy", ctypes.c_int32), ("align_w", ctypes.c_int32),
                 ("align_dx", ctypes.c_int32),
-                ("auto_ksplit", ctypes.c_int64), ("auto_workspace_bytes", ctypes.c_int64)]
+                ("auto_ksplit", ctypes.c_int64), ("auto_workspace_bytes", ctypes.c_int64),
+                ("zero_in_epilogue", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
 
 
 class SubGemm(ctypes.Structure):

@@ -101,6 +101,8 @@ struct GemmArgs {
   int32_t static_shape;  // large-tile kernel: 1 = 64 k tiles per tap, 1 tap; 2 = the fixed 2048-channel
                          // geometry; generic family: 2 = the instance generic_shapes.h lists as static_id
   int32_t static_id;
+  int32_t zblock;      // generic family, one class at phase (0,0) covering every S x S block of dX: its
+                       // epilogue also writes the block's unreached positions (no zero-fill)
   void* ws;            // split-K f32 partial tiles, 256 KiB per workgroup (caller's workspace)
   const void* dy;
   const void* w;
@@ -124,7 +126,7 @@ struct ShapeKey {
   int32_t layout, dtype, bm, bn, nw;
   int32_t N, G, C, K, Cg, Kg, Hi, Wi, Ho, Wo, Y, X, Sh, Sw;
   int32_t tstep_h, tstep_w, delta_h, delta_w;
-  int32_t tiles_m, total_tiles, xcd_remap, num_sub;
+  int32_t tiles_m, total_tiles, xcd_remap, num_sub, zblock;
   SubDesc sub[kShapeMaxSub];
 };
 

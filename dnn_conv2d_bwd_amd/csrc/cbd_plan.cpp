@@ -255,6 +255,12 @@ void log_plan(const cbd_plan_s& pl) {
                  (long long)z.pos_h, (long long)z.pos_w);
 }
 
+// Whole-block epilogue writing pairs of dX elements (value, 0): NCHW with
+// stride 2 along W and an even width.
+bool zblock_pairs(const cbd_problem& p) {
+  return p.layout == CBD_LAYOUT_NCHW && p.stride_w == 2 && p.wi % 2 == 0;
+}
+
 // Every field of a compiled generic-family shape equals the plan's.
 bool generic_shape_matches(const cbd::ShapeKey& k, const cbd::GemmArgs& a, const cbd_problem& p, int64_t threads) {
   if (k.layout != p.layout || k.dtype != p.dtype || k.bm != a.tile_m || k.bn != a.tile_n ||
@@ -265,7 +271,7 @@ bool generic_shape_matches(const cbd::ShapeKey& k, const cbd::GemmArgs& a, const
     return false;
   if (k.tstep_h != a.tstep_h || k.tstep_w != a.tstep_w || k.delta_h != a.delta_h || k.delta_w != a.delta_w ||
       k.tiles_m != a.tiles_m || k.total_tiles != a.total_tiles || k.xcd_remap != a.xcd_remap ||
-      k.num_sub != a.num_sub || a.num_sub > cbd::kShapeMaxSub)
+      k.num_sub != a.num_sub || k.zblock != a.zblock || a.num_sub > cbd::kShapeMaxSub)
     return false;
   for (int q = 0; q < a.num_sub; q++) {
     const cbd::SubDesc &x = k.sub[q], &y = a.sub[q];
@@ -814,6 +820,15 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     d.tile_begin = (int32_t)s.tile_begin;
     a.class_begin[i] = d.tile_begin;
   }
+  // Generic family, one class at phase (0,0) whose lattice is every S x S
+  // block of dX (a 1x1 filter at stride S, for one): the main kernel's
+  // epilogue writes each block whole, zeros included, instead of leaving
+  // the other phases to zero-fill workgroups.
+  const bool zblock = kernel == CBD_KERNEL_GENERIC && !per_class && !no_split && ksplit == 1 &&
+                      subs.size() == 1 && p.stride_h * p.stride_w > 1 && p.stride_h * p.stride_w <= 16 &&
+                      subs[0].phase_h == 0 && subs[0].phase_w == 0 &&
+                      subs[0].pos_h == ceil_div(p.hi, p.stride_h) && subs[0].pos_w == ceil_div(p.wi, p.stride_w);
+  a.zblock = zblock ? 1 : 0;
   // Generic family: the shape-specialised instance whose compiled geometry
   // is exactly this plan's, if one was built.
   a.static_id = 0;
@@ -865,11 +880,12 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   // launch as extra workgroups (one launch instead of two).
   int64_t grid_zero = ceil_div(items, int64_t(cbd::kZeroThreads) * cbd::kZeroItemsPerThread);
   int64_t grid_main = tile;
-  // The row-block family writes unreached positions itself.
-  if (kernel == CBD_KERNEL_NCHW_ROWS) grid_zero = 0;
+  // The row-block family, and the generic family's whole-block epilogue,
+  // write unreached positions themselves.
+  if (kernel == CBD_KERNEL_NCHW_ROWS || zblock) grid_zero = 0;
   a.rg = rgeom;
   std::memset(&a.fz, 0, sizeof(a.fz));
-  if (kernel == CBD_KERNEL_GENERIC && !per_class && items > 0 &&
+  if (kernel == CBD_KERNEL_GENERIC && !per_class && !zblock && items > 0 &&
       (int64_t)zeros.size() <= cbd::kMaxFusedZero &&
       threads == cbd::kZeroThreads &&
       (tile + grid_zero) * threads < (int64_t(1) << 32)) {
@@ -909,12 +925,15 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   info.workspace_bytes = ksplit > 1 ? tile * bm * bn * 4 : 0;  // one f32 partial per (tile, split)
   info.auto_ksplit = 1;
   info.auto_workspace_bytes = 0;
+  info.zero_in_epilogue = (zblock || kernel == CBD_KERNEL_NCHW_ROWS) && zero_elems > 0 ? 1 : 0;
+  info.reserved_ = 0;
   // Pointer alignment: the generic family gathers and stores single
   // elements; a zero-fill of NHWC rows writes 16-byte chunks; the other
   // families move 16-byte vectors.
   if (kernel == CBD_KERNEL_GENERIC) {
     info.align_dy = info.align_w = (int32_t)es;
-    info.align_dx = (zero_elems > 0 && z.chunk == 16) ? 16 : (int32_t)es;
+    info.align_dx = zblock ? (zblock_pairs(p) ? 2 * (int32_t)es : (int32_t)es)
+                    : (zero_elems > 0 && z.chunk == 16) ? 16 : (int32_t)es;
   } else if (kernel == CBD_KERNEL_NCHW_ROWS) {
     // element loads of dY (16-byte loads of W when its rows allow);
     // whole dX rows in the widest store that divides a row

@@ -62,6 +62,18 @@ __device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint3
   }
 }
 
+// Two adjacent elements (lo at byte_off).
+template <int DT>
+__device__ inline void store_pair(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float lo, float hi) {
+  if constexpr (DT == 0) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = {__float_as_uint(lo), __float_as_uint(hi)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(dev::bf16_pack2(lo, hi), r, byte_off, 0, 0);
+  }
+}
+
 template <int DT>
 __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
   if constexpr (DT == 0) {
@@ -83,7 +95,7 @@ struct DynGeo {
   CBD_DYN(N) CBD_DYN(C) CBD_DYN(K) CBD_DYN(Cg) CBD_DYN(Kg) CBD_DYN(Hi) CBD_DYN(Wi) CBD_DYN(Ho)
   CBD_DYN(Wo) CBD_DYN(Y) CBD_DYN(X) CBD_DYN(Sh) CBD_DYN(Sw) CBD_DYN(tstep_h) CBD_DYN(tstep_w)
   CBD_DYN(delta_h) CBD_DYN(delta_w) CBD_DYN(tiles_m) CBD_DYN(total_tiles) CBD_DYN(xcd_remap)
-  CBD_DYN(ksplit)
+  CBD_DYN(ksplit) CBD_DYN(zblock)
 #undef CBD_DYN
   __device__ static uint32_t dy_bytes(const GemmArgs& a) { return a.dy_bytes; }
   __device__ static uint32_t dx_bytes(const GemmArgs& a) { return a.dx_bytes; }
@@ -98,6 +110,7 @@ struct StatGeo {
   CBD_STAT(N) CBD_STAT(C) CBD_STAT(K) CBD_STAT(Cg) CBD_STAT(Kg) CBD_STAT(Hi) CBD_STAT(Wi) CBD_STAT(Ho)
   CBD_STAT(Wo) CBD_STAT(Y) CBD_STAT(X) CBD_STAT(Sh) CBD_STAT(Sw) CBD_STAT(tstep_h) CBD_STAT(tstep_w)
   CBD_STAT(delta_h) CBD_STAT(delta_w) CBD_STAT(tiles_m) CBD_STAT(total_tiles) CBD_STAT(xcd_remap)
+  CBD_STAT(zblock)
 #undef CBD_STAT
   __device__ static constexpr int ksplit(const GemmArgs&) { return 0; }
   static constexpr uint32_t kEs = T::k.dtype == CBD_F32 ? 4 : 2;
@@ -390,6 +403,33 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   const int pbase = LAYOUT == 0 ? (n * C + g * Cg) * Hi * Wi + hi * Wi + wi
                                 : ((n * Hi + hi) * Wi + wi) * C + g * Cg;
   const int cstride = LAYOUT == 0 ? Hi * Wi : 1;
+  if (Geo::zblock(a)) {
+    // One class at phase (0,0) over every S x S block: write the block,
+    // the value at its corner and zeros at the unreached positions (in
+    // element pairs along W for NCHW at stride 2 and an even width).
+    const bool pairs = LAYOUT == 0 && Sw == 2 && (Wi & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < BM * BN / THREADS; i++) {
+      const int m = tid / BN + (THREADS / BN) * i;
+      const float v = lds[m * BN + tid % BN] + lds[(BM + m) * BN + tid % BN];
+      const int c = m0 + m;
+      const bool ok = pv && c < Cg;
+      const int e0 = pbase + c * cstride;
+      if (pairs) {
+        store_pair<DT>(rdx, ok ? (uint32_t)e0 * ES : dev::kOOB, v, 0.f);
+        for (int dh = 1; dh < Sh; dh++)
+          store_pair<DT>(rdx, (ok && hi + dh < Hi) ? (uint32_t)(e0 + dh * Wi) * ES : dev::kOOB, 0.f, 0.f);
+      } else {
+        for (int dh = 0; dh < Sh; dh++)
+          for (int dw = 0; dw < Sw; dw++) {
+            const int e = e0 + (LAYOUT == 0 ? dh * Wi + dw : (dh * Wi + dw) * C);
+            store_elem<DT>(rdx, (ok && hi + dh < Hi && wi + dw < Wi) ? (uint32_t)e * ES : dev::kOOB,
+                           (dh | dw) ? 0.f : v);
+          }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < BM * BN / THREADS; i++) {
     const int m = tid / BN + (THREADS / BN) * i;

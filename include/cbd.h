@@ -287,6 +287,12 @@ typedef struct {
                                configuration, which cbd_run_ws runs given
                                auto_workspace_bytes (1: none) */
   int64_t auto_workspace_bytes; /* workspace that enables it (0: none) */
+  int32_t zero_in_epilogue; /* 1: the main kernel writes the unreached dX
+                               positions itself (generic family: one class
+                               at phase (0,0) covering every stride block,
+                               written whole; row-block family), so there
+                               is no zero-fill work */
+  int32_t reserved_;
 } cbd_plan_info_t;
 
 typedef struct {

@@ -440,6 +440,36 @@ def test_generic_static_instance_matches_runtime(name):
             assert np.array_equal(b.result_bits().reshape(ref.shape), exact_expected_bits(p, ref))
 
 
+# One class at phase (0,0) over every stride block (1x1 filters at stride S):
+# the epilogue writes each block whole, zeros included.  (name, N, G, C, K,
+# Hi, Wi, stride, layout, dtype)
+ZBLOCK_CASES = [
+    ("nchw-f32-pairs", 3, 1, 20, 12, 28, 28, (2, 2), NCHW, "f32"),
+    ("nchw-f32-oddw", 2, 1, 16, 8, 14, 27, (2, 2), NCHW, "f32"),
+    ("nchw-bf16-pairs", 2, 1, 24, 40, 15, 30, (2, 2), NCHW, "bf16"),
+    ("nhwc-f32", 2, 1, 20, 12, 28, 28, (2, 2), NHWC, "f32"),
+    ("nhwc-bf16-s32", 2, 2, 16, 24, 13, 11, (3, 2), NHWC, "bf16"),
+    ("nchw-f32-s21", 2, 1, 33, 17, 9, 10, (2, 1), NCHW, "f32"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(ZBLOCK_CASES)))
+def test_whole_block_epilogue(idx):
+    name, n, g, c, k, hi, wi, st, lay, dt = ZBLOCK_CASES[idx]
+    p = Problem(name, n, g, c, k, hi, wi, 1, 1, st[0], st[1], 0, 0, 1, 1, lay, dt, "u", "u", 0, 0)
+    print(f"[zblock] {p}", flush=True)
+    pl = plan_for(p, cbd.KERNEL_GENERIC)
+    info = pl.info()
+    assert info.zero_in_epilogue == 1 and info.grid_zero == 0 and info.launches == 1
+    sh = oracle.shapes(p)
+    dy = small_ints(9100 + idx, sh["dy"]).astype(np.float32)
+    w = small_ints(9200 + idx, sh["w"]).astype(np.float32)
+    run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
+    ref = oracle.bwd_data(p, dy, w)
+    assert np.array_equal(run.result_bits().reshape(ref.shape), exact_expected_bits(p, ref))
+    assert run.guards_intact()
+
+
 def test_non_default_stream():
     p = by_name("c3a")
     dy, w = operands(p)

@@ -154,8 +154,9 @@ def test_workload_plans():
             for s in subs:
                 assert s.tile_begin == tiles
                 tiles += s.tiles
-            # the generic family folds the zero-fill workgroups into its launch
-            fused = info.num_zero_regions > 0 and info.grid_zero == 0
+            # the generic family folds the zero-fill workgroups into its launch,
+            # or writes the unreached positions in its epilogue
+            fused = info.num_zero_regions > 0 and info.grid_zero == 0 and not info.zero_in_epilogue
             zero_wgs = -(-info.zero_elems // (256 * 2)) if fused and p.layout == NCHW else 0
             assert tiles + zero_wgs == info.grid_main
         if p.name in expect:
@@ -169,6 +170,7 @@ def test_workload_plans():
         c3b = plan_of(c3b_p, force)
         assert c3b.info().zero_elems == 32 * 64 * 28 * 28 * 3 // 4
         assert c3b.info().launches == 1 and c3b.info().grid_zero == 0  # zeros in the main launch
+        assert c3b.info().zero_in_epilogue == 1 and c3b.info().grid_main == 392  # written by its epilogue
     # the row-block family (forced only): one workgroup per CU, balanced row blocks
     rows = {q.name: plan_of(q, cbd.KERNEL_NCHW_ROWS).info() for q in PROBLEMS if q.layout == NCHW}
     assert {n: (i.grid_main, i.rows_per_wg) for n, i in rows.items() if n in ("c1", "c2-14-3", "c3a", "c3b")} \
@@ -451,12 +453,20 @@ def test_alignment_requirements():
     assert (r.kernel, r.align_dy, r.align_dx) == (cbd.KERNEL_NCHW_ROWS, 2, 2)
     bf = cbd.plan(2, 1, 12, 12, 9, 9, 3, 3, 1, 1, 1, "nchw", "bf16", force_kernel=cbd.KERNEL_GENERIC).info()
     assert (bf.align_dy, bf.align_w, bf.align_dx) == (2, 2, 2)
-    # NCHW zero-fill writes elements; NHWC rows of 64 f32 channels in 16-byte chunks
-    z_nchw = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC).info()
-    assert z_nchw.num_zero_regions == 3 and z_nchw.align_dx == 4
-    z_nhwc = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nhwc", "f32",
+    # NCHW zero-fill writes elements; NHWC rows of 64 f32 channels in 16-byte
+    # chunks (1x1 stride 2 with padding 1: the reached phase is (1,1))
+    z_nchw = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC).info()
+    assert z_nchw.num_zero_regions == 3 and z_nchw.align_dx == 4 and not z_nchw.zero_in_epilogue
+    z_nhwc = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 1, 1, "nhwc", "f32",
                       force_kernel=cbd.KERNEL_GENERIC).info()
     assert z_nhwc.num_zero_regions == 3 and (z_nhwc.align_dy, z_nhwc.align_dx) == (4, 16)
+    # without padding the one class is phase (0,0): its epilogue writes whole
+    # 2x2 blocks, in (value, 0) pairs for NCHW with an even width
+    for lay, wi, ax in (("nchw", 28, 8), ("nchw", 27, 4), ("nhwc", 28, 4)):
+        zb = cbd.plan(2, 1, 64, 64, 28, wi, 1, 1, 2, 0, 1, lay, "f32", force_kernel=cbd.KERNEL_GENERIC).info()
+        assert (zb.zero_in_epilogue, zb.grid_zero, zb.launches, zb.align_dx) == (1, 0, 1, ax), (lay, wi)
+    zb16 = cbd.plan(2, 1, 64, 64, 28, 28, 1, 1, 2, 0, 1, "nchw", "bf16", force_kernel=cbd.KERNEL_GENERIC).info()
+    assert zb16.align_dx == 4
     c4 = cbd.plan(16, 1, 2048, 2048, 1, 512, 1, 2, (1, 2), 0, 1, "nhwc", "bf16").info()
     assert (c4.align_dy, c4.align_w, c4.align_dx) == (16, 16, 16)
     pl = cbd.plan(2, 1, 16, 16, 14, 14, 3, 3, 1, 1, 1, "nchw", "f32", force_kernel=cbd.KERNEL_GENERIC)
