@@ -292,6 +292,165 @@ def copy_calibration(nbytes, reps):
     torch.cuda.synchronize()
 
 
+# ---------------------------------------------------------------- profiles ---
+# Summaries under profiles/ of rocprofv3 passes over this script, one pass per
+# directory under RAW named <pass>_<problem>:
+#   kt    rocprofv3 --kernel-trace --stats ... -- bench.py PROF --problem P --steps 50 --warmup 5
+#   ktng  the same with --no-graph (calls issued one by one)
+#   fetch rocprofv3 --pmc FETCH_SIZE ... -- bench.py PROF --problem P --steps 10 --warmup 2
+#           --no-graph --copy-calibration-mib 1024      (write: WRITE_SIZE)
+#   mfma  rocprofv3 --pmc <MFMA_COUNTERS> ... --no-graph; stall: <STALL_COUNTERS>
+PROF = "--cpu-seconds 0 --no-secondary"
+MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+                  "SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_WAVES")
+ROCPROF = "cd /tmp && rocprofv3"
+
+
+def pass_command(kind, prob):
+    out = f"--output-format csv -d <out>/{kind}_{prob} -o prof -- python3 bench.py {PROF} --problem {prob}"
+    if kind in ("kt", "ktng"):
+        return f"{ROCPROF} --kernel-trace --stats {out} --steps 50 --warmup 5" + (" --no-graph" if kind == "ktng" else "")
+    pmc = {"fetch": "FETCH_SIZE", "write": "WRITE_SIZE", "mfma": MFMA_COUNTERS, "stall": STALL_COUNTERS}[kind]
+    cal = " --copy-calibration-mib 1024" if kind in ("fetch", "write") else ""
+    return f"{ROCPROF} --pmc {pmc} {out} --steps 10 --warmup 2 --no-graph{cal}"
+
+
+def summarize_profiles(raw):
+    """Write the profiles/ summaries of the rocprofv3 passes found under raw."""
+    import collections
+    import csv
+    import statistics
+
+    import dnn_conv2d_bwd_amd as cbd
+    from cbd_inputs import problem_by_name
+
+    def kernel_of(prob):
+        p = problem_by_name(prob)
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        info = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
+                        (p.dh, p.dw), p.layout, dt).info()
+        return kernel_key(info), describe(p)
+
+    def trace(d, sym):
+        rows = list(csv.DictReader(open(os.path.join(d, "prof_kernel_trace.csv"))))
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows if sym in r["Kernel_Name"]]
+        name = next(r["Kernel_Name"] for r in rows if sym in r["Kernel_Name"])
+        return name, sorted(durs)
+
+    def bench_line(d):
+        f = d.rstrip("/") + ".out"
+        try:
+            return json.loads(open(f).read().strip().splitlines()[-1])
+        except (OSError, ValueError, IndexError):
+            return None
+
+    def counters(d, sym):
+        agg = collections.defaultdict(float)
+        grid = {}
+        for r in csv.DictReader(open(os.path.join(d, "prof_counter_collection.csv"))):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"])
+            agg[key] += float(r["Counter_Value"])
+            grid[int(r["Dispatch_Id"])] = int(r.get("Grid_Size") or 0)
+        mine = collections.defaultdict(list)
+        copies = collections.defaultdict(list)
+        for (disp, k, c), v in agg.items():
+            if sym in k:
+                mine[c].append(v)
+            elif "copyBuffer" in k:
+                copies[c].append((grid[disp], v))
+        # calibration copies: the largest copy dispatches (smaller ones are
+        # the operands' staging copies)
+        cal = {}
+        for c, lst in copies.items():
+            g = max(x for x, _ in lst)
+            cal[c] = [v for x, v in lst if x == g]
+        return mine, cal
+
+    written = []
+    passes = collections.defaultdict(dict)
+    for d in sorted(os.listdir(raw)):
+        if os.path.isdir(os.path.join(raw, d)) and "_" in d:
+            kind, prob = d.split("_", 1)
+            passes[prob][kind] = os.path.join(raw, d)
+    for prob, ks in passes.items():
+        key, desc = kernel_of(prob)
+        sym = KERNEL_SYMBOL[key][:-len("_kernel")]
+        base = os.path.join(ROOT, "profiles", f"{sym}_{prob}")
+        summary_cmd = f"python3 bench.py --summarize-profiles <out>"
+        if "kt" in ks:
+            out = ["# rocprofv3 kernel-trace summary: " + desc, ""]
+            for kind, title in (("kt", "calls replayed from a HIP graph (the benchmark's timing)"),
+                                ("ktng", "calls issued one by one")):
+                if kind not in ks:
+                    continue
+                name, s_ = trace(ks[kind], sym)
+                out += [f"## {prob}, {title}", f"command: {pass_command(kind, prob)}", f"summary: {summary_cmd}", "",
+                        "| kernel | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|",
+                        f"| {name} | {len(s_)} | {statistics.mean(s_):.3f} | {statistics.median(s_):.3f} | "
+                        f"{s_[0]:.3f} | {s_[-1]:.3f} |", ""]
+                b = bench_line(ks[kind])
+                if b:
+                    out += [f"The same run's own HIP-event time per call ({b['config']['timing']}): "
+                            f"{b['roofline']['launch_us_mean']} us.", ""]
+            open(base + "_kernel_trace.md", "w").write("\n".join(out))
+            written.append(base + "_kernel_trace.md")
+        if "fetch" in ks and "write" in ks:
+            f, cf = counters(ks["fetch"], sym)
+            w, cw = counters(ks["write"], sym)
+            cfm, cwm = statistics.mean(cf["FETCH_SIZE"]), statistics.mean(cw["WRITE_SIZE"])
+            kib = 1024.0 * 1024  # the calibration copy moves 1024 MiB each way
+            sf, sw = kib / cfm, kib / cwm
+            fk, wk = statistics.mean(f["FETCH_SIZE"]), statistics.mean(w["WRITE_SIZE"])
+            rd, wr = fk * 1024 * sf, wk * 1024 * sw
+            lines = [f"# HBM traffic of {KERNEL_SYMBOL[key]} per launch: {desc} (rocprofv3 derived counters)",
+                     f"command_fetch: {pass_command('fetch', prob)}", f"command_write: {pass_command('write', prob)}",
+                     f"summary: {summary_cmd}",
+                     f"kernel_source: dnn_conv2d_bwd_amd/csrc/{KERNEL_SRC[key]} + {' + '.join(KERNEL_HEADERS)}",
+                     f"source_sha256: {kernel_digest(key)}",
+                     f"fetch_size_kib_per_dispatch: {fk:.1f} (dispatches {len(f['FETCH_SIZE'])})",
+                     f"write_size_kib_per_dispatch: {wk:.1f} (dispatches {len(w['WRITE_SIZE'])})",
+                     f"copy_calibration: plain device copy of 1024 MiB (__amd_rocclr_copyBuffer, the largest-grid "
+                     f"copy dispatches only: {len(cf['FETCH_SIZE'])} and {len(cw['WRITE_SIZE'])}); FETCH_SIZE "
+                     f"{cfm:.1f} KiB, WRITE_SIZE {cwm:.1f} KiB per dispatch",
+                     f"scale_fetch: {sf:.4f}", f"scale_write: {sw:.4f}",
+                     f"hbm_read_bytes_per_launch: {rd:.0f}", f"hbm_write_bytes_per_launch: {wr:.0f}",
+                     f"hbm_bytes_per_launch: {rd + wr:.0f}", ""]
+            open(base + "_traffic.txt", "w").write("\n".join(lines))
+            written.append(base + "_traffic.txt")
+        for kind, title in (("mfma", "MFMA counters"), ("stall", "wave stall counters")):
+            if kind not in ks:
+                continue
+            c, _ = counters(ks[kind], sym)
+            n = len(next(iter(c.values())))
+            lines = [f"# {title} of {KERNEL_SYMBOL[key]}: {desc} (rocprofv3 --pmc, mean per dispatch)",
+                     f"command: {pass_command(kind, prob)}", f"summary: {summary_cmd}",
+                     f"kernel_source: dnn_conv2d_bwd_amd/csrc/{KERNEL_SRC[key]} + {' + '.join(KERNEL_HEADERS)}",
+                     f"source_sha256: {kernel_digest(key)}", f"dispatches: {n}"]
+            lines += [f"{k}: {statistics.mean(v):.0f}" for k, v in sorted(c.items())]
+            m = {k: statistics.mean(v) for k, v in c.items()}
+            if kind == "mfma":
+                lines += ["", f"executed_bf16_flop: {m['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.4f} G (512 x MOPS)",
+                          f"mfma_busy_cycles_per_simd: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:.0f} (1024 SIMDs)",
+                          f"gui_active_cycles_per_xcd: {m['GRBM_GUI_ACTIVE'] / 8:.0f} (8 XCDs)",
+                          f"mfma_busy_fraction: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / (m['GRBM_GUI_ACTIVE'] / 8):.3f}"]
+            else:
+                wv = m.get("SQ_WAVES", 1.0)
+                q = lambda k: m[k] * 4 / wv  # noqa: E731  (quad-cycle counters -> cycles per wave)
+                lines += ["", f"per wave ({wv:.0f} waves; SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_ANY count "
+                              f"4-cycle units):",
+                          f"  wave_cycles: {q('SQ_WAVE_CYCLES'):.0f}",
+                          f"  wait_any (waitcnt and barrier): {q('SQ_WAIT_ANY'):.0f}",
+                          f"  wait_inst_any (instruction ready, not issued): {q('SQ_WAIT_INST_ANY'):.0f}",
+                          f"  wait_inst_lds: {q('SQ_WAIT_INST_LDS'):.0f}",
+                          f"  active_inst_any: {q('SQ_ACTIVE_INST_ANY'):.0f}",
+                          f"  mfma_busy_cycles per SIMD: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024:.0f}"]
+            open(base + f"_{kind}_counters.txt", "w").write("\n".join(lines + [""]))
+            written.append(base + f"_{kind}_counters.txt")
+    for f in written:
+        print(os.path.relpath(f, ROOT))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,7 +496,13 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload problem: warm and cold (caches "
                          "flushed) µs/call and the roofline fraction; not the bench line")
+    ap.add_argument("--summarize-profiles", metavar="RAW", default=None,
+                    help="write the profiles/ summaries of the rocprofv3 passes under RAW "
+                         "(<pass>_<problem> directories; no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
