@@ -147,9 +147,8 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   // problems 8.05 -> 7.73 us with eight; the stride-2 64-channel problems
   // 17.1 -> 18.0 and 7.5 -> 8.5 us).
   constexpr int DEPTH = (AE + BE <= 8 && (NW == 8 || BM * BN <= 256)) ? 8 : 2;
-  constexpr int STG = BK * (BM + BN);                  // staging floats per wave
   constexpr int RED = (NW / 2) * BM * BN;              // NW/2 partial tiles at a time
-  constexpr int LDSF = NW * STG > RED ? NW * STG : RED;
+  constexpr int LDSF = RED;
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
   __shared__ float lds[LDSF];
 
@@ -205,27 +204,40 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   const int KT = s.taps_h * s.taps_w * kpt;
   const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
 
-  // Gather roles.  A: channel m0 + lane % BM, k rows lane / BM + AR*e.
-  // B: position n0 + lane % BN, k rows lane / BN + BR*e.  Each lane's part
-  // of an address is fixed (A) or fixed per tap (B); the k tile's part is
-  // wave-uniform and goes to the load's scalar offset.
-  constexpr int AR = 64 / BM, BR = 64 / BN;
-  const int ac = m0 + lane % BM;
-  const int ak = lane / BM, bk = lane / BN;
+  // Gather roles, in the operand layout of v_mfma_f32_16x16x4_f32 (so the
+  // gathered values feed the MFMAs directly, with no pass through LDS):
+  // lane l holds A[m = l % 16][k = l / 16] and B[k = l / 16][n = l % 16] of
+  // each 16 x 4 block.  A element (bm, ks): channel m0 + 16*bm + l % 16, k
+  // row 4*ks + l / 16; B element (bn, ks): position n0 + 16*bn + l % 16, the
+  // same k row.  Each lane's part of an address is fixed (A) or fixed per
+  // tap (B); the k tile's part is wave-uniform and goes to the load's scalar
+  // offset.
+  constexpr int KS = BK / 4;  // k steps of 4 per k tile
+  const int r16 = lane & 15, q4 = lane >> 4;
   const int a_ks = Cg * YX;  // W elements between k rows (both layouts)
-  const uint32_t a_lane =
-      ac < Cg ? (uint32_t)(LAYOUT == 0 ? (ak * Cg + ac) * YX : ak * a_ks + ac) * ES : dev::kOOB;
-  const int bp = n0 + lane % BN;
-  const bool bp_ok = bp < npos;
-  const int bpp = bp_ok ? bp : 0;
-  const int pn = bpp / npix_img;
-  const int prr = bpp - pn * npix_img;
-  const int pth = prr / s.pos_w, ptw = prr - (prr / s.pos_w) * s.pos_w;
+  uint32_t a_lane[MB];
+#pragma unroll
+  for (int bm = 0; bm < MB; bm++) {
+    const int c = m0 + 16 * bm + r16;
+    a_lane[bm] = c < Cg ? (uint32_t)(LAYOUT == 0 ? (q4 * Cg + c) * YX : q4 * a_ks + c) * ES : dev::kOOB;
+  }
   const int b_ks = LAYOUT == 0 ? Ho * Wo : 1;  // dY elements between k rows
-  // dY element of (k row bk, dY pixel (pth, ptw) of image pn); a tap adds a
-  // wave-uniform pixel shift (times K for NHWC).
-  const int bpos = LAYOUT == 0 ? ((pn * K + g * Kg + bk) * Ho + pth) * Wo + ptw
-                               : ((pn * Ho + pth) * Wo + ptw) * K + g * Kg + bk;
+  // Per 16-position block: the dY element of (k row q4, dY pixel (pth, ptw)
+  // of image pn); a tap adds a wave-uniform pixel shift (times K for NHWC).
+  int bpos[NB], pth[NB], ptw[NB];
+  bool bp_ok[NB];
+#pragma unroll
+  for (int bn = 0; bn < NB; bn++) {
+    const int bp = n0 + 16 * bn + r16;
+    bp_ok[bn] = bp < npos;
+    const int bpp = bp_ok[bn] ? bp : 0;
+    const int pn = bpp / npix_img;
+    const int prr = bpp - pn * npix_img;
+    pth[bn] = prr / s.pos_w;
+    ptw[bn] = prr - pth[bn] * s.pos_w;
+    bpos[bn] = LAYOUT == 0 ? ((pn * K + g * Kg + q4) * Ho + pth[bn]) * Wo + ptw[bn]
+                           : ((pn * Ho + pth[bn]) * Wo + ptw[bn]) * K + g * Kg + q4;
+  }
 
   // k tile -> (k tile within its tap, tap row, tap column); advanced
   // without division (the walk is wave-uniform).
@@ -255,31 +267,39 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
     // (wave-uniform by construction; readfirstlane lets the compiler see it)
     const uint32_t a_s = __builtin_amdgcn_readfirstlane(
         (uint32_t)(LAYOUT == 0 ? k0 * a_ks + tapoff : (k0 * YX + tapoff) * Cg) * ES);
-    int dh, dw;  // dY pixel shift of this tap
-    bool bok;
-    if constexpr (NS) {
-      const int ho = dev::dy_index(1, pth, s.beta_h, delta_h, w.jh, a.pad_h, a.dil_h, a.str_h);
-      const int wo = dev::dy_index(1, ptw, s.beta_w, delta_w, w.jw, a.pad_w, a.dil_w, a.str_w);
-      dh = ho - pth;
-      dw = wo - ptw;
-      bok = ho >= 0 && ho < Ho && wo >= 0 && wo < Wo;
-    } else {
+    const int krem = Kg - k0;  // k rows of this tile inside K/G
+    int dh = 0, dw = 0;        // dY pixel shift of this tap (residue split)
+    if constexpr (!NS) {
       dh = uni(s.beta_h - delta_h * w.jh);
       dw = uni(s.beta_w - delta_w * w.jw);
-      bok = pth >= -dh && pth < Ho - dh && ptw >= -dw && ptw < Wo - dw;
     }
-    bok = bok && live && bp_ok;
-    const int shift = LAYOUT == 0 ? dh * Wo + dw : (dh * Wo + dw) * K;
-    const uint32_t b_lane = bok ? (uint32_t)(bpos + shift) * ES : dev::kOOB;
-    const uint32_t al = live ? a_lane : dev::kOOB;
-    const int krem = Kg - k0;  // k rows of this tile inside K/G
 #pragma unroll
-    for (int e = 0; e < AE; e++)
-      av[e] = load_elem<DT>(rw, opaque(al), a_s + (uint32_t)(e * AR * a_ks) * ES);
+    for (int bm = 0; bm < MB; bm++) {
+      const uint32_t al = live ? a_lane[bm] : dev::kOOB;
 #pragma unroll
-    for (int e = 0; e < BE; e++) {
-      const uint32_t off = bk + BR * e < krem ? b_lane : dev::kOOB;
-      bv[e] = load_elem<DT>(rdy, opaque(off), __builtin_amdgcn_readfirstlane((uint32_t)((k0 + BR * e) * b_ks) * ES));
+      for (int ks = 0; ks < KS; ks++)
+        av[bm * KS + ks] = load_elem<DT>(rw, opaque(al), a_s + (uint32_t)(4 * ks * a_ks) * ES);
+    }
+#pragma unroll
+    for (int bn = 0; bn < NB; bn++) {
+      bool bok;
+      int shift;
+      if constexpr (NS) {
+        const int ho = dev::dy_index(1, pth[bn], s.beta_h, delta_h, w.jh, a.pad_h, a.dil_h, a.str_h);
+        const int wo = dev::dy_index(1, ptw[bn], s.beta_w, delta_w, w.jw, a.pad_w, a.dil_w, a.str_w);
+        bok = ho >= 0 && ho < Ho && wo >= 0 && wo < Wo;
+        shift = LAYOUT == 0 ? (ho - pth[bn]) * Wo + (wo - ptw[bn]) : ((ho - pth[bn]) * Wo + (wo - ptw[bn])) * K;
+      } else {
+        bok = pth[bn] >= -dh && pth[bn] < Ho - dh && ptw[bn] >= -dw && ptw[bn] < Wo - dw;
+        shift = LAYOUT == 0 ? dh * Wo + dw : (dh * Wo + dw) * K;
+      }
+      const uint32_t b_lane = (bok && live && bp_ok[bn]) ? (uint32_t)(bpos[bn] + shift) * ES : dev::kOOB;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const uint32_t off = q4 + 4 * ks < krem ? b_lane : dev::kOOB;
+        bv[bn * KS + ks] = load_elem<DT>(rdy, opaque(off),
+                                         __builtin_amdgcn_readfirstlane((uint32_t)((k0 + 4 * ks) * b_ks) * ES));
+      }
     }
   };
 
@@ -289,30 +309,15 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
 #pragma unroll
     for (int j = 0; j < NB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float* As = lds + wave * STG;  // [BK][BM]
-  float* Bs = As + BK * BM;      // [BK][BN]
   auto compute = [&](const float (&av)[AE], const float (&bv)[BE]) {
 #pragma unroll
-    for (int e = 0; e < AE; e++) As[(ak + (64 / BM) * e) * BM + lane % BM] = av[e];
-#pragma unroll
-    for (int e = 0; e < BE; e++) Bs[(bk + (64 / BN) * e) * BN + lane % BN] = bv[e];
-    // Only this wave uses its staging area and a wave's LDS operations run
-    // in order: waiting for its own writes is enough, no barrier.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-#pragma unroll
-    for (int ks = 0; ks < BK / 4; ks++) {
-      const int kr = 4 * ks + (lane >> 4);
-      float x[MB], y[NB];
-#pragma unroll
-      for (int bm = 0; bm < MB; bm++) x[bm] = As[kr * BM + bm * 16 + (lane & 15)];
-#pragma unroll
-      for (int bn = 0; bn < NB; bn++) y[bn] = Bs[kr * BN + bn * 16 + (lane & 15)];
+    for (int ks = 0; ks < KS; ks++)
 #pragma unroll
       for (int bm = 0; bm < MB; bm++)
 #pragma unroll
         for (int bn = 0; bn < NB; bn++)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[bm], y[bn], acc[bm][bn], 0, 0, 0);
-    }
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[bm * KS + ks], bv[bn * KS + ks], acc[bm][bn],
+                                                             0, 0, 0);
   };
 
   // Wave-strided K loop with up to DEPTH k tiles of gathers in flight (a
