@@ -201,7 +201,15 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   const auto rdx = dev::rsrc(dx_p, Geo::dx_bytes(a));
 
   const int kpt = (Kg + BK - 1) / BK;
-  const int KT = s.taps_h * s.taps_w * kpt;
+  // Order of the class's K = (tap, k) pairs.  Classes of 1, 2 or 4 taps run
+  // tap-fastest: element d = q4 + 4*ks of a k tile is tap d % T of k row
+  // k0 + d / T, so a lane keeps one tap for the whole loop and the four
+  // lanes of a channel read taps of one W block (KCYX: all taps of a
+  // channel are contiguous) instead of four k rows of it.  Other classes
+  // (and the zero-insertion form) run k-fastest within one tap per k tile.
+  const int T = s.taps_h * s.taps_w;
+  const bool tapfast = !NS && (T == 1 || T == 2 || T == 4);
+  const int KT = tapfast ? (Kg * T + BK - 1) / BK : T * kpt;
   const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
 
   // Gather roles, in the operand layout of v_mfma_f32_16x16x4_f32 (so the
@@ -303,6 +311,50 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
     }
   };
 
+  // Tap-fast gathers: the lane's tap tl and first k row kd0; per k step the
+  // k row advances by 4 / T, per k tile by BK / T.
+  const int tsh = T == 4 ? 2 : T == 2 ? 1 : 0;
+  const int tl = q4 & (T - 1), kd0 = q4 >> tsh;
+  const int kstep = 4 >> tsh, kpt_tf = BK >> tsh;
+  uint32_t a_tf[MB], b_tf[NB];
+  if (tapfast) {
+    const int jh = tl / s.taps_w, jw = tl - (tl / s.taps_w) * s.taps_w;
+    const int tapoff = (s.cls_h + tstep_h * jh) * Xf + s.cls_w + tstep_w * jw;
+#pragma unroll
+    for (int bm = 0; bm < MB; bm++) {
+      const int c = m0 + 16 * bm + r16;
+      a_tf[bm] = c < Cg ? (uint32_t)(LAYOUT == 0 ? (kd0 * Cg + c) * YX + tapoff : (kd0 * YX + tapoff) * Cg + c) * ES
+                        : dev::kOOB;
+    }
+    const int dh = s.beta_h - delta_h * jh, dw = s.beta_w - delta_w * jw;
+    const int shift = LAYOUT == 0 ? dh * Wo + dw : (dh * Wo + dw) * K;
+#pragma unroll
+    for (int bn = 0; bn < NB; bn++) {
+      const bool bok = bp_ok[bn] && pth[bn] >= -dh && pth[bn] < Ho - dh && ptw[bn] >= -dw && ptw[bn] < Wo - dw;
+      b_tf[bn] = bok ? (uint32_t)(bpos[bn] + (kd0 - q4) * b_ks + shift) * ES : dev::kOOB;
+    }
+  }
+  // Tap-fast k tile kt: W rows past K/G read 0 through the group's
+  // resource; dY rows past K/G are masked per lane.
+  auto gather_tf = [&](int kt, float (&av)[AE], float (&bv)[BE]) {
+    const int k0 = kt * kpt_tf;
+    const uint32_t a_s = __builtin_amdgcn_readfirstlane((uint32_t)(k0 * a_ks) * ES);
+    const int krem = Kg - k0;
+#pragma unroll
+    for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++)
+        av[bm * KS + ks] = load_elem<DT>(rw, opaque(a_tf[bm]), a_s + (uint32_t)(ks * kstep * a_ks) * ES);
+#pragma unroll
+    for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const uint32_t off = kd0 + ks * kstep < krem ? b_tf[bn] : dev::kOOB;
+        bv[bn * KS + ks] = load_elem<DT>(
+            rdy, opaque(off), __builtin_amdgcn_readfirstlane((uint32_t)((k0 + ks * kstep) * b_ks) * ES));
+      }
+  };
+
   f32x4 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; i++)
@@ -323,29 +375,33 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   // Wave-strided K loop with up to DEPTH k tiles of gathers in flight (a
   // ring of registers; a slot is refilled right after its tile is used).
   // Tiles past this workgroup's k range are skipped, not gathered.
-  float av[DEPTH][AE], bv[DEPTH][BE];
-  Walk wn = walk_at(kbeg + wave);  // next tile to gather
-  int kn = kbeg + wave;
-#pragma unroll
-  for (int d = 0; d < DEPTH; d++) {
-    if (kn < kend) {
-      gather(wn, true, av[d], bv[d]);
-      advance(wn, NW);
-    }
-    kn += NW;
-  }
-  for (int kt = kbeg + wave; kt < kend; kt += DEPTH * NW) {
+  auto kloop = [&](auto&& fetch) {
+    float av[DEPTH][AE], bv[DEPTH][BE];
+    int kn = kbeg + wave;  // next tile to gather
 #pragma unroll
     for (int d = 0; d < DEPTH; d++) {
-      if (kt + d * NW < kend) {
-        compute(av[d], bv[d]);
-        if (kn < kend) {
-          gather(wn, true, av[d], bv[d]);
-          advance(wn, NW);
+      if (kn < kend) fetch(kn, av[d], bv[d]);
+      kn += NW;
+    }
+    for (int kt = kbeg + wave; kt < kend; kt += DEPTH * NW) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; d++) {
+        if (kt + d * NW < kend) {
+          compute(av[d], bv[d]);
+          if (kn < kend) fetch(kn, av[d], bv[d]);
+          kn += NW;
         }
-        kn += NW;
       }
     }
+  };
+  if (tapfast) {
+    kloop([&](int kt, float (&av)[AE], float (&bv)[BE]) { gather_tf(kt, av, bv); });
+  } else {
+    Walk wn = walk_at(kbeg + wave);  // walks in step with the tiles fetched
+    kloop([&](int, float (&av)[AE], float (&bv)[BE]) {
+      gather(wn, true, av, bv);
+      advance(wn, NW);
+    });
   }
 
   // Cross-wave sum in a fixed order through LDS (reusing the staging area):
