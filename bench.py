@@ -90,7 +90,7 @@ def kernel_key(info):
 
 
 # Headers every kernel source includes: a change in them changes the kernels.
-KERNEL_HEADERS = ("cbd_device.h", "cbd_kernarg.h", "cbd_internal.h", "generic_shapes.h")
+KERNEL_HEADERS = ("cbd_device.h", "cbd_kernarg.h", "cbd_internal.h", "cbd_geo.h", "generic_shapes.h")
 
 
 def kernel_digest(key):

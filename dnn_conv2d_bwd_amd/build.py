@@ -43,13 +43,14 @@ CFLAGS = [
 ]
 
 
-# Per-source extra flags.  The large-tile and generic kernels take their
+# Per-source extra flags.  The large-tile, generic and grouped-MFMA kernels take their
 # tensors (and sizes) as leading scalar parameters, preloaded into SGPRs at
 # wave launch (code objects keep a fallback that loads them for firmware
 # without preloading).
 EXTRA = {
     "kern_igemm_nhwc_bf16.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
     "kern_igemm_generic.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+    "kern_grouped_mfma.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
 }
 
 

@@ -283,6 +283,28 @@ bool generic_shape_matches(const cbd::ShapeKey& k, const cbd::GemmArgs& a, const
   return true;
 }
 
+// Every field of a compiled grouped-kernel shape equals the plan's (the tile
+// fields hold rows and positions per workgroup).
+bool grouped_shape_matches(const cbd::ShapeKey& k, const cbd::GemmArgs& a, const cbd_problem& p, int64_t threads) {
+  if (k.layout != p.layout || k.dtype != p.dtype || k.bm != a.grp_rows || k.bn != a.grp_cols ||
+      k.nw * 64 != threads)
+    return false;
+  if (k.N != a.N || k.G != a.G || k.C != a.C || k.K != a.K || k.Cg != a.Cg || k.Kg != a.Kg || k.Hi != a.Hi ||
+      k.Wi != a.Wi || k.Ho != a.Ho || k.Wo != a.Wo || k.Y != a.Y || k.X != a.X || k.Sh != a.Sh || k.Sw != a.Sw)
+    return false;
+  if (k.tstep_h != a.tstep_h || k.tstep_w != a.tstep_w || k.delta_h != a.delta_h || k.delta_w != a.delta_w ||
+      k.total_tiles != a.total_tiles || k.num_sub != a.num_sub || a.num_sub > cbd::kShapeMaxSub)
+    return false;
+  for (int q = 0; q < a.num_sub; q++) {
+    const cbd::SubDesc &x = k.sub[q], &y = a.sub[q];
+    if (x.phase_h != y.phase_h || x.phase_w != y.phase_w || x.beta_h != y.beta_h || x.beta_w != y.beta_w ||
+        x.taps_h != y.taps_h || x.taps_w != y.taps_w || x.cls_h != y.cls_h || x.cls_w != y.cls_w ||
+        x.pos_h != y.pos_h || x.pos_w != y.pos_w || x.tile_begin != y.tile_begin)
+      return false;
+  }
+  return true;
+}
+
 // Shortest K loop of any class, in k tiles of the family (split-K gives
 // each split at least one).
 int64_t min_class_ktiles(const std::vector<cbd_subgemm_t>& subs, int32_t kernel, int64_t Kg, int64_t bk) {
@@ -713,7 +735,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     for (size_t i = 0; ok2 && i < subs.size(); i++)
       ok2 = subs[i].phase_w == (int32_t)i && subs[i].class_w == (int32_t)i && subs[i].beta_w == 0 &&
             subs[i].phase_h == 0 && subs[i].beta_h == 0 && subs[i].pos_h == 1 && subs[i].pos_w == Wo;
-    if (static_mode == 1 && kernel != CBD_KERNEL_GENERIC && !ok1) {
+    if (static_mode == 1 && kernel != CBD_KERNEL_GENERIC && kernel != CBD_KERNEL_GROUPED && !ok1) {
       delete pl;
       return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this problem "
                                        "(built: NHWC bf16, K/G = 2048, one tap per class, residue split, "
@@ -842,9 +864,20 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
       }
     }
   }
-  if (static_mode == 1 && kernel == CBD_KERNEL_GENERIC && static_shape == 0) {
+  // Grouped 4x4x4-MFMA kernel: likewise.
+  if (kernel == CBD_KERNEL_GROUPED && grp_mfma && static_mode >= 0 && !per_class) {
+    for (int i = 0; i < cbd::kGroupedShapes; i++) {
+      if (grouped_shape_matches(cbd::kGroupedShapeKeys[i], a, p, threads)) {
+        static_shape = 2;
+        a.static_shape = 2;
+        a.static_id = i;
+        break;
+      }
+    }
+  }
+  if (static_mode == 1 && (kernel == CBD_KERNEL_GENERIC || kernel == CBD_KERNEL_GROUPED) && static_shape == 0) {
     delete pl;
-    return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance of the generic family for this plan "
+    return fail(CBD_ERR_UNSUPPORTED, "no shape-specialised instance for this plan "
                                      "(built for the listed workload shapes only)");
   }
 

@@ -35,7 +35,9 @@
 // row of compute to drain before the wait at the next barrier (loads and
 // stores share one counter).
 #include "cbd_device.h"
+#include "cbd_geo.h"
 #include "cbd_internal.h"
+#include "generic_shapes.h"
 
 namespace cbd {
 namespace {
@@ -50,9 +52,10 @@ __device__ __forceinline__ s16x4 as_s16x4(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(s16x4, v);
 }
 
-template <int G, int NT>
-__device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, char* ring, int n,
-                                          int th0, int th1, int tb, int seg) {
+template <int G, int NT, class Geo>
+__device__ __forceinline__ void mfma_rows(const GemmArgs& a, const void* dy_p, const void* w_p, void* dx_p,
+                                          const SubDesc& s, char* ring, int n, int th0, int th1, int tb,
+                                          int seg) {
   constexpr int CG = 4, ES = 2;
   constexpr int PIXB = G * CG * ES;  // bytes per NHWC pixel: 256 or 512
   constexpr int PSHIFT = G == 32 ? 8 : 9;
@@ -66,7 +69,9 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   const int g = set * 16 + (lane >> 2);
   const int nn = lane & 3;
 
-  const int span = a.delta_w * (s.taps_w - 1);
+  const int Hi = Geo::Hi(a), Wi = Geo::Wi(a), Ho = Geo::Ho(a), Wo = Geo::Wo(a);
+  const int Sh = Geo::Sh(a), Sw = Geo::Sw(a), Xf = Geo::X(a), delta_w = Geo::delta_w(a);
+  const int span = delta_w * (s.taps_w - 1);
   const int col0 = s.beta_w - span + tb;  // dY column of staged column 0
   const int rowb = (seg + span) * PIXB;
   // Slots (whole KiB) also cover the 3 columns past the row that a partial
@@ -75,10 +80,10 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   const int slotb = ni << 10;
   const int nslot = s.taps_h + 1;
 
-  const i32x4 dyd = {(int)(uint32_t)(uintptr_t)a.dy, (int)(((uintptr_t)a.dy >> 32) & 0xffff),
-                     (int)a.dy_bytes, 0x00020000};
-  const auto rw = dev::rsrc(a.w, a.w_bytes);
-  const auto rdx = dev::rsrc(a.dx, a.dx_bytes);
+  const i32x4 dyd = {(int)(uint32_t)(uintptr_t)dy_p, (int)(((uintptr_t)dy_p >> 32) & 0xffff),
+                     (int)Geo::dy_bytes(a), 0x00020000};
+  const auto rw = dev::rsrc(w_p, Geo::w_bytes(a));
+  const auto rdx = dev::rsrc(dx_p, Geo::dx_bytes(a));
   const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring;
   const int nquads = (seg + 3) >> 2;
   char* const out = ring + nslot * slotb;  // output row buffer: 4*nquads pixels
@@ -87,14 +92,14 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   // Write the results of dX row `hrow` (class row) from the output buffer:
   // chunk j = pixel j / CPP, chunk j % CPP (stored at the swizzled place).
   auto flush_row = [&](int hrow) {
-    const uint32_t xr = (uint32_t)((n * a.Hi + s.phase_h + a.Sh * hrow) * a.Wi) * (uint32_t)PIXB;
+    const uint32_t xr = (uint32_t)((n * Hi + s.phase_h + Sh * hrow) * Wi) * (uint32_t)PIXB;
     const int nchunk = seg * CPP;
     for (int j = tid; j < nchunk; j += kGroupedThreads) {
       const int px = j / CPP, c = j - px * CPP;
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 v = *(const u32x4*)(out + px * PIXB + ((c ^ ((px & 3) << 2)) << 4));
       __builtin_amdgcn_raw_buffer_store_b128(
-          v, rdx, xr + ((uint32_t)(s.phase_w + a.Sw * (tb + px)) << PSHIFT) + (uint32_t)(c << 4), 0, 0);
+          v, rdx, xr + ((uint32_t)(s.phase_w + Sw * (tb + px)) << PSHIFT) + (uint32_t)(c << 4), 0, 0);
     }
   };
 
@@ -103,14 +108,14 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   // past the row.  ni KiB-instructions (64 lanes x 16 bytes), dealt to the
   // waves round-robin.
   auto copy_row = [&](int ho, int sl) {
-    const bool hok = ho >= 0 && ho < a.Ho;
-    const int rpix = (n * a.Ho + ho) * a.Wo;
+    const bool hok = ho >= 0 && ho < Ho;
+    const int rpix = (n * Ho + ho) * Wo;
     for (int i = wave; i < ni; i += 4) {
       const int b = (i << 10) + (lane << 4);
       const int col = b >> PSHIFT;
       const int wo = col0 + col;
       const int gc = ((b & (PIXB - 1)) >> 4) ^ ((col & 3) << 2);
-      const bool ok = hok && b < rowb && wo >= 0 && wo < a.Wo;
+      const bool ok = hok && b < rowb && wo >= 0 && wo < Wo;
       const uint32_t off = ok ? (uint32_t)(rpix + wo) * (uint32_t)PIXB + (uint32_t)(gc << 4) : dev::kOOB;
       const uint32_t m0v = __builtin_amdgcn_readfirstlane(ring_base + (uint32_t)(sl * slotb + (i << 10)));
 #pragma clang diagnostic push
@@ -128,20 +133,20 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   for (int jh = s.taps_h - 1; jh >= 0; jh--) copy_row(th0 + s.beta_h - jh, back(jh));
 
   // A operands: lane 4b+m holds W[g*4 + k][ty][tx][m], k = 0..3, per tap.
-  const int YX = a.Y * a.X;
+  const int YX = Geo::Y(a) * Xf;
   s16x4 wa[NT];
   int jhs[NT], cshift[NT];  // tap row; column shift span - delta_w*jw
 #pragma unroll
   for (int tp = 0; tp < NT; tp++) {
     const int jh = tp / s.taps_w;
     const int jw = tp - jh * s.taps_w;
-    const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+    const int ty = s.cls_h + Geo::tstep_h(a) * jh, tx = s.cls_w + Geo::tstep_w(a) * jw;
     jhs[tp] = jh;
-    cshift[tp] = span - a.delta_w * jw;
+    cshift[tp] = span - delta_w * jw;
     uint32_t e[4];
 #pragma unroll
     for (int k = 0; k < 4; k++)
-      e[k] = __builtin_amdgcn_raw_buffer_load_b16(rw, (uint32_t)(((g * CG + k) * YX + ty * a.X + tx) * CG + nn) * ES, 0, 0);
+      e[k] = __builtin_amdgcn_raw_buffer_load_b16(rw, (uint32_t)(((g * CG + k) * YX + ty * Xf + tx) * CG + nn) * ES, 0, 0);
     wa[tp] = as_s16x4(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
   }
 
@@ -202,14 +207,15 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const SubDesc& s, c
   flush_row(th1 - 1);
 }
 
-template <int G>
-__global__ __launch_bounds__(kGroupedThreads) void grouped_mfma_kernel(const GemmArgs a) {
+template <int G, class Geo>
+__global__ __launch_bounds__(kGroupedThreads) void grouped_mfma_kernel(const void* dy_p, const void* w_p,
+                                                                      void* dx_p, const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
-  dev::prefetch_args(a);
-  const int t = dev::chunked_block(blockIdx.x, a.total_tiles);
-  const SubDesc s = a.sub[dev::find_class(a, t)];
+  if constexpr (!Geo::kStatic) dev::prefetch_args(a);
+  const int t = dev::chunked_block(blockIdx.x, Geo::total_tiles(a));
+  const SubDesc s = Geo::sub(a, t);
   // (image, row block, column block), column blocks innermost
-  const int R = a.grp_rows, CB = a.grp_cols;
+  const int R = Geo::grp_rows(a), CB = Geo::grp_cols(a);
   const int rblocks = (s.pos_h + R - 1) / R;
   const int cblocks = (s.pos_w + CB - 1) / CB;
   const int local = t - s.tile_begin;
@@ -222,29 +228,45 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_mfma_kernel(const Gem
   const int seg = tb + CB < s.pos_w ? CB : s.pos_w - tb;
   static_assert(kGroupedMaxTaps == 9, "the switch below covers 1..9 taps");
   switch (s.taps_h * s.taps_w) {
-    case 1: mfma_rows<G, 1>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 2: mfma_rows<G, 2>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 3: mfma_rows<G, 3>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 4: mfma_rows<G, 4>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 5: mfma_rows<G, 5>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 6: mfma_rows<G, 6>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 7: mfma_rows<G, 7>(a, s, ring, n, th0, th1, tb, seg); break;
-    case 8: mfma_rows<G, 8>(a, s, ring, n, th0, th1, tb, seg); break;
-    default: mfma_rows<G, 9>(a, s, ring, n, th0, th1, tb, seg); break;
+    case 1: mfma_rows<G, 1, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 2: mfma_rows<G, 2, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 3: mfma_rows<G, 3, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 4: mfma_rows<G, 4, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 5: mfma_rows<G, 5, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 6: mfma_rows<G, 6, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 7: mfma_rows<G, 7, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    case 8: mfma_rows<G, 8, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
+    default: mfma_rows<G, 9, Geo>(a, dy_p, w_p, dx_p, s, ring, n, th0, th1, tb, seg); break;
   }
 }
 
-template <int G>
+template <int G, class Geo = DynGeo>
 int launch_g(const GemmArgs& a, int64_t grid, void* stream) {
-  void* args[] = {const_cast<GemmArgs*>(&a)};
-  return (int)hipLaunchKernel((const void*)&grouped_mfma_kernel<G>, dim3((unsigned)grid),
+  const void* dy = a.dy;
+  const void* w = a.w;
+  void* dx = a.dx;
+  void* args[] = {&dy, &w, &dx, const_cast<GemmArgs*>(&a)};
+  return (int)hipLaunchKernel((const void*)&grouped_mfma_kernel<G, Geo>, dim3((unsigned)grid),
                               dim3(kGroupedThreads), args, (size_t)a.grp_lds, (hipStream_t)stream);
+}
+
+// A shape-specialised instance (StatGeo<T>, the group count from T).
+int launch_static(const GemmArgs& a, int64_t grid, void* stream) {
+  switch (a.static_id) {
+#define CBD_CASE(i, T, name) \
+  case i:                    \
+    return launch_g<T::k.G, StatGeo<T>>(a, grid, stream);
+    CBD_GROUPED_SHAPE_LIST(CBD_CASE)
+#undef CBD_CASE
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int launch_grouped_mfma(const GemmArgs& a, int64_t grid, void* stream) {
   if (a.Cg != 4) return (int)hipErrorInvalidValue;
+  if (a.static_shape == 2) return launch_static(a, grid, stream);
   switch (a.G) {
     case 32: return launch_g<32>(a, grid, stream);
     case 64: return launch_g<64>(a, grid, stream);

@@ -37,6 +37,7 @@
 // order and writes dX.
 #include "cbd_device.h"
 #include "cbd_internal.h"
+#include "cbd_geo.h"
 #include "generic_shapes.h"
 
 namespace cbd {
@@ -82,53 +83,6 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)dev::bf16_rne(v), r, byte_off, 0, 0);
   }
 }
-
-// Geometry of a launch: read from the kernel arguments (DynGeo, the
-// descriptor-driven instances) or fixed at compile time (StatGeo<T>, the
-// shape-specialised instances: T::k is one plan's whole geometry, so every
-// index computation folds to constants and no argument is read before the
-// first gather but the three tensor pointers, which arrive preloaded).
-struct DynGeo {
-  static constexpr bool kStatic = false;
-#define CBD_DYN(f) \
-  __device__ static int f(const GemmArgs& a) { return a.f; }
-  CBD_DYN(N) CBD_DYN(C) CBD_DYN(K) CBD_DYN(Cg) CBD_DYN(Kg) CBD_DYN(Hi) CBD_DYN(Wi) CBD_DYN(Ho)
-  CBD_DYN(Wo) CBD_DYN(Y) CBD_DYN(X) CBD_DYN(Sh) CBD_DYN(Sw) CBD_DYN(tstep_h) CBD_DYN(tstep_w)
-  CBD_DYN(delta_h) CBD_DYN(delta_w) CBD_DYN(tiles_m) CBD_DYN(total_tiles) CBD_DYN(xcd_remap)
-  CBD_DYN(ksplit) CBD_DYN(zblock)
-#undef CBD_DYN
-  __device__ static uint32_t dy_bytes(const GemmArgs& a) { return a.dy_bytes; }
-  __device__ static uint32_t dx_bytes(const GemmArgs& a) { return a.dx_bytes; }
-  __device__ static SubDesc sub(const GemmArgs& a, int t) { return a.sub[dev::find_class(a, t)]; }
-};
-
-template <class T>
-struct StatGeo {
-  static constexpr bool kStatic = true;
-#define CBD_STAT(f) \
-  __device__ static constexpr int f(const GemmArgs&) { return T::k.f; }
-  CBD_STAT(N) CBD_STAT(C) CBD_STAT(K) CBD_STAT(Cg) CBD_STAT(Kg) CBD_STAT(Hi) CBD_STAT(Wi) CBD_STAT(Ho)
-  CBD_STAT(Wo) CBD_STAT(Y) CBD_STAT(X) CBD_STAT(Sh) CBD_STAT(Sw) CBD_STAT(tstep_h) CBD_STAT(tstep_w)
-  CBD_STAT(delta_h) CBD_STAT(delta_w) CBD_STAT(tiles_m) CBD_STAT(total_tiles) CBD_STAT(xcd_remap)
-  CBD_STAT(zblock)
-#undef CBD_STAT
-  __device__ static constexpr int ksplit(const GemmArgs&) { return 0; }
-  static constexpr uint32_t kEs = T::k.dtype == CBD_F32 ? 4 : 2;
-  __device__ static constexpr uint32_t dy_bytes(const GemmArgs&) {
-    return (uint32_t)(T::k.N * T::k.K * T::k.Ho * T::k.Wo) * kEs;
-  }
-  __device__ static constexpr uint32_t dx_bytes(const GemmArgs&) {
-    return (uint32_t)(T::k.N * T::k.C * T::k.Hi * T::k.Wi) * kEs;
-  }
-  // The class of logical tile t: classes own ascending tile ranges.
-  __device__ static SubDesc sub(const GemmArgs&, int t) {
-    SubDesc r = T::k.sub[0];
-#pragma unroll
-    for (int q = 1; q < T::k.num_sub; q++)
-      if (t >= T::k.sub[q].tile_begin) r = T::k.sub[q];
-    return r;
-  }
-};
 
 // NS: the zero-insertion form (no residue split: each tap's dY index needs a
 // divisibility test); otherwise a tap's dY index is the position plus a

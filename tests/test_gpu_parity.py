@@ -440,6 +440,28 @@ def test_generic_static_instance_matches_runtime(name):
             assert np.array_equal(b.result_bits().reshape(ref.shape), exact_expected_bits(p, ref))
 
 
+@pytest.mark.parametrize("name", ["c5-s2", "c5-s1"])
+def test_grouped_static_instance_matches_runtime(name):
+    """The grouped 4x4x4-MFMA kernel's shape-specialised instance of each
+    grouped workload problem gives the same bits as its descriptor-driven
+    kernel, on random and integer operands; integer operands bit-exact
+    against the oracle."""
+    p = by_name(name)
+    print(f"[static-grouped] {name}", flush=True)
+    pa, pb = plan_for(p, static_shape=-1), plan_for(p)
+    assert pa.info().static_shape == 0 and pb.info().static_shape == 2
+    for kind in ("dist", "int"):
+        dy, w = operands(p, kind)
+        dy_d, w_d = to_device(dy, p), to_device(w, p)
+        a = DeviceRun(p, pa, dy_d, w_d)()
+        b = DeviceRun(p, pb, dy_d, w_d)()
+        assert np.array_equal(a.result_bits(), b.result_bits()), kind
+        assert a.guards_intact() and b.guards_intact()
+        if kind == "int":
+            ref = oracle.bwd_data(p, dy, w)
+            assert np.array_equal(b.result_bits().reshape(ref.shape), exact_expected_bits(p, ref))
+
+
 # One class at phase (0,0) over every stride block (1x1 filters at stride S):
 # the epilogue writes each block whole, zeros included.  (name, N, G, C, K,
 # Hi, Wi, stride, layout, dtype)

@@ -373,6 +373,33 @@ def test_generic_static_shapes():
         cbd.plan(31, 1, 64, 64, 28, 28, 3, 3, 2, 1, 1, "nchw", "f32", static_shape=1)
 
 
+GROUPED_STATIC = ("c5-s2", "c5-s1")
+
+
+def test_grouped_static_shapes():
+    """The grouped workload problems find their shape-specialised instance of
+    the 4x4x4-MFMA kernel with the descriptor-driven plan's launch; forced
+    row kernels, per-class plans, other batches and static_shape=-1 plans do
+    not, and requiring one where none exists is refused."""
+    by = {q.name: q for q in PROBLEMS}
+    for name in GROUPED_STATIC:
+        p = by[name]
+        a = plan_of(p).info()
+        assert (a.kernel, a.variant, a.static_shape) == (cbd.KERNEL_GROUPED, 3, 2), name
+        dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
+        args = (p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw), (p.dh, p.dw), p.layout, dt)
+        d = cbd.plan(*args, static_shape=-1).info()
+        assert (d.static_shape, d.variant) == (0, 3)
+        assert (d.grid_main, d.grid_zero, d.launches, d.rows_per_wg, d.cols_per_wg, d.threads_main) == \
+            (a.grid_main, a.grid_zero, a.launches, a.rows_per_wg, a.cols_per_wg, a.threads_main)
+        assert cbd.plan(*args, static_shape=1).info().static_shape == 2
+        assert cbd.plan(*args, per_class=True).info().static_shape == 0
+    c5 = by["c5-s2"]
+    assert plan_of(c5.with_(n=63)).info().static_shape == 0
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(63, 32, 128, 128, 56, 56, 3, 3, 2, 1, 1, "nhwc", "bf16", static_shape=1)
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"),
                     reason="passes made-up device addresses to a real launch: only on a machine "
                            "with no GPU driver at all, where the launch itself must fail")
