@@ -15,7 +15,10 @@ Prints ONE JSON line:
                work excluded) over the K timed steps, wall clock between two
                device synchronisations; the K calls are captured once in a HIP
                graph and replayed (cbd_run launches kernels only), or with
-               --no-graph issued one by one;
+               --no-graph issued one by one.  Before them: the W warmup calls,
+               then untimed calls for about --settle-ms of GPU time (the clock
+               of the part rises over the first tens of milliseconds of
+               sustained load; `settle` in the line gives the count);
   roofline     dominant kernel: algorithmic flops (or bytes) per launch divided
                by its mean launch duration from HIP events recorded on the
                launch stream (around the replay / K, or around each call),
@@ -23,11 +26,10 @@ Prints ONE JSON line:
                `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE +
                WRITE_SIZE (profiles/, scaled by a plain copy of known size),
                null when the kernel source changed after the counters were taken;
-  cpu_baseline the CPU oracle on the host cores over a bounded random sample of
-               the same problem's outputs, scaled to TFLOP/s, with the parity
-               of the GPU's dX at those elements against the oracle (relative
-               L2, max error, bf16 ulps, exact zeros; `pass` applies the fp32 or
-               bf16 tolerance);
+  cpu_baseline the CPU oracle's loop nest on the host cores over the whole
+               problem (one call, nothing scaled), with the parity of the
+               GPU's whole dX against it (relative L2, max error, bf16 ulps,
+               exact zeros; `pass` applies the fp32 or bf16 tolerance);
   machine      GPU name and architecture, HIP version, maximum shader clock,
                host CPU model.
 
@@ -40,6 +42,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -451,11 +454,43 @@ def summarize_profiles(raw):
         print(os.path.relpath(f, ROOT))
 
 
+def settle(args, torch, graph, call, stream):
+    """Untimed calls for about args.settle_ms of GPU time, issued back to back
+    (whole replays of the captured graph, or single calls), ending with a
+    synchronisation; returns the number of calls.  The part raises its clock
+    over the first few tens of milliseconds of sustained load after an idle
+    period (MI355X, headline problem: 60 us per call over the first 200 calls,
+    52 us from about 30 ms on), so timed steps taken right after a short
+    warmup measure the ramp rather than the sustained rate."""
+    if args.settle_ms <= 0:
+        return 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+        per, unit = args.steps, "replay"
+    else:
+        call()
+        per, unit = 1, "call"
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), 1e-3)
+    n = max(1, min(100000, int(math.ceil(args.settle_ms / ms))))
+    for _ in range(n):
+        graph.replay() if graph is not None else call()
+    torch.cuda.synchronize()
+    return (n + 1) * per
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="after the warmup steps, untimed calls for about this much GPU time so "
+                         "that the clock reaches its sustained level before the timed steps "
+                         "(0 disables; reported in the JSON line)")
     ap.add_argument("--problem", default="c4")
     ap.add_argument("--cpu-seconds", type=float, default=1.0,
                     help="0 skips the CPU baseline; any other value runs the oracle once on the "
@@ -580,6 +615,8 @@ def main():
             graph = None
             timing = f"stream (graph capture failed: {type(e).__name__})"
     torch.cuda.synchronize()
+    settle_calls = settle(args, torch, graph, lambda: cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws),
+                          stream)
     if graph is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -624,6 +661,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"calls": settle_calls, "target_ms": args.settle_ms},
         "ms_per_step": round(step_s * 1e3, 6),
         "us_per_call": round(step_s * 1e6, 3),
         "higher_is_better": True,

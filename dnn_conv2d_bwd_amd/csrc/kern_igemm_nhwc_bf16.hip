@@ -132,6 +132,11 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
   __shared__ uint32_t gtab[MAX_TAPS * BN];  // dY byte offset of (tap, position row), channel g*Kg
   __shared__ uint32_t otab[BN];             // dX byte offset of position row, channel g*Cg + m0
   __shared__ uint32_t atab[MAX_TAPS];       // W byte offset of (tap, k row 0), channel g*Cg
+  // FIX: bf16 staging of one column group of the C tile (64 position rows x
+  // 512 B), filled while the next group's MFMAs run; with the four stages
+  // this takes the whole 160 KiB of LDS, so FIX keeps no dX table (it
+  // computes dX offsets directly).
+  __shared__ __attribute__((aligned(16))) char stg[FIX ? 64 * 512 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;  // wm: 128-channel half, wn: 128-position half
@@ -205,11 +210,7 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
   // dY offsets of every tap (not needed with one tap), the dX offsets, and
   // the W offset of every tap.
   auto build_tables = [&]() {
-    if constexpr (FIX) {
-      const int p = n0 + tid;
-      otab[tid] = p < npos ? (uint32_t)(2 * p + fix_r) * (FIX_CH * 2u) + (uint32_t)m0 * 2u : dev::kOOB;
-      return;
-    }
+    if constexpr (FIX) return;
     if (tid < BN) {
       const int p = n0 + tid;
       const bool pv = p < npos;
@@ -443,7 +444,9 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
   // pinned with scheduling barriers: a wave issues at most one instruction
   // per four clocks, so everything besides the MFMAs has to be spread thin.
   auto half = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], auto rstc, int rks,
-                  bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0, auto&& advance) {
+                  bf16x8 (&ra)[4], bf16x8 (&rb)[4], auto dstc, int j0, auto&& advance,
+                  auto nlc) {
+    constexpr int NL = decltype(nlc)::value;  // loads in this half: 4, or 8 (W and dY of one tile)
 #pragma unroll
     for (int q = 0; q < 16; q++) {
       // Boustrophedon order over the 4x4 blocks: consecutive MFMAs change
@@ -451,8 +454,13 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
       const int bm = q >> 2, bn = (bm & 1) ? 3 - (q & 3) : (q & 3);
       acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bm], fb[bn], acc[bm][bn], 0, 0, 0);
       if (q < 12) read_one(rstc, rks, q, ra, rb);
-      if ((q & 3) == 2) set_m0(dstc, j0 + (q >> 2));
-      if ((q & 3) == 3) load_m0(j0 + (q >> 2));
+      if constexpr (NL == 4) {
+        if ((q & 3) == 2) set_m0(dstc, j0 + (q >> 2));
+        if ((q & 3) == 3) load_m0(j0 + (q >> 2));
+      } else {
+        if ((q & 1) == 0) set_m0(dstc, j0 + (q >> 1));
+        if ((q & 1) == 1) load_m0(j0 + (q >> 1));
+      }
       if (q == 1) advance();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -489,12 +497,148 @@ __global__ __launch_bounds__(THREADS, 1) void igemm_nhwc_bf16_kernel(
   auto iter = [&](int kt, auto stc) {
     constexpr int ST = decltype(stc)::value;
     half(fa0, fb0, stc, 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(),
-         DMA_PER_TILE / 2, [&]() { advance_a(kb + kt + NSTAGE); });
+         DMA_PER_TILE / 2, [&]() { advance_a(kb + kt + NSTAGE); }, std::integral_constant<int, 4>());
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE));
     __builtin_amdgcn_s_barrier();
     half(fa1, fb1, std::integral_constant<int, (ST + 1) & (NSTAGE - 1)>(), 0, fa0, fb0, stc, 0,
-         [&]() { advance_b(kb + kt + NSTAGE); });
+         [&]() { advance_b(kb + kt + NSTAGE); }, std::integral_constant<int, 4>());
   };
+  // ---- FIX: the last four k tiles (all resident, one per stage) one
+  // column group bn at a time -- 32 positions of each wave's half, all four
+  // k tiles -- so that group bn's accumulators are final three groups
+  // before the end.  Its conversion to bf16 (into the staging buffer) and
+  // its dX stores then run between the MFMAs of the next group, and only
+  // the last group's stores remain after the last MFMA.  Per element the
+  // summation order is the main loop's (k ascending), so the result is the
+  // same bits.  The A fragments of the four tiles are read once (group 0)
+  // and kept; B is read per step.  Group 0 waits for tiles KT-3..KT-1 as it
+  // reaches them.
+  auto tail_and_store = [&]() {
+    bf16x8 ta[NSTAGE][2][4];  // [tile][k step][bm]
+    bf16x8 tb[2];
+#pragma unroll
+    for (int i = 0; i < 4; i++) ta[0][0][i] = fa0[i];
+    tb[0] = fb0[0];
+    // Staging: row r = 32 wn + (lane & 31) holds position wn*128 + 32 bn + (lane & 31);
+    // 16-byte chunk c/8 at chunk (c/8) ^ (r & 31) (conflict-free 8-byte writes).
+    lds_char* const sg = (lds_char*)stg;
+    const int srow = wn * 32 + (lane & 31);
+    lds_char* sw[4][4];
+#pragma unroll
+    for (int bm = 0; bm < 4; bm++)
+#pragma unroll
+      for (int qq = 0; qq < 4; qq++) {
+        const int chunk = wm * 16 + bm * 4 + qq;
+        sw[bm][qq] = sg + srow * 512 + ((chunk ^ (srow & 31)) << 4) + ((lane >> 5) << 3);
+      }
+    // Stores: thread = (row r0 = tid >> 5 of each 8, chunk sc = tid & 31);
+    // item it covers staging row 8 it + r0.  dX pixel of position p is
+    // 2p + fix_r (positions past npos fall beyond dX's record count).
+    const int r0 = tid >> 5, sc = tid & 31;
+    lds_char* sr[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) sr[i] = sg + (i * 8 + r0) * 512 + (((sc ^ r0) ^ (i * 8)) << 4);
+    const uint32_t obase = (uint32_t)(2 * (n0 + r0) + fix_r) * (FIX_CH * 2u) + (uint32_t)m0 * 2u + (uint32_t)sc * 16u;
+    auto convert_part = [&](int bn, int bm, int qq) {
+      u32x2 o;
+      o[0] = dev::bf16_pack2(acc[bm][bn][4 * qq + 0], acc[bm][bn][4 * qq + 1]);
+      o[1] = dev::bf16_pack2(acc[bm][bn][4 * qq + 2], acc[bm][bn][4 * qq + 3]);
+      *(__attribute__((address_space(3))) u32x2*)sw[bm][qq] = o;
+    };
+    u32x4 sv[8];  // the group's staged chunks of this thread, read at once after the fill barrier
+    auto read_items = [&]() {
+#pragma unroll
+      for (int it = 0; it < 8; it++)
+        sv[it] = *(const __attribute__((address_space(3))) u32x4*)(sr[it & 3] + (it >> 2) * (32 * 512));
+    };
+    auto store_item = [&](int bn, int it) {
+      const uint32_t prow = (uint32_t)((it >> 2) * 128 + bn * 32 + (it & 3) * 8);  // position row - r0
+      __builtin_amdgcn_raw_buffer_store_b128(u4{sv[it][0], sv[it][1], sv[it][2], sv[it][3]}, rdx,
+                                             obase + prow * (2u * FIX_CH * 2u), 0, kStoreAux);
+    };
+    auto sync_lds = [&]() {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));  // lgkmcnt(0), vmcnt unconstrained
+      __builtin_amdgcn_s_barrier();
+    };
+#pragma unroll
+    for (int st = 0; st < 32; st++) {
+      const int g = st >> 3, j = (st >> 1) & 3, ks = st & 1, ph = st & 7;
+      const int s1 = st + 1, g1 = s1 >> 3, j1 = (s1 >> 1) & 3, ks1 = s1 & 1;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        acc[q][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[j][ks][q], tb[st & 1], acc[q][g], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q == 0) {
+          if (s1 < 32 && g1 == 0 && ks1 == 0) {
+            // tile KT-4+j1 (stage j1) complete: its loads are older than the
+            // 8 (3 - j1) loads of the later tiles
+            if (j1 == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+            if (j1 == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+            if (j1 == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __builtin_amdgcn_s_barrier();
+          }
+          if (g >= 2 && ph == 0) sync_lds();  // staging read out by every thread
+          if (g >= 1 && ph == 4) {
+            sync_lds();  // staging filled by every thread
+            read_items();
+          }
+        }
+        if (s1 < 32) {
+          if (q == 0) tb[s1 & 1] = *(const bf16x8*)(smem + j1 * BBYTES + b_rd[g1][ks1]);
+          if (g1 == 0) {
+            lds_char* at = (lds_char*)smem + j1 * ABYTES;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(at + a_rd[q][ks1][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(at + a_rd[q][ks1][1]));
+            ta[j1][ks1][q] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+        if (g >= 1 && ph < 4) convert_part(g - 1, ph, q);
+        // stores of the staged group: items 0, 1 at q = 2, 3 of the read
+        // step, then two per step
+        if (g >= 1 && ph == 4 && q >= 2) store_item(g - 1, q - 2);
+        if (g >= 1 && ph > 4 && (q & 1) == 0) store_item(g - 1, 2 * (ph - 4) + (q >> 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    sync_lds();
+#pragma unroll
+    for (int bm = 0; bm < 4; bm++)
+#pragma unroll
+      for (int qq = 0; qq < 4; qq++) convert_part(3, bm, qq);
+    sync_lds();
+    read_items();
+#pragma unroll
+    for (int it = 0; it < 8; it++) store_item(3, it);
+  };
+
+  if constexpr (FIX) {
+    // Tiles [0, KT-4) here; the last of them loads the W and dY parts of
+    // tile KT-1 together (no loads past the end); tiles [KT-4, KT) in the
+    // tail.
+    static_assert(SKPT * STAPS % NSTAGE == 0 && SKPT * STAPS >= 2 * NSTAGE, "FIX: whole rounds of stages");
+#pragma unroll 1
+    for (int kt = 0; kt < KT - 2 * NSTAGE; kt += NSTAGE) {
+      iter(kt, std::integral_constant<int, 0>());
+      iter(kt + 1, std::integral_constant<int, 1>());
+      iter(kt + 2, std::integral_constant<int, 2>());
+      iter(kt + 3, std::integral_constant<int, 3>());
+    }
+    iter(KT - 8, std::integral_constant<int, 0>());
+    iter(KT - 7, std::integral_constant<int, 1>());
+    iter(KT - 6, std::integral_constant<int, 2>());
+    {
+      const int kt = KT - 5;
+      constexpr int ST = 3;
+      half(fa0, fb0, std::integral_constant<int, ST>(), 1, fa1, fb1, std::integral_constant<int, (ST + 3) & (NSTAGE - 1)>(),
+           DMA_PER_TILE / 2, [&]() { advance_a(kb + kt + NSTAGE); }, std::integral_constant<int, 4>());
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NSTAGE - 2) * DMA_PER_TILE));
+      __builtin_amdgcn_s_barrier();
+      half(fa1, fb1, std::integral_constant<int, 0>(), 0, fa0, fb0, std::integral_constant<int, ST>(), 0,
+           [&]() { advance_b(kb + kt + NSTAGE); }, std::integral_constant<int, 8>());
+    }
+    tail_and_store();
+    return;
+  }
 #pragma unroll 1
   for (int kt = 0; kt < KT; kt += NSTAGE) {
     iter(kt, std::integral_constant<int, 0>());
