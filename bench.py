@@ -299,10 +299,11 @@ def copy_calibration(nbytes, reps):
 # Summaries under profiles/ of rocprofv3 passes over this script, one pass per
 # directory under RAW named <pass>_<problem>:
 #   kt    rocprofv3 --kernel-trace --stats ... -- bench.py PROF --problem P --steps 50 --warmup 5
+#           (with the clock-settle calls; the summary also gives the 50 timed calls alone)
 #   ktng  the same with --no-graph (calls issued one by one)
 #   fetch rocprofv3 --pmc FETCH_SIZE ... -- bench.py PROF --problem P --steps 10 --warmup 2
-#           --no-graph --copy-calibration-mib 1024      (write: WRITE_SIZE)
-#   mfma  rocprofv3 --pmc <MFMA_COUNTERS> ... --no-graph; stall: <STALL_COUNTERS>
+#           --no-graph --settle-ms 0 --copy-calibration-mib 1024      (write: WRITE_SIZE)
+#   mfma  rocprofv3 --pmc <MFMA_COUNTERS> ... --no-graph --settle-ms 0; stall: <STALL_COUNTERS>
 PROF = "--cpu-seconds 0 --no-secondary"
 MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
 STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
@@ -316,7 +317,7 @@ def pass_command(kind, prob):
         return f"{ROCPROF} --kernel-trace --stats {out} --steps 50 --warmup 5" + (" --no-graph" if kind == "ktng" else "")
     pmc = {"fetch": "FETCH_SIZE", "write": "WRITE_SIZE", "mfma": MFMA_COUNTERS, "stall": STALL_COUNTERS}[kind]
     cal = " --copy-calibration-mib 1024" if kind in ("fetch", "write") else ""
-    return f"{ROCPROF} --pmc {pmc} {out} --steps 10 --warmup 2 --no-graph{cal}"
+    return f"{ROCPROF} --pmc {pmc} {out} --steps 10 --warmup 2 --no-graph --settle-ms 0{cal}"
 
 
 def summarize_profiles(raw):
@@ -336,10 +337,11 @@ def summarize_profiles(raw):
         return kernel_key(info), describe(p)
 
     def trace(d, sym):
-        rows = list(csv.DictReader(open(os.path.join(d, "prof_kernel_trace.csv"))))
-        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows if sym in r["Kernel_Name"]]
-        name = next(r["Kernel_Name"] for r in rows if sym in r["Kernel_Name"])
-        return name, sorted(durs)
+        """Kernel name and its dispatch durations (us) in start order."""
+        rows = [r for r in csv.DictReader(open(os.path.join(d, "prof_kernel_trace.csv"))) if sym in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows]
+        return rows[0]["Kernel_Name"], durs
 
     def bench_line(d):
         f = d.rstrip("/") + ".out"
@@ -387,14 +389,19 @@ def summarize_profiles(raw):
                                 ("ktng", "calls issued one by one")):
                 if kind not in ks:
                     continue
-                name, s_ = trace(ks[kind], sym)
-                out += [f"## {prob}, {title}", f"command: {pass_command(kind, prob)}", f"summary: {summary_cmd}", "",
-                        "| kernel | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|",
-                        f"| {name} | {len(s_)} | {statistics.mean(s_):.3f} | {statistics.median(s_):.3f} | "
-                        f"{s_[0]:.3f} | {s_[-1]:.3f} |", ""]
+                name, d_ = trace(ks[kind], sym)
                 b = bench_line(ks[kind])
+                steps = b["steps"] if b else 50
+                row = lambda lbl, x: (f"| {lbl} | {len(x)} | {statistics.mean(x):.3f} | {statistics.median(x):.3f} | "
+                                      f"{min(x):.3f} | {max(x):.3f} |")
+                out += [f"## {prob}, {title}", f"command: {pass_command(kind, prob)}", f"summary: {summary_cmd}",
+                        f"kernel: {name}", "",
+                        "| dispatches | calls | avg us | median us | min us | max us |", "|---|---|---|---|---|---|",
+                        row("all (warmup, capture, clock settle, timed)", d_),
+                        row(f"the {steps} timed calls (the last {steps})", d_[-steps:]), ""]
                 if b:
-                    out += [f"The same run's own HIP-event time per call ({b['config']['timing']}): "
+                    out += [f"The same run's own HIP-event time per call ({b['config']['timing']}, after "
+                            f"{b.get('settle', {}).get('calls', 0)} clock-settle calls): "
                             f"{b['roofline']['launch_us_mean']} us.", ""]
             open(base + "_kernel_trace.md", "w").write("\n".join(out))
             written.append(base + "_kernel_trace.md")
@@ -531,6 +538,8 @@ def main():
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload problem: warm and cold (caches "
                          "flushed) µs/call and the roofline fraction; not the bench line")
+    ap.add_argument("--cold-flush", choices=("read", "write"), default="read",
+                    help="--all: how the 512 MiB sweep before each cold call evicts the caches")
     ap.add_argument("--summarize-profiles", metavar="RAW", default=None,
                     help="write the profiles/ summaries of the rocprofv3 passes under RAW "
                          "(<pass>_<problem> directories; no GPU needed)")
@@ -734,8 +743,11 @@ def all_problems(args):
     """Every workload problem: warm = back-to-back calls under one event pair
     (host launch cost included: small problems are bounded by it); graph = the
     same calls replayed from a captured HIP graph (GPU time only); cold = calls
-    each preceded (outside its event pair) by a 512 MiB write that evicts L2
-    and the MALL.  Fractions are of the problem's own roofline."""
+    each preceded (outside its event pair) by a sweep over a 512 MiB buffer
+    that evicts L2 and the MALL: a read sweep by default, which leaves the
+    caches clean (a write sweep, --cold-flush write, leaves dirty lines whose
+    write-back then falls inside the timed call).  Fractions are of the
+    problem's own roofline."""
     import numpy as np
     import torch
 
@@ -743,7 +755,15 @@ def all_problems(args):
     from cbd_inputs import PROBLEMS, draw, seed_for
 
     stream = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(64 << 20, dtype=torch.float64, device="cuda")  # 512 MiB
+    sink = torch.empty((), dtype=torch.float64, device="cuda")
+
+    def evict():
+        if args.cold_flush == "write":
+            flush.fill_(1.0)
+        else:
+            torch.sum(flush, dim=0, out=sink)
+    torch.cuda.synchronize()
     mach = machine()
     for p in PROBLEMS:
         dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
@@ -769,7 +789,7 @@ def all_problems(args):
         warm = e0.elapsed_time(e1) * 1e3 / args.steps
         cold = []
         for _ in range(50):
-            flush.fill_(1)
+            evict()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             cbd.run(pl, dy_d, w_d, dx_d, stream=stream)
@@ -829,7 +849,7 @@ def all_problems(args):
             "static_shape": info.static_shape,
             "us_graph_descriptor_driven": round(us_dyn, 2) if us_dyn is not None else None,
             "us_warm": round(warm, 2), "us_graph": round(us_graph, 2),
-            "us_cold_median": round(med, 2),
+            "us_cold_median": round(med, 2), "cold_flush": args.cold_flush + " sweep of 512 MiB",
             "us_cold_p10": round(float(np.percentile(cold, 10)), 2),
             "us_cold_p90": round(float(np.percentile(cold, 90)), 2),
             "bound": bound + (" (launch latency in practice)" if p.name in LATENCY_BOUND else ""),
