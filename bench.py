@@ -756,13 +756,16 @@ def all_problems(args):
 
     stream = torch.cuda.current_stream()
     flush = torch.ones(64 << 20, dtype=torch.float64, device="cuda")  # 512 MiB
-    sink = torch.empty((), dtype=torch.float64, device="cuda")
+    rows = flush.view(65536, 1024)
+    rowmax = torch.empty(65536, dtype=torch.float64, device="cuda")
 
     def evict():
+        # read sweep: a row-wise max (one output per 8 KiB row, no
+        # cross-block reduction); write sweep: a fill kernel
         if args.cold_flush == "write":
             flush.fill_(1.0)
         else:
-            torch.sum(flush, dim=0, out=sink)
+            torch.amax(rows, dim=1, out=rowmax)
     torch.cuda.synchronize()
     mach = machine()
     for p in PROBLEMS:

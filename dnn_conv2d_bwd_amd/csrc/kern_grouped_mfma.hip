@@ -42,6 +42,16 @@
 namespace cbd {
 namespace {
 
+// Cache policy of the dX stores: sc0 sc1 (bits 0 and 4 of the buffer_store
+// cache-policy operand), written through instead of held dirty in L2.
+// Measured on the 32-group 3x3 problems (graph / cold-cache us): stride 2
+// 13.1 / 18.4 -> 11.7 / 17.1, stride 1 20.1 / 25.3 -> 19.0 / 24.8; the
+// non-temporal hint alone, or with sc0 sc1, was slower cold on stride 1.
+#ifndef CBD_GROUPED_STORE_AUX
+#define CBD_GROUPED_STORE_AUX 17
+#endif
+constexpr int kStoreAux = CBD_GROUPED_STORE_AUX;
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -99,7 +109,7 @@ __device__ __forceinline__ void mfma_rows(const GemmArgs& a, const void* dy_p, c
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 v = *(const u32x4*)(out + px * PIXB + ((c ^ ((px & 3) << 2)) << 4));
       __builtin_amdgcn_raw_buffer_store_b128(
-          v, rdx, xr + ((uint32_t)(s.phase_w + Sw * (tb + px)) << PSHIFT) + (uint32_t)(c << 4), 0, 0);
+          v, rdx, xr + ((uint32_t)(s.phase_w + Sw * (tb + px)) << PSHIFT) + (uint32_t)(c << 4), 0, kStoreAux);
     }
   };
 
