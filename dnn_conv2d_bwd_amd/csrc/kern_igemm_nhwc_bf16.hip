@@ -36,7 +36,9 @@
 //   * epilogue: accumulators -> bf16 (nearest-even, v_cvt_pk_bf16_f32) -> LDS
 //     ([position][c], chunk ^ (row & 31)) -> 16-byte coalesced stores along
 //     each dX pixel row, in four column groups so that one group's stores
-//     drain while the next is converted;
+//     drain while the next is converted; in the 2048-channel instance the
+//     last four k tiles run one column group at a time instead, so that
+//     three groups' conversions and stores overlap the remaining MFMAs;
 //   * a fully shape-specialised instance for the 2048-channel 1x2 stride-2
 //     problem (any batch and even width) takes the class from its tile
 //     index and computes every offset with shifts and multiplies; the
