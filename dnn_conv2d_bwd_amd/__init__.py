@@ -55,7 +55,7 @@ class PlanOptions(ctypes.Structure):
                 ("rows_per_wg", ctypes.c_int32), ("grouped_dot", ctypes.c_int32),
                 ("cols_per_wg", ctypes.c_int32), ("ksplit", ctypes.c_int32),
                 ("per_class", ctypes.c_int32), ("static_shape", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("merge_phases", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -163,11 +163,11 @@ class Plan:
 
     def __init__(self, problem: Problem, force_kernel: int = KERNEL_AUTO, no_split: bool = False,
                  rows_per_wg: int = 0, grouped_dot: bool = False, cols_per_wg: int = 0,
-                 ksplit: int = 0, per_class: bool = False, static_shape: int = 0):
+                 ksplit: int = 0, per_class: bool = False, static_shape: int = 0, merge_phases: int = 0):
         self.problem = problem
         h = ctypes.c_void_p()
         opts = PlanOptions(force_kernel, 1 if no_split else 0, rows_per_wg, 1 if grouped_dot else 0,
-                           cols_per_wg, ksplit, 1 if per_class else 0, int(static_shape))
+                           cols_per_wg, ksplit, 1 if per_class else 0, int(static_shape), int(merge_phases))
         _check(_lib.cbd_plan_ex(ctypes.byref(problem), ctypes.byref(opts), ctypes.byref(h)),
                "cbd_plan")
         self._h = h
@@ -226,11 +226,11 @@ class Plan:
 def plan(n=None, g=1, c=None, k=None, hi=None, wi=None, y=None, x=None, stride=1, pad=0, dil=1,
          layout="nchw", dtype="f32", force_kernel=KERNEL_AUTO, problem=None,
          no_split=False, rows_per_wg=0, grouped_dot=False, cols_per_wg=0, ksplit=0,
-         per_class=False, static_shape=0) -> Plan:
+         per_class=False, static_shape=0, merge_phases=0) -> Plan:
     if problem is None:
         problem = make_problem(n, g, c, k, hi, wi, y, x, stride, pad, dil, layout, dtype)
     return Plan(problem, force_kernel, no_split, rows_per_wg, grouped_dot, cols_per_wg, ksplit,
-                per_class, static_shape)
+                per_class, static_shape, merge_phases)
 
 
 def _torch_dtype(dt):

@@ -25,6 +25,7 @@ struct DynGeo {
   __device__ static uint32_t dx_bytes(const GemmArgs& a) { return a.dx_bytes; }
   __device__ static uint32_t w_bytes(const GemmArgs& a) { return a.w_bytes; }
   __device__ static SubDesc sub(const GemmArgs& a, int t) { return a.sub[dev::find_class(a, t)]; }
+  __device__ static SubDesc sub_at(const GemmArgs& a, int i) { return a.sub[i]; }
 };
 
 template <class T>
@@ -59,6 +60,7 @@ struct StatGeo {
       if (t >= T::k.sub[q].tile_begin) r = T::k.sub[q];
     return r;
   }
+  __device__ static constexpr SubDesc sub_at(const GemmArgs&, int i) { return T::k.sub[i]; }
 };
 
 }  // namespace cbd

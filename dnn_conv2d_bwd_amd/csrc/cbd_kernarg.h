@@ -96,6 +96,7 @@ struct GemmArgs {
   int32_t grp_mfma;    // 1: the pipelined kernel on 4x4x4 MFMA (bf16, C/G = 4, G in {32, 64})
   int32_t grp_cols;    // MFMA pipelined kernels: positions per column block of a row
   int32_t grp_wide;    // 1: the 16x16x16-MFMA kernel (bf16, C/G = K/G in {16, 32})
+  int32_t grp_merged;  // 1: the 4x4x4-MFMA kernel with the four phases of a 2x2 stride in one workgroup
   int32_t gen_waves;   // generic family: waves per workgroup (4, or 8 for long K on small grids)
   int32_t ksplit;      // large-tile kernel: workgroups sharing a tile's K loop (<= 1: none)
   int32_t static_shape;  // large-tile kernel: 1 = 64 k tiles per tap, 1 tap; 2 = the fixed 2048-channel

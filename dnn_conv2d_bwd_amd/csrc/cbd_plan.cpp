@@ -219,8 +219,9 @@ const char* kernel_name(int32_t k, int64_t variant) {
   if (k == CBD_KERNEL_GENERIC) return "generic";
   if (k == CBD_KERNEL_NCHW_ROWS) return "nchw_rows (row blocks)";
   static const char* const grouped[] = {"grouped/direct", "grouped/rows", "grouped/pipelined-dot",
-                                        "grouped/pipelined-4x4x4-mfma", "grouped/pipelined-16x16x16-mfma"};
-  return variant >= 0 && variant < 5 ? grouped[variant] : "grouped";
+                                        "grouped/pipelined-4x4x4-mfma", "grouped/pipelined-16x16x16-mfma",
+                                        "grouped/pipelined-4x4x4-mfma, phases merged"};
+  return variant >= 0 && variant < 6 ? grouped[variant] : "grouped";
 }
 
 void log_plan(const cbd_plan_s& pl) {
@@ -349,9 +350,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int32_t ksplit_opt = 0;
   bool per_class = false;
   int32_t static_mode = 0;
+  int32_t merge_opt = 0;
   if (options) {
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 3; i++)
       if (options->reserved[i]) return fail(CBD_ERR_INVALID_ARG, "options.reserved must be zero");
+    if (options->merge_phases < -1 || options->merge_phases > 1)
+      return fail(CBD_ERR_INVALID_ARG, "options.merge_phases must be -1, 0 or 1");
+    merge_opt = options->merge_phases;
     if (options->static_shape < -1 || options->static_shape > 1)
       return fail(CBD_ERR_INVALID_ARG, "options.static_shape must be -1, 0 or 1");
     static_mode = options->static_shape;
@@ -576,7 +581,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   int64_t slots = 0;
   int64_t grp_lds = 0;
   int64_t grp_rows = 0, grp_cols = 0;
-  bool grp_mfma = false, grp_wide = false;
+  bool grp_mfma = false, grp_wide = false, grp_merged = false;
+  int64_t merged_tiles = 0;
   if (kernel == CBD_KERNEL_GROUPED && (Cg == 16 || Cg == 32) && rows_opt < 0) {
     delete pl;
     return fail(CBD_ERR_UNSUPPORTED, "16 or 32 channels per group run only on the pipelined kernel "
@@ -676,7 +682,73 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
         ring = lds_mfma(cb);
       }
     }
-    if (pipe_ok && ring <= cbd::kLdsPerCu) {
+    // Merged phases: stride 2 x 2, each of the four phases a class, taps
+    // one dY row and column apart, at most 4 taps per class.  A workgroup
+    // walks class rows of one image and a block of cb class columns for all
+    // four phases: its ring holds the union of the phases' dY rows (span_h +
+    // 1 in use, one more being filled) over the union of their columns, and
+    // its output buffer two dX row segments of 2 * 4*ceil(cb/4) pixels.
+    bool merge_ok = grp_mfma && !per_class && p.stride_h == 2 && p.stride_w == 2 && ah.delta == 1 &&
+                    aw.delta == 1 && subs.size() == 4;
+    int64_t lo_h = 0, hi_h = 0, lo_w = 0, hi_w = 0, mph = 0, mpw = 0;
+    if (merge_ok) {
+      int seen = 0;
+      lo_h = lo_w = INT64_MAX;
+      hi_h = hi_w = INT64_MIN;
+      for (const auto& s : subs) {
+        seen |= 1 << (s.phase_h * 2 + s.phase_w);
+        if (s.taps_h * s.taps_w > 4) merge_ok = false;
+        lo_h = std::min<int64_t>(lo_h, s.beta_h - (s.taps_h - 1));
+        hi_h = std::max<int64_t>(hi_h, s.beta_h);
+        lo_w = std::min<int64_t>(lo_w, s.beta_w - (s.taps_w - 1));
+        hi_w = std::max<int64_t>(hi_w, s.beta_w);
+        mph = std::max<int64_t>(mph, s.pos_h);
+        mpw = std::max<int64_t>(mpw, s.pos_w);
+      }
+      if (seen != 15) merge_ok = false;
+    }
+    auto lds_merged = [&](int64_t cb) {
+      const int64_t seg = std::min<int64_t>(cb, mpw);
+      const int64_t rowb = (seg + (hi_w - lo_w) + 3) * pixb;
+      return (hi_h - lo_h + 2) * ceil_div(rowb, 1024) * 1024 + 2 * 8 * ceil_div(seg, 4) * pixb;
+    };
+    if (merge_opt == 1 && !merge_ok) {
+      delete pl;
+      return fail(CBD_ERR_UNSUPPORTED, "merge_phases = 1: needs the grouped 4x4x4-MFMA kernel at stride 2 x 2 "
+                                       "with every phase a class of at most 4 taps, taps one dY row and "
+                                       "column apart, and not per_class");
+    }
+    // Only on request: measured slower than one class per workgroup (c5-s2
+    // 19.3 against 11.8 us: a third as many workgroups, each row four times
+    // the work and its 28 KiB of dX stores drained before the next row).
+    if (merge_ok && merge_opt == 1) {
+      int64_t cb = 4 * ceil_div(mpw, 4);
+      if (cols_opt > 0) {
+        cb = std::min<int64_t>(cb, 4 * ceil_div(cols_opt, 4));
+      } else {
+        for (int64_t k = 2; lds_merged(cb) > cbd::kLdsPerCu / 3 && cb > 4; k++)
+          cb = 4 * ceil_div(mpw, 4 * k);
+      }
+      if (lds_merged(cb) <= cbd::kLdsPerCu) {
+        grp_merged = true;
+        grp_cols = cb;
+        ring = lds_merged(cb);
+      } else if (merge_opt == 1) {
+        delete pl;
+        return fail(CBD_ERR_UNSUPPORTED, "merge_phases = 1: a column block's rows exceed LDS");
+      }
+    }
+    if (grp_merged) {
+      const int64_t units = p.n * mph * ceil_div(mpw, grp_cols);  // (image, class row, column block)
+      if (rows_opt > 0) {
+        grp_rows = std::min<int64_t>(rows_opt, mph);
+      } else {
+        const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / ring);
+        grp_rows = std::min<int64_t>(mph, std::max<int64_t>(1, ceil_div(units, resident)));
+      }
+      grp_lds = ring;
+      merged_tiles = p.n * ceil_div(mph, grp_rows) * ceil_div(mpw, grp_cols);
+    } else if (pipe_ok && ring <= cbd::kLdsPerCu) {
       int64_t units = 0;  // (image, class row, column block)
       for (const auto& s : subs) units += p.n * s.pos_h * (grp_mfma ? ceil_div(s.pos_w, grp_cols) : 1);
       if (rows_opt > 0) {
@@ -755,6 +827,8 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     s.tile_begin = tile;
     if (kernel == CBD_KERNEL_NCHW_ROWS)
       s.tiles = 0, s.tile_begin = 0;  // every workgroup serves every class
+    else if (grp_merged)
+      s.tiles = 0, s.tile_begin = 0;  // every workgroup serves every class
     else if (kernel == CBD_KERNEL_GROUPED)
       s.tiles = grp_wide      ? p.n * ceil_div(s.pos_h, grp_rows) * (p.g / (256 / (2 * Cg))) *
                                     ceil_div(s.pos_w, grp_cols)
@@ -769,6 +843,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     exec += p.g * s.m * s.n * s.k;
   }
   if (kernel == CBD_KERNEL_NCHW_ROWS) tile = p.n * p.g * rgeom.c_blocks * rgeom.row_blocks;
+  if (grp_merged) tile = merged_tiles;
   // A launch must stay below 2^32 work-items.
   if (tile * threads >= (int64_t(1) << 32)) {
     delete pl;
@@ -823,6 +898,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
   a.grp_rows = (int32_t)grp_rows;
   a.grp_mfma = grp_mfma ? 1 : 0;
   a.grp_wide = grp_wide ? 1 : 0;
+  a.grp_merged = grp_merged ? 1 : 0;
   a.grp_cols = (int32_t)grp_cols;
   a.ksplit = ksplit > 1 ? (int32_t)ksplit : 0;
   a.static_shape = static_shape;
@@ -865,7 +941,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     }
   }
   // Grouped 4x4x4-MFMA kernel: likewise.
-  if (kernel == CBD_KERNEL_GROUPED && grp_mfma && static_mode >= 0 && !per_class) {
+  if (kernel == CBD_KERNEL_GROUPED && grp_mfma && !grp_merged && static_mode >= 0 && !per_class) {
     for (int i = 0; i < cbd::kGroupedShapes; i++) {
       if (grouped_shape_matches(cbd::kGroupedShapeKeys[i], a, p, threads)) {
         static_shape = 2;
@@ -977,6 +1053,7 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     info.align_dy = info.align_w = info.align_dx = 16;
   }
   info.variant = kernel != CBD_KERNEL_GROUPED ? 0
+                 : grp_merged                  ? 5
                  : grp_wide                    ? 4
                  : grp_mfma                    ? 3
                  : grp_rows > 0                ? 2

@@ -150,18 +150,28 @@ typedef struct {
   int32_t per_class;    /* 1: one main launch per residue class instead of one
                            for all (an ablation of the single launch; not
                            with ksplit); 0 or 1 */
-  int32_t static_shape; /* large-tile kernel: shape-specialised instances
-                           compute the same bits as the descriptor-driven
-                           kernel.  Level 1: k tiles per tap and taps per
-                           class fixed at compile time (K/G = 2048, one tap
-                           per class).  Level 2: the whole geometry fixed
-                           (G = 1, C = K = 2048, Hi = 1, a 1x2 filter at
-                           stride 2 along W, no padding, even Wi; any N and
-                           Wi; not with per_class).  0: the most specialised
-                           one that matches; 1: required (UNSUPPORTED if none
-                           matches); -1: never (the descriptor-driven kernel,
-                           for comparison) */
-  int32_t reserved[4];  /* must be zero */
+  int32_t static_shape; /* shape-specialised instances, which compute the
+                           same bits as the descriptor-driven kernel.
+                           Large-tile kernel, level 1: k tiles per tap and
+                           taps per class fixed at compile time (K/G =
+                           2048, one tap per class); level 2: the whole
+                           geometry fixed (G = 1, C = K = 2048, Hi = 1, a
+                           1x2 filter at stride 2 along W, no padding, even
+                           Wi; any N and Wi; not with per_class).  Generic
+                           and grouped 4x4x4-MFMA kernels: level 2, the
+                           whole plan of one of the listed workload
+                           problems (not with per_class or ksplit).  0: the
+                           most specialised one that matches; 1: required
+                           (UNSUPPORTED if none matches); -1: never (the
+                           descriptor-driven kernel, for comparison) */
+  int32_t merge_phases; /* grouped 4x4x4-MFMA kernel at stride 2 x 2 with
+                           every phase a class (taps one dY row and column
+                           apart, at most 4 taps per class): 1 runs one
+                           workgroup per block of class rows for all four
+                           phases, writing whole dX rows (a comparison
+                           form, measured slower; UNSUPPORTED where it does
+                           not apply); 0 or -1: one class per workgroup */
+  int32_t reserved[3];  /* must be zero */
 } cbd_plan_options;
 
 /* Build a plan (host-only work; needs no GPU).  On success *out_plan owns a
@@ -278,7 +288,9 @@ typedef struct {
                                dot-product instructions, 3 pipelined rows on
                                4x4x4 MFMA (bf16, C/G = 4, G = 32 or 64),
                                4 pipelined rows on 16x16x16 MFMA (bf16, C/G
-                               = 16 or 32); other families: 0 */
+                               = 16 or 32), 5 as 3 with the four phases of a
+                               2 x 2 stride in one workgroup (merge_phases
+                               = 1); other families: 0 */
   int32_t align_dy, align_w, align_dx; /* byte alignment cbd_run requires of
                                each pointer: the element size for the generic
                                family (16 for dx when a zero-fill writes

@@ -37,12 +37,12 @@ def operands(p, kind="dist"):
 
 
 def plan_for(p, force=cbd.KERNEL_AUTO, rows_per_wg=0, grouped_dot=False, cols_per_wg=0, ksplit=0,
-             per_class=False, static_shape=0):
+             per_class=False, static_shape=0, merge_phases=0):
     dt = cbd.F32 if p.dtype == "f32" else cbd.BF16
     return cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw),
                     (p.dh, p.dw), p.layout, dt, force_kernel=force, rows_per_wg=rows_per_wg,
                     grouped_dot=grouped_dot, cols_per_wg=cols_per_wg, ksplit=ksplit,
-                    per_class=per_class, static_shape=static_shape)
+                    per_class=per_class, static_shape=static_shape, merge_phases=merge_phases)
 
 
 def torch_dtype(p):

@@ -663,13 +663,15 @@ def test_fuzz_grouped_mfma(seed, count):
             continue
         rows = rng.choice([0, 1, 2, 5, 64])
         cols = rng.choice([0, 0, 4, 8, 13])
+        merge = rng.choice([0, 1])
         try:
-            pl = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols)
+            pl = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols, merge_phases=merge)
         except cbd.CbdError:
             continue
-        if pl.info().variant != 3:
+        if pl.info().variant not in (3, 5):
             continue
-        print(f"[fuzz-mfma] i={done} rows={rows} cols={cols} {p}", flush=True)
+        print(f"[fuzz-mfma] i={done} rows={rows} cols={cols} merge={merge} variant={pl.info().variant} {p}",
+              flush=True)
         sh = oracle.shapes(p)
         dy = small_ints(4000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
         w = small_ints(4000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
@@ -679,6 +681,67 @@ def test_fuzz_grouped_mfma(seed, count):
         assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
         assert run.guards_intact(), (p, rows, cols)
         done += 1
+
+
+# The 4x4x4-MFMA kernel with the four phases of a 2 x 2 stride in one
+# workgroup: random sizes (odd and even extents, so that phases differ in
+# rows and columns), filters up to 4 x 4, padding, rows and column blocks;
+# integer operands bit-exact against the oracle, and the same bits as one
+# class per workgroup.
+@pytest.mark.parametrize("seed,count", [(19, 50)])
+def test_fuzz_grouped_mfma_merged(seed, count):
+    rng = random.Random(seed)
+    done = 0
+    while done < count:
+        g = rng.choice([32, 64])
+        y, x = rng.randint(2, 4), rng.randint(2, 4)
+        p = Problem("fuzz-merged", rng.randint(1, 3), g, 4 * g, 4 * g, rng.randint(2, 37),
+                    rng.randint(2, 37), y, x, 2, 2, rng.randint(0, y - 1), rng.randint(0, x - 1), 1, 1,
+                    NHWC, "bf16", "u", "u", 0, 0)
+        if (p.hi + 2 * p.ph - (p.y - 1) - 1 < 0 or p.wi + 2 * p.pw - (p.x - 1) - 1 < 0):
+            continue
+        rows = rng.choice([0, 1, 2, 3, 64])
+        cols = rng.choice([0, 0, 4, 8, 13])
+        try:
+            pm = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols, merge_phases=1)
+        except cbd.CbdError:
+            continue
+        pu = plan_for(p, cbd.KERNEL_GROUPED, rows, False, cols, merge_phases=-1)
+        assert pm.info().variant == 5 and pu.info().variant == 3
+        print(f"[fuzz-merged] i={done} rows={rows} cols={cols} R={pm.info().rows_per_wg} "
+              f"CB={pm.info().cols_per_wg} grid={pm.info().grid_main} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(5000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(5000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
+        dy_d, w_d = to_device(dy, p), to_device(w, p)
+        rm = DeviceRun(p, pm, dy_d, w_d)()
+        ru = DeviceRun(p, pu, dy_d, w_d)()
+        want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle.bwd_data(p, dy, w)))
+        got = rm.result_f32()
+        assert np.array_equal(got, want.reshape(got.shape)), (p, rows, cols)
+        assert np.array_equal(rm.result_bits(), ru.result_bits()), (p, rows, cols)
+        assert rm.guards_intact() and ru.guards_intact(), (p, rows, cols)
+        done += 1
+
+
+@pytest.mark.parametrize("name", ["c5-s2", "gs-c4-56-s2", "gs-c4-7-s2"])
+def test_grouped_merged_matches_per_class(name):
+    """The merged-phase plan (merge_phases = 1) of a stride-2 grouped
+    workload gives the same bits as its default one-class-per-workgroup
+    plan, on the workload's distributions; against the oracle within the
+    bf16 tolerance."""
+    p = by_name(name) if not name.startswith("gs-") else [q for q in GROUPED_SWEEP if q.name == name][0]
+    print(f"[merged] {name}", flush=True)
+    pm, pu = plan_for(p, merge_phases=1), plan_for(p)
+    assert pm.info().variant == 5 and pu.info().variant == 3
+    dy, w = operands(p)
+    dy_d, w_d = to_device(dy, p), to_device(w, p)
+    rm = DeviceRun(p, pm, dy_d, w_d)()
+    ru = DeviceRun(p, pu, dy_d, w_d)()
+    assert np.array_equal(rm.result_bits(), ru.result_bits())
+    ok, info = check(p, rm, oracle.bwd_data(p, dy, w))
+    assert ok, info
+    assert rm.guards_intact() and ru.guards_intact()
 
 
 # The grouped sweep (32 groups x 4..32 channels, 56..7 pixels, stride 1/2)

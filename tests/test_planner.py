@@ -400,6 +400,38 @@ def test_grouped_static_shapes():
         cbd.plan(63, 32, 128, 128, 56, 56, 3, 3, 2, 1, 1, "nhwc", "bf16", static_shape=1)
 
 
+def test_merge_phases_option():
+    """merge_phases = 1 runs the stride-2 grouped workload with the four
+    phases in one workgroup (variant 5, whole-image grid, no class tile
+    ranges); the default keeps one class per workgroup; a problem the merged
+    form does not serve is refused, and out-of-range values are invalid."""
+    by = {q.name: q for q in PROBLEMS}
+    p = by["c5-s2"]
+    args = (p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw), (p.dh, p.dw), p.layout, cbd.BF16)
+    d = cbd.plan(*args).info()
+    assert d.variant == 3
+    pm = cbd.plan(*args, merge_phases=1)
+    m = pm.info()
+    assert (m.variant, m.static_shape, m.num_zero_regions, m.launches) == (5, 0, 0, 1)
+    subs = pm.subgemms()
+    assert len(subs) == 4 and all(s.tiles == 0 and s.tile_begin == 0 for s in subs)
+    assert {(s.phase_h, s.phase_w) for s in subs} == {(0, 0), (0, 1), (1, 0), (1, 1)}
+    ph = max(s.pos_h for s in subs)
+    pw = max(s.pos_w for s in subs)
+    assert m.grid_main == p.n * -(-ph // m.rows_per_wg) * -(-pw // m.cols_per_wg)
+    assert m.cols_per_wg % 4 == 0 and 0 < m.lds_dynamic <= 160 * 1024
+    assert m.useful_flops == d.useful_flops and m.executed_macs == d.executed_macs
+    assert cbd.plan(*args, merge_phases=-1).info().variant == 3
+    s1 = by["c5-s1"]
+    with pytest.raises(cbd.CbdError):  # stride 1: one class
+        cbd.plan(s1.n, s1.g, s1.c, s1.k, s1.hi, s1.wi, s1.y, s1.x, (s1.sh, s1.sw), (s1.ph, s1.pw),
+                 (s1.dh, s1.dw), s1.layout, cbd.BF16, merge_phases=1)
+    with pytest.raises(cbd.CbdError):  # per_class
+        cbd.plan(*args, merge_phases=1, per_class=True)
+    with pytest.raises(cbd.CbdError):
+        cbd.plan(*args, merge_phases=2)
+
+
 @pytest.mark.skipif(os.path.exists("/dev/kfd"),
                     reason="passes made-up device addresses to a real launch: only on a machine "
                            "with no GPU driver at all, where the launch itself must fail")
