@@ -14,6 +14,7 @@ namespace cbd {
 // first gather but the three tensor pointers, which arrive preloaded).
 struct DynGeo {
   static constexpr bool kStatic = false;
+  static constexpr int kRowPats = kRowPatsAll;  // row-load patterns compiled in (generic family)
 #define CBD_DYN(f) \
   __device__ static int f(const GemmArgs& a) { return a.f; }
   CBD_DYN(N) CBD_DYN(C) CBD_DYN(K) CBD_DYN(Cg) CBD_DYN(Kg) CBD_DYN(Hi) CBD_DYN(Wi) CBD_DYN(Ho)
@@ -28,9 +29,25 @@ struct DynGeo {
   __device__ static SubDesc sub_at(const GemmArgs& a, int i) { return a.sub[i]; }
 };
 
+// A descriptor-driven launch whose classes need only the row-load
+// patterns in M (the others are not compiled into it, which keeps its
+// register count to that of the paths it runs).
+template <int M>
+struct DynGeoRows : DynGeo {
+  static constexpr int kRowPats = M;
+};
+
 template <class T>
 struct StatGeo {
   static constexpr bool kStatic = true;
+  // Row-load patterns of its classes.
+  static constexpr int row_pats() {
+    int m = 0;
+    for (int q = 0; q < T::k.num_sub; q++)
+      m |= 1 << row_pattern(T::k.sub[q].taps_h, T::k.sub[q].taps_w, T::k.sub[q].cls_w, T::k.X, T::k.tstep_w);
+    return m & kRowPatsAll;
+  }
+  static constexpr int kRowPats = row_pats();
 #define CBD_STAT(f) \
   __device__ static constexpr int f(const GemmArgs&) { return T::k.f; }
   CBD_STAT(N) CBD_STAT(C) CBD_STAT(K) CBD_STAT(Cg) CBD_STAT(Kg) CBD_STAT(Hi) CBD_STAT(Wi) CBD_STAT(Ho)

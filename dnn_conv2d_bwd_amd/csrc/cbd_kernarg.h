@@ -72,6 +72,20 @@ struct RowsGeom {
   uint32_t mag_plane, mag_rw, mag_perk, mag_yx, mag_perc, mag_chunks;
 };
 
+// Row-load pattern of a residue class on the generic family (f32 KCYX):
+// the taps of one filter row lie within three consecutive W elements, so
+// a lane reads them with one two- or three-element load.  1 / 2: one tap
+// per row (followed by an element of the same row) in 1 / 2 rows; 3 / 4:
+// two taps two apart in 1 / 2 rows; 5: 3 x 3 adjacent taps; 0: none.
+constexpr int row_pattern(int taps_h, int taps_w, int cls_w, int X, int tstep_w) {
+  return taps_w == 1 && cls_w + 1 < X                   ? (taps_h == 1 ? 1 : taps_h == 2 ? 2 : 0)
+         : taps_w == 2 && tstep_w == 2                  ? (taps_h == 1 ? 3 : taps_h == 2 ? 4 : 0)
+         : taps_w == 3 && tstep_w == 1 && taps_h == 3 ? 5
+                                                        : 0;
+}
+constexpr int kRowPatsAll = 0x3e;     // patterns 1-5
+constexpr int kRowPatsStride2 = 0x1e; // patterns 1-4
+
 struct GemmArgs {
   // problem (element counts; every tensor is < 2^31 bytes)
   int32_t N, G, C, K, Cg, Kg;
@@ -104,6 +118,7 @@ struct GemmArgs {
   int32_t static_id;
   int32_t zblock;      // generic family, one class at phase (0,0) covering every S x S block of dX: its
                        // epilogue also writes the block's unreached positions (no zero-fill)
+  int32_t row_pats;    // generic family, f32 KCYX: bit p set when a class has row-load pattern p
   void* ws;            // split-K f32 partial tiles, 256 KiB per workgroup (caller's workspace)
   const void* dy;
   const void* w;

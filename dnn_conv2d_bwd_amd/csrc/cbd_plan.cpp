@@ -548,12 +548,18 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     // Long K on a small grid of 32x32 tiles: eight waves per workgroup share
     // the K loop (a wave's gather chain halves; measured: 32 channels, 3x3,
     // N = 32, 14-16 pixels, 36 k tiles on 196-256 workgroups, 6 % faster;
-    // with short K or many workgroups eight waves were slower).
+    // with short K or many workgroups eight waves were slower).  f32 KCYX
+    // classes with a row-load pattern run k tiles of 4 k rows (8 for one or
+    // two taps) over all their taps: 8 such tiles for those 32-channel
+    // problems, where four waves are 8 % faster than eight.
     if (bm == 32 && bn == 32) {
       int64_t grid32 = 0, kt = 0;
+      const bool rows = p.dtype == CBD_F32 && p.layout == CBD_LAYOUT_NCHW && !no_split;
       for (const auto& s : subs) {
         grid32 += p.g * ceil_div(Cg, 32) * ceil_div(s.n, 32);
-        kt = std::max<int64_t>(kt, int64_t(s.taps_h) * s.taps_w * ceil_div(Kg, bk));
+        const int taps = s.taps_h * s.taps_w;
+        const bool rl = rows && cbd::row_pattern(s.taps_h, s.taps_w, s.class_w, (int)p.x, s.tstep_w) != 0;
+        kt = std::max<int64_t>(kt, rl ? ceil_div(Kg, taps <= 2 ? 8 : 4) : int64_t(taps) * ceil_div(Kg, bk));
       }
       if (grid32 < 512 && kt >= 32) threads = 8 * 64;
     }
@@ -927,6 +933,13 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
                       subs[0].phase_h == 0 && subs[0].phase_w == 0 &&
                       subs[0].pos_h == ceil_div(p.hi, p.stride_h) && subs[0].pos_w == ceil_div(p.wi, p.stride_w);
   a.zblock = zblock ? 1 : 0;
+  // Generic family, f32 KCYX: the row-load patterns of the classes (the
+  // launch picks an instance compiled with just those).
+  a.row_pats = 0;
+  if (kernel == CBD_KERNEL_GENERIC && p.dtype == CBD_F32 && p.layout == CBD_LAYOUT_NCHW && !no_split)
+    for (const auto& s : subs)
+      a.row_pats |= 1 << cbd::row_pattern(s.taps_h, s.taps_w, s.class_w, (int)p.x, s.tstep_w);
+  a.row_pats &= cbd::kRowPatsAll;
   // Generic family: the shape-specialised instance whose compiled geometry
   // is exactly this plan's, if one was built.
   a.static_id = 0;

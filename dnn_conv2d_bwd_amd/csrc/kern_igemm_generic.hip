@@ -29,6 +29,10 @@
 // up to 32x32, 16 on larger ones.  Operands are gathered
 // element-wise with buffer loads (out-of-range -> 0: padding, ragged tiles,
 // taps off dY's edge) and converted to f32; bf16 products are exact in f32.
+// f32 KCYX classes whose taps in a filter row lie within three consecutive
+// elements (3x3 filters at stride 1 or 2, among others) instead read W one
+// filter row per two- or three-element load and run K tap by tap over k
+// tiles of 4 (or 8) k rows ("row loads", below).
 //
 // Split-K (a plan with ksplit S >= 2, for grids too small to fill the GPU):
 // the S workgroups of a tile are S consecutive logical tiles; workgroup sp
@@ -81,6 +85,25 @@ __device__ inline void store_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
   } else {
     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)dev::bf16_rne(v), r, byte_off, 0, 0);
+  }
+}
+
+// WID (2 or 3) consecutive f32 elements at byte offset voff + soff: one
+// multi-element load per lane.
+template <int WID>
+__device__ inline void load_row(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float (&v)[WID]) {
+  if constexpr (WID == 2) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    v[0] = __uint_as_float(x.x);
+    v[1] = __uint_as_float(x.y);
+  } else {
+    static_assert(WID == 3, "row loads are 2 or 3 elements");
+    typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+    const u3 x = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    v[0] = __uint_as_float(x.x);
+    v[1] = __uint_as_float(x.y);
+    v[2] = __uint_as_float(x.z);
   }
 }
 
@@ -348,7 +371,115 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
       }
     }
   };
-  if (tapfast) {
+  // Row loads (f32 KCYX, residue split; classes whose taps in one filter
+  // row lie within three consecutive elements): lane (channel c, k row q4)
+  // reads the taps of one filter row of its W[k][c] block with a single
+  // two- or three-element load, and K runs k-fastest within each tap:
+  // k step (kg, t) of a k tile pairs W[k0 + 4kg + q4][c][tap t] with
+  // dY[k0 + 4kg + q4][position shifted by tap t].  A single-element gather
+  // whose lanes are Y*X elements apart costs the address path about 3.5x a
+  // contiguous one, while a two- to four-element load costs 2x whatever its
+  // pattern, so reading a row of taps per load cuts that work by 2.5-7x;
+  // the dY gathers keep their contiguous 16-position runs.
+  auto row_path = [&](auto th_c, auto tw_c, auto ts_c) {
+    constexpr int TH = decltype(th_c)::value, TW = decltype(tw_c)::value, TS = decltype(ts_c)::value;
+    constexpr int TT = TH * TW;
+    constexpr int WID = TW == 1 ? 2 : (TW - 1) * TS + 1;  // elements per row load
+    // One k tile in flight per wave: with 64 VGPRs eight waves fit a SIMD,
+    // and on the 64-channel stride-2 problem that occupancy is worth more
+    // than a second tile of gathers per wave (11.2 against 12.0 us).
+    constexpr int KG = TT <= 2 ? 2 : 1;  // groups of 4 k rows per k tile
+    constexpr int RD = 1;                // k tiles in flight per wave
+    const int KTr = (Kg + 4 * KG - 1) / (4 * KG);
+    const int kb = KTr * sp / S, ke = KTr * (sp + 1) / S;
+    uint32_t wl[MB];
+#pragma unroll
+    for (int bm = 0; bm < MB; bm++) {
+      const int c = m0 + 16 * bm + r16;
+      wl[bm] = c < Cg ? (uint32_t)((q4 * Cg + c) * YX + s.cls_w) * ES : dev::kOOB;
+    }
+    uint32_t wrow[TH];
+#pragma unroll
+    for (int jh = 0; jh < TH; jh++) wrow[jh] = uni((s.cls_h + tstep_h * jh) * Xf * (int)ES);
+    uint32_t bl[NB][TT];
+#pragma unroll
+    for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+      for (int jh = 0; jh < TH; jh++)
+#pragma unroll
+        for (int jw = 0; jw < TW; jw++) {
+          const int dh = s.beta_h - delta_h * jh, dw = s.beta_w - delta_w * jw;
+          const bool ok = bp_ok[bn] && pth[bn] >= -dh && pth[bn] < Ho - dh && ptw[bn] >= -dw && ptw[bn] < Wo - dw;
+          bl[bn][jh * TW + jw] = ok ? (uint32_t)(bpos[bn] + dh * Wo + dw) * ES : dev::kOOB;
+        }
+    float wv[RD][KG][MB][TH][WID], bv[RD][KG][NB][TT];
+    auto fetch = [&](int kt, float (&w)[KG][MB][TH][WID], float (&b)[KG][NB][TT]) {
+#pragma unroll
+      for (int kg = 0; kg < KG; kg++) {
+        const int k = (kt * KG + kg) * 4;
+        const uint32_t a_s = uni(k * a_ks * (int)ES);
+#pragma unroll
+        for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+          for (int jh = 0; jh < TH; jh++) load_row<WID>(rw, opaque(wl[bm]), a_s + wrow[jh], w[kg][bm][jh]);
+        const bool kok = q4 < Kg - k;  // dY rows past K/G read 0
+        const uint32_t b_s = uni(k * b_ks * (int)ES);
+#pragma unroll
+        for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+          for (int tt = 0; tt < TT; tt++) b[kg][bn][tt] = load_elem<DT>(rdy, opaque(kok ? bl[bn][tt] : dev::kOOB), b_s);
+      }
+    };
+    auto comp = [&](const float (&w)[KG][MB][TH][WID], const float (&b)[KG][NB][TT]) {
+#pragma unroll
+      for (int kg = 0; kg < KG; kg++)
+#pragma unroll
+        for (int jh = 0; jh < TH; jh++)
+#pragma unroll
+          for (int jw = 0; jw < TW; jw++)
+#pragma unroll
+            for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+              for (int bn = 0; bn < NB; bn++)
+                acc[bm][bn] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[kg][bm][jh][jw * TS], b[kg][bn][jh * TW + jw],
+                                                                   acc[bm][bn], 0, 0, 0);
+    };
+    int kn = kb + wave;
+#pragma unroll
+    for (int d = 0; d < RD; d++) {
+      if (kn < ke) fetch(kn, wv[d], bv[d]);
+      kn += NW;
+    }
+    for (int kt = kb + wave; kt < ke; kt += RD * NW) {
+#pragma unroll
+      for (int d = 0; d < RD; d++) {
+        if (kt + d * NW < ke) {
+          comp(wv[d], bv[d]);
+          if (kn < ke) fetch(kn, wv[d], bv[d]);
+          kn += NW;
+        }
+      }
+    }
+  };
+  int rpat = 0;  // row-load pattern of this class (0: none)
+  if constexpr (DT == 0 && LAYOUT == 0 && !NS)
+    rpat = uni(row_pattern(s.taps_h, s.taps_w, s.cls_w, Xf, tstep_w));
+  constexpr int pats = MB * NB <= 4 ? Geo::kRowPats : 0;  // (larger tiles: registers)
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if ((pats & 2) && rpat == 1) {
+    row_path(I1(), I1(), I0());
+  } else if ((pats & 4) && rpat == 2) {
+    row_path(I2(), I1(), I0());
+  } else if ((pats & 8) && rpat == 3) {
+    row_path(I1(), I2(), I2());
+  } else if ((pats & 16) && rpat == 4) {
+    row_path(I2(), I2(), I2());
+  } else if ((pats & 32) && rpat == 5) {
+    row_path(I3(), I3(), I1());
+  } else if (tapfast) {
     kloop([&](int kt, float (&av)[AE], float (&bv)[BE]) { gather_tf(kt, av, bv); });
   } else {
     Walk wn = walk_at(kbeg + wave);  // walks in step with the tiles fetched
@@ -505,6 +636,20 @@ int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
   void* args[] = {&dy, &w, &dx, const_cast<GemmArgs*>(&a)};
   const void* k = a.no_split ? (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, true, DynGeo>
                              : (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeo>;
+  if constexpr (DT == 0 && LAYOUT == 0 && BM * BN <= 1024) {
+    // f32 KCYX: an instance compiled with only the row-load patterns the
+    // classes need (any pattern it lacks runs the general K order).
+    constexpr int kS2 = kRowPatsStride2, k33 = kRowPatsAll & ~kRowPatsStride2;
+    const int rp = a.row_pats & kRowPatsAll;
+    if (!a.no_split) {
+      if (rp == 0)
+        k = (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeoRows<0>>;
+      else if ((rp & ~kS2) == 0)
+        k = (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeoRows<kS2>>;
+      else if (rp == k33)
+        k = (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeoRows<k33>>;
+    }
+  }
   return (int)hipLaunchKernel(k,
                               dim3((unsigned)grid), dim3(NW * 64), args, 0,
                               (hipStream_t)stream);

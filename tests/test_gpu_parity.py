@@ -602,6 +602,74 @@ def test_fuzz_random_values(family, seed, count):
         assert ok, (p, info)
 
 
+def row_load_patterns(p):
+    """Row-load patterns of the residue classes of an f32 NCHW problem on
+    the generic family (host restatement of the kernel's choice, used only
+    to show which K orders a fuzz set reaches): per class, 1/2 = one tap
+    per filter row in 1/2 rows, 3/4 = two taps two apart in 1/2 rows,
+    5 = 3x3 adjacent taps, 0 = another order."""
+    import math
+
+    def axis(f, s, d, pad):
+        step = s // math.gcd(s, d)
+        out = []
+        for ph in range(s):
+            taps = [j for j in range(f) if (ph + pad - j * d) % s == 0]
+            if taps:
+                out.append((len(taps), taps[0], step))
+        return out
+    pats = set()
+    for th, _, _ in axis(p.y, p.sh, p.dh, p.ph):
+        for tw, cw, stw in axis(p.x, p.sw, p.dw, p.pw):
+            if tw == 1 and cw + 1 < p.x:
+                pats.add({1: 1, 2: 2}.get(th, 0))
+            elif tw == 2 and stw == 2:
+                pats.add({1: 3, 2: 4}.get(th, 0))
+            elif tw == 3 and stw == 1 and th == 3:
+                pats.add(5)
+            else:
+                pats.add(0)
+    return pats
+
+
+@pytest.mark.parametrize("seed,count,ksplit", [(31, 120, 0), (32, 40, 3)])
+def test_fuzz_generic_row_loads(seed, count, ksplit):
+    """f32 NCHW problems on the generic family whose classes read W a
+    filter row at a time (1-3 taps per load): filters 2, 3 and 5, strides
+    1-3, dilation 1-2, groups, K/G not a multiple of 4 (k rows past K/G),
+    ragged channel and position tiles, and split-K over the row-load k
+    tiles; bit-exact on integer operands, every pattern reached."""
+    rng = random.Random(seed)
+    seen = set()
+    done = 0
+    while done < count:
+        g = rng.choice([1, 1, 2, 3])
+        f = rng.choice([2, 3, 3, 5])
+        s = rng.choice([1, 2, 2, 3])
+        d = rng.choice([1, 1, 2])
+        pad = rng.randint(0, 2)
+        p = Problem("fuzz-rows", rng.randint(1, 3), g, g * rng.randint(1, 40), g * rng.randint(1, 40),
+                    rng.randint(2, 20), rng.randint(2, 20), f, f, s, s, pad, pad, d, d, NCHW, "f32",
+                    "u", "u", 0, 0)
+        if p.hi + 2 * p.ph - p.dh * (p.y - 1) - 1 < 0 or p.wi + 2 * p.pw - p.dw * (p.x - 1) - 1 < 0:
+            continue
+        pats = row_load_patterns(p)
+        seen |= pats
+        opts = {"ksplit": ksplit} if ksplit else {}
+        pl = plan_for(p, cbd.KERNEL_GENERIC, **opts)
+        print(f"[fuzz-rows] i={done} pats={sorted(pats)} ksplit={pl.info().ksplit} {p}", flush=True)
+        sh = oracle.shapes(p)
+        dy = small_ints(9000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
+        w = small_ints(9000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
+        ws = torch.empty(max(pl.workspace_size(), 1), dtype=torch.uint8, device="cuda")
+        run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
+        ref = oracle.bwd_data(p, dy, w)
+        assert np.array_equal(run.result_bits().reshape(ref.shape), exact_expected_bits(p, ref)), p
+        assert run.guards_intact(), p
+        done += 1
+    assert {1, 2, 3, 4, 5} <= seen, seen
+
+
 # Grouped family: the pipelined row kernel with several rows per workgroup
 # (the automatic choice gives tiny problems one row each), and the one-row
 # kernel it replaces (rows_per_wg = -1).

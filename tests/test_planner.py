@@ -464,10 +464,15 @@ def test_generic_tile_choice():
         assert (inf.tile_m, inf.tile_n, inf.tile_k) == (32, 32, 8), q.name
     c1 = plan_of([q for q in PROBLEMS if q.name == "c1"][0], cbd.KERNEL_GENERIC).info()
     assert (c1.tile_m, c1.tile_n, c1.tile_k) == (16, 16, 8)
-    # eight waves per workgroup only for long K (>= 32 k tiles) on small grids
+    # eight waves per workgroup only for long K (>= 32 k tiles) on small grids;
+    # f32 KCYX classes that read W a filter row at a time count k tiles of 4 k
+    # rows over all taps (8 for the 3x3 32-channel problems: four waves)
     waves = {q.name: plan_of(q, cbd.KERNEL_GENERIC).info().threads_main // 64 for q in PROBLEMS[:9]}
-    assert waves == {"c1": 4, "c2-14-1": 4, "c2-14-3": 8, "c2-15-1": 4, "c2-15-3": 8,
-                     "c2-16-1": 4, "c2-16-3": 8, "c3a": 4, "c3b": 4}
+    assert waves == {"c1": 4, "c2-14-1": 4, "c2-14-3": 4, "c2-15-1": 4, "c2-15-3": 4,
+                     "c2-16-1": 4, "c2-16-3": 4, "c3a": 4, "c3b": 4}
+    # the same 3x3 stride-1 32-channel problem in NHWC (no row loads): eight
+    nhwc = [q for q in PROBLEMS if q.name == "c2-14-3"][0].with_(layout=NHWC)
+    assert plan_of(nhwc, cbd.KERNEL_GENERIC).info().threads_main == 8 * 64
     big = P_("g64", 16, 1, 64, 64, 64, 64, 1, 1, 1, 1, 0, 0, 1, 1, NCHW, "f32", "u", "u", 0, 0)
     inf = plan_of(big, cbd.KERNEL_GENERIC).info()
     assert (inf.tile_m, inf.tile_n, inf.tile_k, inf.grid_main) == (64, 64, 16, 1024)
