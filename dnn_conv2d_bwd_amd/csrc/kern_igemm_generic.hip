@@ -421,14 +421,38 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
 #pragma unroll
         for (int bm = 0; bm < MB; bm++)
 #pragma unroll
-          for (int jh = 0; jh < TH; jh++) load_row<WID>(rw, opaque(wl[bm]), a_s + wrow[jh], w[kg][bm][jh]);
-        const bool kok = q4 < Kg - k;  // dY rows past K/G read 0
+          for (int jh = 0; jh < TH; jh++) load_row<WID>(rw, wl[bm], a_s + wrow[jh], w[kg][bm][jh]);
         const uint32_t b_s = uni(k * b_ks * (int)ES);
+        if (Kg - k >= 4) {  // (wave-uniform) all four k rows inside K/G: the offsets as they are
 #pragma unroll
-        for (int bn = 0; bn < NB; bn++)
+          for (int bn = 0; bn < NB; bn++)
 #pragma unroll
-          for (int tt = 0; tt < TT; tt++) b[kg][bn][tt] = load_elem<DT>(rdy, opaque(kok ? bl[bn][tt] : dev::kOOB), b_s);
+            for (int tt = 0; tt < TT; tt++) b[kg][bn][tt] = load_elem<DT>(rdy, bl[bn][tt], b_s);
+        } else {  // dY rows past K/G read 0
+          const bool kok = q4 < Kg - k;
+#pragma unroll
+          for (int bn = 0; bn < NB; bn++)
+#pragma unroll
+            for (int tt = 0; tt < TT; tt++)
+              b[kg][bn][tt] = load_elem<DT>(rdy, opaque(kok ? bl[bn][tt] : dev::kOOB), b_s);
+        }
       }
+    };
+    // Elements of a row load that no tap uses (the middle one of taps two
+    // apart, the second one of a single tap): kept live until the tile's
+    // MFMAs have issued, so that their registers are not handed to the next
+    // load's operands while the load is still in flight (which would make
+    // every following load wait for the previous one).
+    auto keep_unused = [&](const float (&w)[KG][MB][TH][WID]) {
+#pragma unroll
+      for (int kg = 0; kg < KG; kg++)
+#pragma unroll
+        for (int bm = 0; bm < MB; bm++)
+#pragma unroll
+          for (int jh = 0; jh < TH; jh++)
+#pragma unroll
+            for (int e = 0; e < WID; e++)
+              if (TW == 1 ? e != 0 : (e % TS != 0 || e / TS >= TW)) asm volatile("" ::"v"(w[kg][bm][jh][e]));
     };
     auto comp = [&](const float (&w)[KG][MB][TH][WID], const float (&b)[KG][NB][TT]) {
 #pragma unroll
@@ -455,6 +479,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
       for (int d = 0; d < RD; d++) {
         if (kt + d * NW < ke) {
           comp(wv[d], bv[d]);
+          keep_unused(wv[d]);
           if (kn < ke) fetch(kn, wv[d], bv[d]);
           kn += NW;
         }
