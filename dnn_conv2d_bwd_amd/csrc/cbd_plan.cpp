@@ -562,6 +562,18 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
         kt = std::max<int64_t>(kt, rl ? ceil_div(Kg, taps <= 2 ? 8 : 4) : int64_t(taps) * ceil_div(Kg, bk));
       }
       if (grid32 < 512 && kt >= 32) threads = 8 * 64;
+      // Every class reading W by rows with one to four taps (stride 2, for
+      // one): two waves per workgroup, each with two k tiles in flight
+      // (measured, descriptor-driven: 64 channels, 3x3, stride 2, N = 8-64,
+      // 784-3136 tiles, 5-14 % faster than four waves; shape-specialised,
+      // the workload problem 10.6 against 10.8 us; with nine-tap classes
+      // two waves were 19-22 % slower).
+      bool rows_s2 = rows && ksplit_opt < 2 && !subs.empty();
+      for (const auto& s : subs) {
+        const int rp = cbd::row_pattern(s.taps_h, s.taps_w, s.class_w, (int)p.x, s.tstep_w);
+        rows_s2 = rows_s2 && rp >= 1 && rp <= 4;
+      }
+      if (rows_s2 && threads == 4 * 64) threads = 2 * 64;
     }
   } else if (kernel == CBD_KERNEL_NHWC_BF16) {
     bm = cbd::kFastBM; bn = cbd::kFastBN; bk = cbd::kFastBK; threads = cbd::kFastThreads;

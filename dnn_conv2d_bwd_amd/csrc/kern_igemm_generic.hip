@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   // problems 8.05 -> 7.73 us with eight; the stride-2 64-channel problems
   // 17.1 -> 18.0 and 7.5 -> 8.5 us).
   constexpr int DEPTH = (AE + BE <= 8 && (NW == 8 || BM * BN <= 256)) ? 8 : 2;
-  constexpr int RED = (NW / 2) * BM * BN;              // NW/2 partial tiles at a time
+  constexpr int RED = (NW > 4 ? NW / 2 : 2) * BM * BN;  // NW/2 (at least two) partial tiles at a time
   constexpr int LDSF = RED;
   constexpr uint32_t ES = DT == 0 ? 4 : 2;
   __shared__ float lds[LDSF];
@@ -385,11 +385,15 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
     constexpr int TH = decltype(th_c)::value, TW = decltype(tw_c)::value, TS = decltype(ts_c)::value;
     constexpr int TT = TH * TW;
     constexpr int WID = TW == 1 ? 2 : (TW - 1) * TS + 1;  // elements per row load
-    // One k tile in flight per wave: with 64 VGPRs eight waves fit a SIMD,
-    // and on the 64-channel stride-2 problem that occupancy is worth more
-    // than a second tile of gathers per wave (11.2 against 12.0 us).
-    constexpr int KG = TT <= 2 ? 2 : 1;  // groups of 4 k rows per k tile
-    constexpr int RD = 1;                // k tiles in flight per wave
+    // k tiles in flight per wave: one on four-wave workgroups (64 VGPRs,
+    // eight waves per SIMD: there that occupancy is worth more than a
+    // second tile per wave, 11.2 against 12.0 us on the 64-channel
+    // stride-2 problem); two on the two-wave workgroups the planner gives
+    // grids of one- to four-tap classes (one cross-wave sum instead of two,
+    // 92 VGPRs: 10.6 against 10.8 us shape-specialised, 13.0 against 13.7
+    // descriptor-driven; three or four tiles were 10.9 and 11.4 us).
+    constexpr int KG = TT <= 2 ? 2 : 1;       // groups of 4 k rows per k tile
+    constexpr int RD = NW == 2 && TT <= 4 ? 2 : 1;
     const int KTr = (Kg + 4 * KG - 1) / (4 * KG);
     const int kb = KTr * sp / S, ke = KTr * (sp + 1) / S;
     uint32_t wl[MB];
@@ -666,6 +670,11 @@ int launch_one(const GemmArgs& a, int64_t grid, void* stream) {
     // classes need (any pattern it lacks runs the general K order).
     constexpr int kS2 = kRowPatsStride2, k33 = kRowPatsAll & ~kRowPatsStride2;
     const int rp = a.row_pats & kRowPatsAll;
+    if constexpr (NW == 2) {
+      if (!a.no_split && (rp & ~kS2) == 0 && rp != 0)
+        k = (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeoRows<kS2>>;
+      return (int)hipLaunchKernel(k, dim3((unsigned)grid), dim3(NW * 64), args, 0, (hipStream_t)stream);
+    }
     if (!a.no_split) {
       if (rp == 0)
         k = (const void*)&igemm_generic_kernel<DT, LAYOUT, BM, BN, NW, false, DynGeoRows<0>>;
@@ -728,6 +737,10 @@ int launch_tiles(const GemmArgs& a, int64_t grid, void* stream) {
   if (a.tile_m == 64 && a.tile_n == 64) return launch_one<DT, LAYOUT, 64, 64>(a, grid, stream);
   if (a.tile_m == 32 && a.tile_n == 64) return launch_one<DT, LAYOUT, 32, 64>(a, grid, stream);
   if (a.tile_m == 64 && a.tile_n == 32) return launch_one<DT, LAYOUT, 64, 32>(a, grid, stream);
+  if constexpr (DT == 0 && LAYOUT == 0) {
+    // two waves: f32 KCYX plans whose classes all read W by rows (patterns 1-4)
+    if (a.tile_m == 32 && a.tile_n == 32 && a.gen_waves == 2) return launch_one<DT, LAYOUT, 32, 32, 2>(a, grid, stream);
+  }
   if (a.tile_m == 32 && a.tile_n == 32)
     return a.gen_waves == 8 ? launch_one<DT, LAYOUT, 32, 32, 8>(a, grid, stream)
                             : launch_one<DT, LAYOUT, 32, 32>(a, grid, stream);
