@@ -104,6 +104,13 @@ cbd_status run_impl(const cbd_plan_t* plan, const void* dy, const void* w, void*
         c.sub[0] = a.sub[i];
         c.sub[0].tile_begin = 0;
         c.class_begin[0] = 0;
+        if (info.kernel == CBD_KERNEL_GENERIC && a.tile_n > 0) {  // the class's divisor reciprocals at index 0
+          const cbd::SubDesc& d = a.sub[i];
+          const int64_t npix = int64_t(d.pos_h) * d.pos_w;
+          c.mag_npix[0] = cbd::recip32(npix);
+          c.mag_posw[0] = cbd::recip32(d.pos_w);
+          c.mag_pergroup[0] = cbd::recip32(int64_t(a.tiles_m) * ((int64_t(a.N) * npix + a.tile_n - 1) / a.tile_n));
+        }
         c.num_sub = 1;
         c.total_tiles = (int32_t)plan->subs[i].tiles;
         err = launch_main(c, plan->subs[i].tiles);

@@ -27,6 +27,20 @@ struct DynGeo {
   __device__ static uint32_t w_bytes(const GemmArgs& a) { return a.w_bytes; }
   __device__ static SubDesc sub(const GemmArgs& a, int t) { return a.sub[dev::find_class(a, t)]; }
   __device__ static SubDesc sub_at(const GemmArgs& a, int i) { return a.sub[i]; }
+  __device__ static int sub_index(const GemmArgs& a, int t) { return dev::find_class(a, t); }
+  // The reciprocals of class ci's divisors (read together, right after the
+  // class's descriptor), and x / d with one of them (a division for the
+  // classes past the first kMagSub, whose reciprocals are not stored).
+  struct Mags {
+    uint32_t npix, posw, pergroup, tiles_m;
+  };
+  __device__ static Mags mags(const GemmArgs& a, int ci) {
+    const int c = ci < kMagSub ? ci : 0;
+    return Mags{a.mag_npix[c], a.mag_posw[c], a.mag_pergroup[c], a.mag_tiles_m};
+  }
+  __device__ static uint32_t div(int ci, uint32_t x, uint32_t d, uint32_t mag) {
+    return ci < kMagSub ? dev::fdiv(x, d, mag) : x / d;
+  }
 };
 
 // A descriptor-driven launch whose classes need only the row-load
@@ -78,6 +92,20 @@ struct StatGeo {
     return r;
   }
   __device__ static constexpr SubDesc sub_at(const GemmArgs&, int i) { return T::k.sub[i]; }
+  __device__ static int sub_index(const GemmArgs&, int t) {
+    int r = 0;
+#pragma unroll
+    for (int q = 1; q < T::k.num_sub; q++)
+      if (t >= T::k.sub[q].tile_begin) r = q;
+    return r;
+  }
+  // (divisors fixed per class: plain divisions, which the compiler folds
+  // where the classes agree)
+  struct Mags {
+    uint32_t npix, posw, pergroup, tiles_m;
+  };
+  __device__ static constexpr Mags mags(const GemmArgs&, int) { return Mags{0, 0, 0, 0}; }
+  __device__ static uint32_t div(int, uint32_t x, uint32_t d, uint32_t) { return x / d; }
 };
 
 }  // namespace cbd

@@ -9,6 +9,13 @@ namespace cbd {
 // Sub-GEMM (one stride-residue class) descriptors per launch.  The class
 // count is at most stride_h * stride_w, which the planner caps at 64.
 constexpr int kMaxSub = 64;
+constexpr int kMagSub = 16;  // classes with precomputed divisor reciprocals
+
+// ceil(2^32 / d) for d >= 2, 0 for d <= 1: x / d is umulhi(x, r) or one less.
+constexpr uint32_t recip32(int64_t d) {
+  return d <= 1 ? 0u
+                : (uint32_t)((uint64_t(1) << 32) / (uint64_t)d + ((uint64_t(1) << 32) % (uint64_t)d != 0));
+}
 constexpr int kMaxZero = 64;
 
 // One stride-residue class (i_h, i_w).  Along each axis the class owns the
@@ -128,6 +135,12 @@ struct GemmArgs {
   // from one batch of scalar loads instead of one load per class.
   int32_t class_begin[kMaxSub];
   SubDesc sub[kMaxSub];
+  // Rounded-up reciprocals ceil(2^32 / d) (0 for d = 1) of the generic
+  // family's per-class divisors, for the first kMagSub classes: positions
+  // per image (pos_h * pos_w), pos_w, and tiles per group (tiles_m *
+  // tiles_n); and of tiles_m.
+  uint32_t mag_npix[kMagSub], mag_posw[kMagSub], mag_pergroup[kMagSub];
+  uint32_t mag_tiles_m;
   FusedZero fz;
 };
 // Kernel arguments travel in the 4 KiB kernel-argument segment.

@@ -935,7 +935,14 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     d.pos_h = (int32_t)s.pos_h; d.pos_w = (int32_t)s.pos_w;
     d.tile_begin = (int32_t)s.tile_begin;
     a.class_begin[i] = d.tile_begin;
+    if (kernel == CBD_KERNEL_GENERIC && i < (size_t)cbd::kMagSub) {
+      const int64_t npix = s.pos_h * s.pos_w;
+      a.mag_npix[i] = magic32(npix);
+      a.mag_posw[i] = magic32(s.pos_w);
+      a.mag_pergroup[i] = magic32(tiles_m * ceil_div(p.n * npix, bn));
+    }
   }
+  a.mag_tiles_m = magic32(tiles_m);
   // Generic family, one class at phase (0,0) whose lattice is every S x S
   // block of dX (a 1x1 filter at stride S, for one): the main kernel's
   // epilogue writes each block whole, zeros included, instead of leaving

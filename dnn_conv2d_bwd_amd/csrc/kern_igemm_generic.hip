@@ -156,19 +156,23 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   }
 
   const int t = dev::logical_tile(blockIdx.x, total_tiles, Geo::xcd_remap(a));
-  const SubDesc s = Geo::sub(a, t);
+  // (descriptor-driven: the class index selects the divisor reciprocals)
+  const int ci = Geo::kStatic ? 0 : Geo::sub_index(a, t);
+  const SubDesc s = Geo::kStatic ? Geo::sub(a, t) : Geo::sub_at(a, ci);
+  const auto mg = Geo::mags(a, ci);
   const int npix_img = s.pos_h * s.pos_w;
   const int npos = N * npix_img;
   const int tiles_n = (npos + BN - 1) / BN;
   const int per_group = tiles_m * tiles_n;
   const int S = Geo::ksplit(a) > 1 ? Geo::ksplit(a) : 1;
   const int lt = t - s.tile_begin;
-  const int local = lt / S;
+  const int local = S > 1 ? lt / S : lt;
   const int sp = lt - local * S;  // split index (0 without split-K)
-  const int g = local / per_group;
+  const int g = (int)Geo::div(ci, (uint32_t)local, (uint32_t)per_group, mg.pergroup);
   const int rem = local - g * per_group;
-  const int m0 = (rem % tiles_m) * BM;
-  const int n0 = (rem / tiles_m) * BN;
+  const int mt = (int)Geo::div(0, (uint32_t)rem, (uint32_t)tiles_m, mg.tiles_m);
+  const int m0 = (rem - mt * tiles_m) * BM;
+  const int n0 = mt * BN;
 
   const int YX = Yf * Xf;
   const auto rdy = dev::rsrc(dy_p, Geo::dy_bytes(a));
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   const int T = s.taps_h * s.taps_w;
   const bool tapfast = !NS && (T == 1 || T == 2 || T == 4);
   const int KT = tapfast ? (Kg * T + BK - 1) / BK : T * kpt;
-  const int kbeg = KT * sp / S, kend = KT * (sp + 1) / S;  // this workgroup's k tiles
+  const int kbeg = S > 1 ? KT * sp / S : 0, kend = S > 1 ? KT * (sp + 1) / S : KT;  // this workgroup's k tiles
 
   // Gather roles, in the operand layout of v_mfma_f32_16x16x4_f32 (so the
   // gathered values feed the MFMAs directly, with no pass through LDS):
@@ -216,9 +220,9 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
     const int bp = n0 + 16 * bn + r16;
     bp_ok[bn] = bp < npos;
     const int bpp = bp_ok[bn] ? bp : 0;
-    const int pn = bpp / npix_img;
+    const int pn = (int)Geo::div(ci, (uint32_t)bpp, (uint32_t)npix_img, mg.npix);
     const int prr = bpp - pn * npix_img;
-    pth[bn] = prr / s.pos_w;
+    pth[bn] = (int)Geo::div(ci, (uint32_t)prr, (uint32_t)s.pos_w, mg.posw);
     ptw[bn] = prr - pth[bn] * s.pos_w;
     bpos[bn] = LAYOUT == 0 ? ((pn * K + g * Kg + q4) * Ho + pth[bn]) * Wo + ptw[bn]
                            : ((pn * Ho + pth[bn]) * Wo + ptw[bn]) * K + g * Kg + q4;
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
     constexpr int KG = TT <= 2 ? 2 : 1;       // groups of 4 k rows per k tile
     constexpr int RD = NW == 2 && TT <= 4 ? 2 : 1;
     const int KTr = (Kg + 4 * KG - 1) / (4 * KG);
-    const int kb = KTr * sp / S, ke = KTr * (sp + 1) / S;
+    const int kb = S > 1 ? KTr * sp / S : 0, ke = S > 1 ? KTr * (sp + 1) / S : KTr;
     uint32_t wl[MB];
 #pragma unroll
     for (int bm = 0; bm < MB; bm++) {
@@ -571,9 +575,9 @@ __global__ __launch_bounds__(NW * 64, 2) void igemm_generic_kernel(const void* d
   const int p = n0 + tid % BN;
   const bool pv = p < npos;
   const int pp = pv ? p : 0;
-  const int n = pp / npix_img;
+  const int n = (int)Geo::div(ci, (uint32_t)pp, (uint32_t)npix_img, mg.npix);
   const int rr = pp - n * npix_img;
-  const int th = rr / s.pos_w, tw = rr - (rr / s.pos_w) * s.pos_w;
+  const int th = (int)Geo::div(ci, (uint32_t)rr, (uint32_t)s.pos_w, mg.posw), tw = rr - th * s.pos_w;
   const int hi = s.phase_h + Sh * th, wi = s.phase_w + Sw * tw;
   const int pbase = LAYOUT == 0 ? (n * C + g * Cg) * Hi * Wi + hi * Wi + wi
                                 : ((n * Hi + hi) * Wi + wi) * C + g * Cg;
