@@ -186,9 +186,10 @@ def parity_of(p, got, ref64):
     return res
 
 
-def graph_us(cbd, torch, pl, dy_d, w_d, dx_d, ws=None, calls=50, reps=4):
-    """GPU µs per call: `calls` calls captured in a HIP graph, replayed `reps`
-    times under one event pair (no host launch cost)."""
+def graph_us(cbd, torch, pl, dy_d, w_d, dx_d, ws=None, calls=200, reps=3):
+    """GPU µs per call: `calls` calls captured in a HIP graph, replayed once
+    untimed and then `reps` times under one event pair (no host launch cost;
+    a replay's own fixed launch cost, ≈ 12 µs, is spread over `calls`)."""
     stream = torch.cuda.current_stream()
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
@@ -800,27 +801,9 @@ def all_problems(args):
             torch.cuda.synchronize()
             cold.append(a.elapsed_time(b) * 1e3)
         cold = np.array(cold)
-        # GPU time without host launch cost: 50 calls captured in a HIP graph
+        # GPU time without host launch cost: calls captured in a HIP graph
         # (the calls launch kernels only: no allocation, copy or memset).
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            cbd.run(pl, dy_d, w_d, dx_d, stream=cap)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(graph, stream=cap):
-                for _ in range(50):
-                    cbd.run(pl, dy_d, w_d, dx_d, stream=cap)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(4):
-            graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        us_graph = g0.elapsed_time(g1) * 1e3 / 200
+        us_graph = graph_us(cbd, torch, pl, dy_d, w_d, dx_d)
         # the descriptor-driven kernel of the same plan (static_shape=-1), for
         # the shape-specialised instances' comparison
         us_dyn = None
