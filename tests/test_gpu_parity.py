@@ -7,9 +7,9 @@ determinism checks, a non-default stream, and seeded fuzz over layouts,
 dtypes, groups, strides, dilations and padding for each kernel family.
 
 The large bf16 case (dY 16x1x256x2048, W 2048x1x2x2048) is checked element
-by element on sampled outputs the oracle computes one at a time, and on
-every output against its two-GEMM form (fp64 numpy matmul; that reduction
-is pinned against the oracle in test_oracle_pins.py).
+by element on sampled outputs the oracle computes one at a time and on
+every output against one call of the oracle over the whole problem (about a
+second on the host's threads, shared by the tests of its seeded operands).
 """
 import random
 
@@ -39,6 +39,20 @@ def _gpu():
 
 def by_name(name):
     return [p for p in PROBLEMS if p.name == name][0]
+
+
+_FULL_REF = {}
+
+
+def oracle_full(p, kind="dist"):
+    """The oracle's whole dX of a workload problem's seeded operands (one
+    call each, kept for the tests that share it: about a second for the
+    headline problem on the host's threads)."""
+    key = (p.name, kind, p.n, p.hi, p.wi)
+    if key not in _FULL_REF:
+        dy, w = operands(p, kind)
+        _FULL_REF[key] = oracle.bwd_data(p, dy, w)
+    return _FULL_REF[key]
 
 
 def unreached_mask(p):
@@ -169,14 +183,7 @@ def test_workload_integer_exact(name):
     pl = plan_for(p)
     run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     got = run.result_f32()
-    if name == "c4":
-        # two plain GEMMs (pinned reduction): dX[:,0,r::2,:] = dY[:,0] @ W[:,0,r,:]
-        ref = np.empty(got.shape, dtype=np.float64)
-        for r in range(2):
-            ref[:, 0, r::2, :] = (dy[:, 0].reshape(-1, p.k).astype(np.float64)
-                                  @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
-    else:
-        ref = oracle.bwd_data(p, dy, w)
+    ref = oracle_full(p, "int")
     want = oracle.bf16_bits_to_f32(exact_expected_bits(p, ref)) if p.dtype == "bf16" \
         else exact_expected_bits(p, ref).view(np.float32)
     assert np.array_equal(got, want.reshape(got.shape))
@@ -184,8 +191,9 @@ def test_workload_integer_exact(name):
 
 
 def test_c4_full_size():
-    """The headline bf16 problem: sampled oracle outputs plus the full tensor
-    against the two-GEMM form."""
+    """The headline bf16 problem: sampled oracle outputs (tile corners and
+    random points, one at a time) and every output against one call of the
+    oracle's fp64 loop nest over the whole problem."""
     p = by_name("c4")
     print("[parity] c4 full size", flush=True)
     dy, w = operands(p)
@@ -205,11 +213,8 @@ def test_c4_full_size():
     got_pts = bits[pts[:, 0], pts[:, 2], pts[:, 3], pts[:, 1]]
     ok, info = check_bf16(got_pts, ref_pts)
     assert ok, info
-    # every output against the fp64 two-GEMM form
-    ref = np.empty((p.n, 1, p.wi, p.c), dtype=np.float64)
-    dy2 = dy[:, 0].reshape(-1, p.k).astype(np.float64)
-    for r in range(2):
-        ref[:, 0, r::2, :] = (dy2 @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
+    # every output against the oracle over the whole problem
+    ref = oracle_full(p).reshape(bits.shape)
     ok, info = check_bf16(bits, ref)
     print("[parity] c4", info, flush=True)
     assert ok, info
@@ -220,8 +225,8 @@ def test_c4_full_size():
 
 @pytest.mark.parametrize("ksplit", [2, 3, 8])
 def test_c4_ksplit(ksplit):
-    """Split-K on the headline problem: every output against the fp64
-    two-GEMM form, and equal to itself on a second call."""
+    """Split-K on the headline problem: every output against the oracle,
+    and equal to itself on a second call."""
     p = by_name("c4")
     print(f"[ksplit] c4 ksplit={ksplit}", flush=True)
     dy, w = operands(p)
@@ -231,11 +236,7 @@ def test_c4_ksplit(ksplit):
     run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p), workspace=ws)()
     bits = run.result_bits().reshape(p.n, p.hi, p.wi, p.c)
     assert run.guards_intact()
-    ref = np.empty((p.n, 1, p.wi, p.c), dtype=np.float64)
-    dy2 = dy[:, 0].reshape(-1, p.k).astype(np.float64)
-    for r in range(2):
-        ref[:, 0, r::2, :] = (dy2 @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
-    ok, info = check_bf16(bits, ref)
+    ok, info = check_bf16(bits, oracle_full(p).reshape(bits.shape))
     print("[ksplit] c4", info, flush=True)
     assert ok, info
     bits1 = bits.copy()
@@ -934,7 +935,7 @@ def test_no_split_vs_oracle(name):
 
 def test_no_split_c4_integer_exact():
     """Headline problem in the zero-insertion form on the large-tile kernel:
-    bit-exact against its two-GEMM form on integer data."""
+    bit-exact against the oracle on integer data."""
     p = by_name("c4")
     print("[no-split] c4", flush=True)
     dy, w = operands(p, "int")
@@ -942,11 +943,7 @@ def test_no_split_c4_integer_exact():
     assert pl.info().kernel == cbd.KERNEL_NHWC_BF16
     run = DeviceRun(p, pl, to_device(dy, p), to_device(w, p))()
     got = run.result_f32()
-    ref = np.empty(got.shape, dtype=np.float64)
-    for r in range(2):
-        ref[:, 0, r::2, :] = (dy[:, 0].reshape(-1, p.k).astype(np.float64)
-                              @ w[:, 0, r, :].astype(np.float64)).reshape(p.n, -1, p.c)
-    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, ref))
+    want = oracle.bf16_bits_to_f32(exact_expected_bits(p, oracle_full(p, "int")))
     assert np.array_equal(got, want.reshape(got.shape))
     assert run.guards_intact()
 
