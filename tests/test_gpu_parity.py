@@ -638,10 +638,12 @@ def test_fuzz_generic_row_loads(seed, count, ksplit):
     """f32 NCHW problems on the generic family whose classes read W a
     filter row at a time (1-3 taps per load): filters 2, 3 and 5, strides
     1-3, dilation 1-2, groups, K/G not a multiple of 4 (k rows past K/G),
-    ragged channel and position tiles, and split-K over the row-load k
-    tiles; bit-exact on integer operands, every pattern reached."""
+    ragged channel and position tiles, two- and four-wave workgroups, and
+    split-K over the row-load k tiles; bit-exact on integer operands, every
+    pattern reached."""
     rng = random.Random(seed)
     seen = set()
+    waves = set()
     done = 0
     while done < count:
         g = rng.choice([1, 1, 2, 3])
@@ -658,7 +660,9 @@ def test_fuzz_generic_row_loads(seed, count, ksplit):
         seen |= pats
         opts = {"ksplit": ksplit} if ksplit else {}
         pl = plan_for(p, cbd.KERNEL_GENERIC, **opts)
-        print(f"[fuzz-rows] i={done} pats={sorted(pats)} ksplit={pl.info().ksplit} {p}", flush=True)
+        waves.add(pl.info().threads_main // 64)
+        print(f"[fuzz-rows] i={done} pats={sorted(pats)} ksplit={pl.info().ksplit} "
+              f"waves={pl.info().threads_main // 64} {p}", flush=True)
         sh = oracle.shapes(p)
         dy = small_ints(9000 * seed + 3 * done + 1, sh["dy"]).astype(np.float32)
         w = small_ints(9000 * seed + 3 * done + 2, sh["w"]).astype(np.float32)
@@ -669,6 +673,8 @@ def test_fuzz_generic_row_loads(seed, count, ksplit):
         assert run.guards_intact(), p
         done += 1
     assert {1, 2, 3, 4, 5} <= seen, seen
+    if not ksplit:  # two-wave workgroups (all classes one- to four-tap row loads) reached too
+        assert 2 in waves and 4 in waves, waves
 
 
 # Grouped family: the pipelined row kernel with several rows per workgroup
