@@ -36,6 +36,9 @@ Prints ONE JSON line:
     python bench.py --all      one line per workload problem: warm, graph and
                                cold (caches flushed) us/call, roofline fractions,
                                and the same sampled oracle check (about 1 s each).
+    python bench.py --problem P --cold-calls 50
+                               only calls each after a cache sweep (run under
+                               rocprofv3 --kernel-trace for cold kernel durations).
 """
 from __future__ import annotations
 
@@ -302,6 +305,8 @@ def copy_calibration(nbytes, reps):
 #   kt    rocprofv3 --kernel-trace --stats ... -- bench.py PROF --problem P --steps 50 --warmup 5
 #           (with the clock-settle calls; the summary also gives the 50 timed calls alone)
 #   ktng  the same with --no-graph (calls issued one by one)
+#   ktcold rocprofv3 --kernel-trace --stats ... -- bench.py PROF --problem P --cold-calls 50
+#           (each call after a cache sweep: the kernel's cold duration)
 #   fetch rocprofv3 --pmc FETCH_SIZE ... -- bench.py PROF --problem P --steps 10 --warmup 2
 #           --no-graph --settle-ms 0 --copy-calibration-mib 1024      (write: WRITE_SIZE)
 #   mfma  rocprofv3 --pmc <MFMA_COUNTERS> ... --no-graph --settle-ms 0; stall: <STALL_COUNTERS>
@@ -316,6 +321,8 @@ def pass_command(kind, prob):
     out = f"--output-format csv -d <out>/{kind}_{prob} -o prof -- python3 bench.py {PROF} --problem {prob}"
     if kind in ("kt", "ktng"):
         return f"{ROCPROF} --kernel-trace --stats {out} --steps 50 --warmup 5" + (" --no-graph" if kind == "ktng" else "")
+    if kind == "ktcold":
+        return f"{ROCPROF} --kernel-trace --stats {out} --cold-calls 50"
     pmc = {"fetch": "FETCH_SIZE", "write": "WRITE_SIZE", "mfma": MFMA_COUNTERS, "stall": STALL_COUNTERS}[kind]
     cal = " --copy-calibration-mib 1024" if kind in ("fetch", "write") else ""
     return f"{ROCPROF} --pmc {pmc} {out} --steps 10 --warmup 2 --no-graph --settle-ms 0{cal}"
@@ -406,6 +413,33 @@ def summarize_profiles(raw):
                             f"{b['roofline']['launch_us_mean']} us.", ""]
             open(base + "_kernel_trace.md", "w").write("\n".join(out))
             written.append(base + "_kernel_trace.md")
+        if "ktcold" in ks:
+            name, d_ = trace(ks["ktcold"], sym)
+            b = bench_line(ks["ktcold"])
+            row = (f"| {len(d_)} | {statistics.mean(d_):.3f} | {statistics.median(d_):.3f} | "
+                   f"{min(d_):.3f} | {max(d_):.3f} |")
+            out = [f"# rocprofv3 kernel-trace summary, cold caches: {desc}", "",
+                   f"## {prob}, calls each after a 512 MiB read sweep (L2 and MALL evicted), one at a time",
+                   f"command: {pass_command('ktcold', prob)}", f"summary: {summary_cmd}",
+                   f"kernel: {name}", "",
+                   "| dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|", row, ""]
+            if b:
+                med = statistics.median(d_)
+                if prob in HBM_BOUND:
+                    mb = b["alg_mbytes"]
+                    roof = (f"Algorithmic bytes {mb} MB per call: {mb / med:.3f} TB/s at the median "
+                            f"dispatch, {mb / med / (PEAK_HBM_GBS / 1e3):.3f} of 8 TB/s.")
+                else:
+                    gf = b["useful_gflop"]
+                    peak = PEAK_BF16_TFLOPS if "bf16" in desc else PEAK_F32_TFLOPS
+                    roof = (f"Useful {gf} GFLOP per call: {gf / med * 1e3:.1f} TFLOP/s at the median "
+                            f"dispatch, {gf / med * 1e3 / peak:.3f} of the dense MFMA peak ({peak} TFLOP/s; "
+                            f"no clock-settle calls before these dispatches).")
+                out += [roof + " The same run's HIP-event pair around each call (which adds the launch "
+                        f"latency of a lone call): median {b['us_cold_event_median']} us, mean "
+                        f"{b['us_cold_event_mean']} us ({b['launches']} launch(es) per call).", ""]
+            open(base + "_cold_kernel_trace.md", "w").write("\n".join(out))
+            written.append(base + "_cold_kernel_trace.md")
         if "fetch" in ks and "write" in ks:
             f, cf = counters(ks["fetch"], sym)
             w, cw = counters(ks["write"], sym)
@@ -540,7 +574,12 @@ def main():
                     help="one JSON line per workload problem: warm and cold (caches "
                          "flushed) µs/call and the roofline fraction; not the bench line")
     ap.add_argument("--cold-flush", choices=("read", "write"), default="read",
-                    help="--all: how the 512 MiB sweep before each cold call evicts the caches")
+                    help="--all, --cold-calls: how the 512 MiB sweep before each cold call "
+                         "evicts the caches")
+    ap.add_argument("--cold-calls", type=int, default=0,
+                    help="run only this many calls of --problem, each after a cache sweep "
+                         "and alone on the GPU (for a kernel trace of cold dispatches); "
+                         "prints their event-pair times, not the bench line")
     ap.add_argument("--summarize-profiles", metavar="RAW", default=None,
                     help="write the profiles/ summaries of the rocprofv3 passes under RAW "
                          "(<pass>_<problem> directories; no GPU needed)")
@@ -592,6 +631,9 @@ def main():
     # with a workspace the plan runs its split configuration, if it has one
     eff_ksplit = info.ksplit if info.ksplit > 1 else (info.auto_ksplit if ws is not None else 1)
     stream = torch.cuda.current_stream()
+    if args.cold_calls:
+        cold_calls(args, torch, np, cbd, p, info, pl, dy_d, w_d, dx_d, ws, stream)
+        return
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib << 20, 5)
@@ -740,6 +782,49 @@ def grouped_sweep(args):
         del dy_d, w_d, dx_d
 
 
+def cache_sweep(torch, how):
+    """A callable that evicts L2 and the MALL with a sweep over a 512 MiB
+    buffer: a read sweep (a row-wise max, one output per 8 KiB row, no
+    cross-block reduction) leaves the caches clean; a write sweep (a fill
+    kernel) leaves dirty lines whose write-back falls into whatever runs next."""
+    flush = torch.ones(64 << 20, dtype=torch.float64, device="cuda")  # 512 MiB
+    rows = flush.view(65536, 1024)
+    rowmax = torch.empty(65536, dtype=torch.float64, device="cuda")
+
+    def evict():
+        if how == "write":
+            flush.fill_(1.0)
+        else:
+            torch.amax(rows, dim=1, out=rowmax)
+    return evict
+
+
+def cold_calls(args, torch, np, cbd, p, info, pl, dy_d, w_d, dx_d, ws, stream):
+    """Calls each preceded by a cache sweep and followed by a synchronisation:
+    every dispatch of the problem's kernels in this run starts with cold
+    caches, so a kernel trace of the run gives the kernel's own cold duration
+    (without the launch latency that the event pair around a single call
+    includes).  Prints one JSON line with the event-pair times."""
+    evict = cache_sweep(torch, args.cold_flush)
+    us = []
+    for _ in range(args.cold_calls):
+        evict()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cbd.run(pl, dy_d, w_d, dx_d, stream=stream, workspace=ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us.append(a.elapsed_time(b) * 1e3)
+    us = np.array(us)
+    print(json.dumps({"problem": p.name, "workload": describe(p), "kernel": KERNEL_SYMBOL[kernel_key(info)],
+                      "launches": info.launches, "cold_calls": args.cold_calls,
+                      "cold_flush": args.cold_flush + " sweep of 512 MiB",
+                      "us_cold_event_median": round(float(np.median(us)), 3),
+                      "us_cold_event_mean": round(float(np.mean(us)), 3),
+                      "alg_mbytes": round(algorithmic_bytes(p, info) / 1e6, 3),
+                      "useful_gflop": round(info.useful_flops / 1e9, 5)}), flush=True)
+
+
 def all_problems(args):
     """Every workload problem: warm = back-to-back calls under one event pair
     (host launch cost included: small problems are bounded by it); graph = the
@@ -756,17 +841,7 @@ def all_problems(args):
     from cbd_inputs import PROBLEMS, draw, seed_for
 
     stream = torch.cuda.current_stream()
-    flush = torch.ones(64 << 20, dtype=torch.float64, device="cuda")  # 512 MiB
-    rows = flush.view(65536, 1024)
-    rowmax = torch.empty(65536, dtype=torch.float64, device="cuda")
-
-    def evict():
-        # read sweep: a row-wise max (one output per 8 KiB row, no
-        # cross-block reduction); write sweep: a fill kernel
-        if args.cold_flush == "write":
-            flush.fill_(1.0)
-        else:
-            torch.amax(rows, dim=1, out=rowmax)
+    evict = cache_sweep(torch, args.cold_flush)
     torch.cuda.synchronize()
     mach = machine()
     for p in PROBLEMS:
