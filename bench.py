@@ -745,8 +745,10 @@ def main():
 
 def grouped_sweep(args):
     """Each grouped-sweep shape: 10 warm-up calls, then args.steps calls
-    under one event pair; algorithmic bytes per µs against the HBM roofline
-    (every shape has arithmetic intensity far below the bf16 ridge)."""
+    under one event pair (warm: the host's launch rate bounds the small
+    shapes) and the same calls replayed from a HIP graph (GPU time only);
+    algorithmic bytes per µs against the HBM roofline (every shape has
+    arithmetic intensity far below the bf16 ridge)."""
     import torch
 
     import dnn_conv2d_bwd_amd as cbd
@@ -771,14 +773,18 @@ def grouped_sweep(args):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.steps
+        us_g = graph_us(cbd, torch, pl, dy_d, w_d, dx_d)
         nbytes = algorithmic_bytes(p, info)
-        gbs = nbytes / us / 1e3
+        gbs, gbs_g = nbytes / us / 1e3, nbytes / us_g / 1e3
         print(json.dumps({
             "problem": p.name, "workload": describe(p), "kernel": cbd.KERNEL_NAMES[info.kernel],
             "variant": info.variant, "grid": info.grid_main, "us_warm": round(us, 3),
+            "us_graph": round(us_g, 3),
             "useful_tflops": round(info.useful_flops / us / 1e6, 3),
-            "alg_mbytes": round(nbytes / 1e6, 3), "gbs": round(gbs, 1),
-            "roofline": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+            "useful_tflops_graph": round(info.useful_flops / us_g / 1e6, 3),
+            "alg_mbytes": round(nbytes / 1e6, 3), "gbs": round(gbs, 1), "gbs_graph": round(gbs_g, 1),
+            "roofline": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "frac_graph": round(gbs_g / PEAK_HBM_GBS, 4)}), flush=True)
         del dy_d, w_d, dx_d
 
 

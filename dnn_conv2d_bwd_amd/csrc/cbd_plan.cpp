@@ -646,8 +646,26 @@ extern "C" cbd_status cbd_plan_ex(const cbd_problem* problem, const cbd_plan_opt
     if (rows_opt > 0) {
       grp_rows = std::min<int64_t>(rows_opt, max_pos_h);
     } else {
-      const int64_t resident = 256 * std::min<int64_t>(4, cbd::kLdsPerCu / grp_lds);
-      grp_rows = std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(units, resident)));
+      // Rows per workgroup so that the grid fills up to four workgroups per
+      // compute unit (fewer where LDS holds fewer).  A workgroup's fixed cost
+      // (the filter taps into registers, the ring's first rows) is paid once
+      // per row block, so where that leaves blocks of four rows or fewer the
+      // grid halves (twice the rows each), and halves again below three rows;
+      // then the rows are split evenly over the blocks of a column.  Measured
+      // on the grouped sweep (N = 32, 3x3, graph replays): 32 channels per
+      // group at 7x7 13.0 -> 10.2 us, at 14x14 17.6 -> 14.3 us, 8 per group
+      // at 14x14 12.5 -> 8.9 us; shapes with longer blocks (7 rows or more)
+      // ran slower on half the grid (16 per group, 56x56 stride 2:
+      // 23.3 -> 32.5 us) and keep it.
+      const int64_t per_cu = std::min<int64_t>(4, cbd::kLdsPerCu / grp_lds);
+      auto rows_at = [&](int64_t wgs_per_cu) {
+        const int64_t resident = 256 * std::min<int64_t>(wgs_per_cu, per_cu);
+        return std::min<int64_t>(max_pos_h, std::max<int64_t>(1, ceil_div(units, resident)));
+      };
+      grp_rows = rows_at(4);
+      if (grp_rows <= 4) grp_rows = rows_at(2);
+      if (grp_rows <= 2) grp_rows = rows_at(1);
+      grp_rows = ceil_div(max_pos_h, ceil_div(max_pos_h, grp_rows));
     }
   } else if (kernel == CBD_KERNEL_GROUPED && !subs.empty()) {
     // The row and direct kernels put one group per lane of a 256-lane

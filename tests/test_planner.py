@@ -601,3 +601,33 @@ def test_split_k_plans():
     with pytest.raises(cbd.CbdError) as e:
         mk(by["c5-s2"], ksplit=2)
     assert e.value.status == 2
+
+
+def test_grouped_wide_rows_per_workgroup():
+    """The 16x16x16-MFMA grouped kernel's row blocks: up to four workgroups
+    per compute unit, half as many (twice the rows) where blocks would have
+    four rows or fewer and again below three, rows split evenly over a
+    column's blocks; the grid is images x row blocks x 256-byte group slices
+    x column blocks."""
+    from cbd_inputs import GROUPED_SWEEP
+    want = {"gs-c8-14-s1": 4, "gs-c8-7-s1": 2, "gs-c16-7-s1": 4, "gs-c32-7-s1": 4, "gs-c32-14-s1": 7,
+            "gs-c32-56-s1": 28, "gs-c16-56-s2": 14, "gs-c8-56-s1": 10, "gs-c32-28-s2": 14}
+    seen = set()
+    for p in GROUPED_SWEEP:
+        if p.c // p.g < 8:
+            continue
+        pl = cbd.plan(p.n, p.g, p.c, p.k, p.hi, p.wi, p.y, p.x, (p.sh, p.sw), (p.ph, p.pw), (p.dh, p.dw),
+                      p.layout, cbd.BF16)
+        i = pl.info()
+        subs = pl.subgemms()
+        ph = max(s.pos_h for s in subs)
+        pw = max(s.pos_w for s in subs)
+        r = i.rows_per_wg
+        blocks = -(-ph // r)
+        assert -(-ph // blocks) == r, (p.name, r, ph)  # even blocks
+        slices = p.c * 2 // 256
+        assert i.grid_main == sum(p.n * -(-s.pos_h // r) * slices * -(-s.pos_w // i.cols_per_wg) for s in subs)
+        if p.name in want:
+            assert r == want[p.name], (p.name, r)
+            seen.add(p.name)
+    assert seen == set(want)
