@@ -122,43 +122,109 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
   // A operands: group gl = wave*GPW + j (global gb*GB + gl); lane l holds
   // W[g*CG + 16 kh + 4 lq + e][ty][tx][16 ch + ln], e = 0..3 (paired groups
   // of 8: the entry of real group 2g + ln/8 where k and c fall in the same
-  // group, 0 elsewhere).
+  // group, 0 elsewhere).  W is c-contiguous; for the paired groups of 8 the
+  // lanes of a pair (ln even, ln + 1) each read two 4-byte words, channels
+  // (ln & ~1, +1) of k rows 2 (ln & 1) + {0, 1}, and swap them (DPP): the
+  // even lane keeps the low halves of all four rows, the odd lane the high
+  // halves, with half the loads of one 2-byte gather per element (8
+  // channels per group, N = 32: 7x7 7.0 -> 6.4 us, 28x28 14.3 -> 13.3).
   const int YX = a.Y * a.X;
+  const int odd = ln & 1, hsh = 16 * odd;
   s16x4 wa[GPW][NT][H][H];
   int jhs[NT], cshift[NT];
 #pragma unroll
   for (int tp = 0; tp < NT; tp++) {
     const int jh = tp / s.taps_w;
+    jhs[tp] = jh;
+    cshift[tp] = span - a.delta_w * (tp - jh * s.taps_w);
+  }
+  // The words of tap tp: k rows 4 lq + 2 odd + i, channels (ln & ~1, +1).
+  // Taps are pipelined one deep (tap tp + 1's loads in flight while tap
+  // tp's are swapped and packed), which keeps the registers this takes to
+  // two taps' words.
+  typedef uint32_t TapWords[GPW][H][H][2];
+  auto load_tap = [&](int tp, TapWords& wl) {
+    const int jh = tp / s.taps_w;
     const int jw = tp - jh * s.taps_w;
     const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
-    jhs[tp] = jh;
-    cshift[tp] = span - a.delta_w * jw;
 #pragma unroll
     for (int j = 0; j < GPW; j++) {
       const int g = gb * GB + wave * GPW + j;
 #pragma unroll
       for (int kh = 0; kh < H; kh++)
 #pragma unroll
-        for (int ch = 0; ch < H; ch++) {
-          uint32_t e[4];
+        for (int ch = 0; ch < H; ch++)
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            if constexpr (PAIR8) {
-              const int k = 4 * lq + q;  // 0..15 within the pair
-              const bool on = (k >> 3) == (ln >> 3);
-              const int rg = 2 * g + (ln >> 3);
-              e[q] = __builtin_amdgcn_raw_buffer_load_b16(
-                  rw, on ? (uint32_t)(((rg * 8 + (k & 7)) * YX + ty * a.X + tx) * 8 + (ln & 7)) * ES : dev::kOOB,
-                  0, 0);
-            } else {
+          for (int i = 0; i < 2; i++) {
+            const int q = 2 * odd + i;
+            const int k = 4 * lq + q;  // 0..15 within the pair; k / 8 == lq / 2 for all four rows
+            const bool on = (k >> 3) == (ln >> 3);
+            const int rg = 2 * g + (ln >> 3);
+            wl[j][kh][ch][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                rw, on ? (uint32_t)(((rg * 8 + (k & 7)) * YX + ty * a.X + tx) * 8 + (ln & 6)) * ES : dev::kOOB,
+                0, 0);
+          }
+    }
+  };
+  // Partner's words (lane ^ 1, DPP quad_perm [1, 0, 3, 2]); the even lane
+  // takes the low halves (its channel) of rows 0, 1 (its own words) and 2, 3
+  // (the partner's), the odd lane the high halves of rows 0, 1 (the
+  // partner's) and 2, 3 (its own).
+  auto half2 = [&](uint32_t x0, uint32_t x1) {
+    return ((x0 >> hsh) & 0xffffu) | (((x1 >> hsh) & 0xffffu) << 16);
+  };
+  auto pack_tap = [&](int tp, const TapWords& wl) {
+#pragma unroll
+    for (int j = 0; j < GPW; j++)
+#pragma unroll
+      for (int kh = 0; kh < H; kh++)
+#pragma unroll
+        for (int ch = 0; ch < H; ch++) {
+          const uint32_t w0 = wl[j][kh][ch][0], w1 = wl[j][kh][ch][1];
+          const uint32_t p0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w0, 0xB1, 0xf, 0xf, false);
+          const uint32_t p1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xf, 0xf, false);
+          const uint32_t a0 = odd ? p0 : w0, a1 = odd ? p1 : w1;  // rows 0, 1
+          const uint32_t b0 = odd ? w0 : p0, b1 = odd ? w1 : p1;  // rows 2, 3
+          const u32x2 v = {half2(a0, a1), half2(b0, b1)};
+          wa[j][tp][kh][ch] = __builtin_bit_cast(s16x4, v);
+        }
+  };
+  if constexpr (PAIR8) {
+    TapWords wbuf[2];
+    load_tap(0, wbuf[0]);
+#pragma unroll
+    for (int tp = 0; tp < NT; tp++) {
+      if (tp + 1 < NT) load_tap(tp + 1, wbuf[(tp + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      pack_tap(tp, wbuf[tp & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // 16 or 32 channels: one 2-byte gather per element (the paired words
+    // measured slower here: at 32 channels the kernel's registers rise
+    // past what four waves per SIMD allow).
+#pragma unroll
+    for (int tp = 0; tp < NT; tp++) {
+      const int jh = tp / s.taps_w;
+      const int jw = tp - jh * s.taps_w;
+      const int ty = s.cls_h + a.tstep_h * jh, tx = s.cls_w + a.tstep_w * jw;
+#pragma unroll
+      for (int j = 0; j < GPW; j++) {
+        const int g = gb * GB + wave * GPW + j;
+#pragma unroll
+        for (int kh = 0; kh < H; kh++)
+#pragma unroll
+          for (int ch = 0; ch < H; ch++) {
+            uint32_t e[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++)
               e[q] = __builtin_amdgcn_raw_buffer_load_b16(
                   rw, (uint32_t)(((g * CG + 16 * kh + 4 * lq + q) * YX + ty * a.X + tx) * CG + 16 * ch + ln) * ES, 0,
                   0);
-            }
+            const u32x2 v = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            wa[j][tp][kh][ch] = __builtin_bit_cast(s16x4, v);
           }
-          const u32x2 v = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-          wa[j][tp][kh][ch] = __builtin_bit_cast(s16x4, v);
-        }
+      }
     }
   }
 
@@ -217,8 +283,12 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
   flush_row(th1 - 1);
 }
 
+// 32 channels per group: at most 128 VGPRs (four waves per SIMD, as many
+// workgroups as LDS holds where the ring is small; the compiler's own choice
+// was 133): 28x28 stride 2 22.5 -> 17.2 us, 14x14 stride 2 13.1 -> 10.5,
+// 28x28 stride 1 33.4 -> 30.6 (N = 32), no spills.
 template <int CG, bool PAIR8>
-__global__ __launch_bounds__(kGroupedThreads) void grouped_wide_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kGroupedThreads, CG == 32 ? 4 : 1) void grouped_wide_kernel(const GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char ring[];
   constexpr int GB = SB / ((PAIR8 ? 8 : CG) * 2);  // the problem's groups per workgroup
   dev::prefetch_args(a);
