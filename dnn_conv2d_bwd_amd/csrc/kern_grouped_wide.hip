@@ -127,7 +127,7 @@ __device__ __forceinline__ void wide_rows(const GemmArgs& a, const SubDesc& s, c
   // (ln & ~1, +1) of k rows 2 (ln & 1) + {0, 1}, and swap them (DPP): the
   // even lane keeps the low halves of all four rows, the odd lane the high
   // halves, with half the loads of one 2-byte gather per element (8
-  // channels per group, N = 32: 7x7 7.0 -> 6.4 us, 28x28 14.3 -> 13.3).
+  // channels per group, N = 32: 7x7 7.0 -> 6.3 us, 28x28 14.3 -> 13.1).
   const int YX = a.Y * a.X;
   const int odd = ln & 1, hsh = 16 * odd;
   s16x4 wa[GPW][NT][H][H];
